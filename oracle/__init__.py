@@ -1,0 +1,166 @@
+"""fp64 CPU oracle of the Naju selective scan -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path never does, and this
+package imports nothing from the product package.
+
+The arithmetic lives in ``naju_oracle.c`` (plain C, fp64, sequential time
+loops); this module only builds it with gcc, marshals numpy arrays and
+returns numpy arrays.  Definitions followed (reproduction README of arXiv
+2607.21000, "Core equations" and the block flowchart):
+
+    x_n  = sigma(a_n) x_{n-1} + sigma(b_n) h_n B_n^T
+    ys_n = x_n C_n / sqrt(N) + D h_n
+    block: h = SiLU(causal depthwise conv(u)),  y = ys * SiLU(z)
+
+Parity pinning: every function here is pinned by ``tests/test_oracle_pins.py``
+against closed forms, brute force, library routines (scipy lfilter, numpy
+matmul) and central finite differences.  Nothing here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "naju_oracle.c")
+_LIB = os.path.join(_HERE, "libnaju_oracle.so")
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, no FMA contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC",
+               "-shared", "-std=c11", _SRC, "-o", tmp, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = ctypes.CDLL(_LIB)
+        i64 = ctypes.c_int64
+        p = ctypes.c_void_p
+        _lib.naju_oracle_scan_fwd.argtypes = [i64] * 4 + [p] * 9
+        _lib.naju_oracle_scan_bwd.argtypes = [i64] * 4 + [p] * 16
+        _lib.naju_oracle_conv_silu.argtypes = [i64] * 4 + [p] * 5
+        _lib.naju_oracle_block_fwd.argtypes = [i64] * 5 + [p] * 13
+        _lib.naju_oracle_block_bwd.argtypes = [i64] * 5 + [p] * 22
+        for f in ("naju_oracle_scan_fwd", "naju_oracle_scan_bwd", "naju_oracle_conv_silu",
+                  "naju_oracle_block_fwd", "naju_oracle_block_bwd"):
+            getattr(_lib, f).restype = None
+    return _lib
+
+
+def _in(x, shape=None):
+    """Read-only fp64 C-contiguous copy (or None)."""
+    if x is None:
+        return None
+    arr = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    if shape is not None and arr.shape != tuple(shape):
+        raise ValueError("oracle: expected shape %s, got %s" % (tuple(shape), arr.shape))
+    return arr
+
+
+def _p(arr):
+    return None if arr is None else arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dims(h, B):
+    Bt, L, Di = np.shape(h)
+    N = np.shape(B)[-1]
+    return int(Bt), int(L), int(Di), int(N)
+
+
+def scan_fwd(h, a, b, B, C, D, x0=None):
+    """Returns (ys [Bt,L,Di], x_final [Bt,Di,N]) in fp64."""
+    lib = _load()
+    Bt, L, Di, N = _dims(h, B)
+    t3, tn, st = (Bt, L, Di), (Bt, L, N), (Bt, Di, N)
+    h, a, b = _in(h, t3), _in(a, t3), _in(b, t3)
+    B, C, D, x0 = _in(B, tn), _in(C, tn), _in(D, (Di,)), _in(x0, st)
+    ys = np.empty(t3)
+    xf = np.empty(st)
+    lib.naju_oracle_scan_fwd(Bt, L, Di, N, _p(h), _p(a), _p(b), _p(B), _p(C), _p(D), _p(x0),
+                             _p(ys), _p(xf))
+    return ys, xf
+
+
+def scan_bwd(h, a, b, B, C, D, x0, g, dx_final=None):
+    """Reverse mode of scan_fwd for upstream gradient g = dLoss/dys.
+
+    Returns dict with dh, da, db [Bt,L,Di]; dB, dC [Bt,L,N]; dD [Di]; dx0 [Bt,Di,N].
+    """
+    lib = _load()
+    Bt, L, Di, N = _dims(h, B)
+    t3, tn, st = (Bt, L, Di), (Bt, L, N), (Bt, Di, N)
+    h, a, b, g = _in(h, t3), _in(a, t3), _in(b, t3), _in(g, t3)
+    B, C, D = _in(B, tn), _in(C, tn), _in(D, (Di,))
+    x0, dxf = _in(x0, st), _in(dx_final, st)
+    out = {k: np.empty(t3) for k in ("dh", "da", "db")}
+    out.update(dB=np.empty(tn), dC=np.empty(tn), dD=np.empty(Di), dx0=np.empty(st))
+    lib.naju_oracle_scan_bwd(Bt, L, Di, N, _p(h), _p(a), _p(b), _p(B), _p(C), _p(D), _p(x0),
+                             _p(g), _p(dxf), _p(out["dh"]), _p(out["da"]), _p(out["db"]),
+                             _p(out["dB"]), _p(out["dC"]), _p(out["dD"]), _p(out["dx0"]))
+    return out
+
+
+def conv_silu(u, w, conv_state=None):
+    """Returns (pre, h): causal depthwise conv of u with taps w [Di,K], then SiLU."""
+    lib = _load()
+    Bt, L, Di = np.shape(u)
+    K = int(np.shape(w)[1])
+    u, w = _in(u, (Bt, L, Di)), _in(w, (Di, K))
+    cs = _in(conv_state, (Bt, K - 1, Di))
+    pre = np.empty((Bt, L, Di))
+    h = np.empty((Bt, L, Di))
+    lib.naju_oracle_conv_silu(Bt, L, Di, K, _p(u), _p(w), _p(cs), _p(pre), _p(h))
+    return pre, h
+
+
+def block_fwd(u, z, w, a, b, B, C, D, x0=None, conv_state=None):
+    """Returns (y, x_final, conv_state_out)."""
+    lib = _load()
+    Bt, L, Di, N = _dims(u, B)
+    K = int(np.shape(w)[1])
+    t3, tn, st = (Bt, L, Di), (Bt, L, N), (Bt, Di, N)
+    u, z, a, b = _in(u, t3), _in(z, t3), _in(a, t3), _in(b, t3)
+    w, cs = _in(w, (Di, K)), _in(conv_state, (Bt, K - 1, Di))
+    B, C, D, x0 = _in(B, tn), _in(C, tn), _in(D, (Di,)), _in(x0, st)
+    y = np.empty(t3)
+    xf = np.empty(st)
+    cso = np.empty((Bt, K - 1, Di))
+    lib.naju_oracle_block_fwd(Bt, L, Di, N, K, _p(u), _p(z), _p(w), _p(cs), _p(a), _p(b),
+                              _p(B), _p(C), _p(D), _p(x0), _p(y), _p(xf), _p(cso))
+    return y, xf, cso
+
+
+def block_bwd(u, z, w, a, b, B, C, D, x0, dy, dx_final=None, conv_state=None):
+    """Reverse mode of block_fwd.  Returns dict with du, dz, dw, dconv_state, da, db,
+    dB, dC, dD, dx0."""
+    lib = _load()
+    Bt, L, Di, N = _dims(u, B)
+    K = int(np.shape(w)[1])
+    t3, tn, st = (Bt, L, Di), (Bt, L, N), (Bt, Di, N)
+    u, z, a, b, dy = _in(u, t3), _in(z, t3), _in(a, t3), _in(b, t3), _in(dy, t3)
+    w, cs = _in(w, (Di, K)), _in(conv_state, (Bt, K - 1, Di))
+    B, C, D = _in(B, tn), _in(C, tn), _in(D, (Di,))
+    x0, dxf = _in(x0, st), _in(dx_final, st)
+    out = {k: np.empty(t3) for k in ("du", "dz", "da", "db")}
+    out.update(dw=np.empty((Di, K)), dconv_state=np.empty((Bt, K - 1, Di)),
+               dB=np.empty(tn), dC=np.empty(tn), dD=np.empty(Di), dx0=np.empty(st))
+    lib.naju_oracle_block_bwd(Bt, L, Di, N, K, _p(u), _p(z), _p(w), _p(cs), _p(a), _p(b),
+                              _p(B), _p(C), _p(D), _p(x0), _p(dy), _p(dxf),
+                              _p(out["du"]), _p(out["dz"]), _p(out["dw"]),
+                              _p(out["dconv_state"]), _p(out["da"]), _p(out["db"]),
+                              _p(out["dB"]), _p(out["dC"]), _p(out["dD"]), _p(out["dx0"]))
+    return out

@@ -1,0 +1,400 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each test ties the oracle to something other than itself: brute force of the
+unrolled closed form, a dense masked-matrix form evaluated with numpy matmul,
+constant-gate geometric series, a first-order IIR filter (scipy lfilter),
+special cases (lossless retention, pure decay, C = 0), the fading-memory
+inequality, associativity of the affine recurrence (chaining), exact
+homogeneity / Euler identities of the reverse mode, and central finite
+differences of every gradient.
+
+Sources: the recurrence and readout are the "Core equations" of the Naju
+reproduction README (arXiv 2607.21000); the block wiring (causal depthwise
+conv + SiLU front end, SiLU(z) output modulation, direct feedthrough) is that
+page's flowchart and "Background and main changes"; stability (0 < f < 1,
+Schur-stable frozen coordinates) and the fading-memory/BIBO property are in
+the paper's abstract (shd-paper.top summary page); the equivalence of the
+sequential recurrence and the affine scan is the README's "Scope" section.
+"""
+import numpy as np
+import pytest
+import scipy.signal
+from scipy.special import expit
+
+import oracle
+from selective_state_space_naju_amd import inputs
+
+
+def rand_case(Bt=2, L=24, Di=5, N=16, seed=0, a_mu=1.0, b_mu=0.0, x0=True):
+    rng = np.random.default_rng(seed)
+    d = dict(
+        h=rng.standard_normal((Bt, L, Di)),
+        a=rng.standard_normal((Bt, L, Di)) + a_mu,
+        b=rng.standard_normal((Bt, L, Di)) + b_mu,
+        B=rng.standard_normal((Bt, L, N)),
+        C=rng.standard_normal((Bt, L, N)),
+        D=rng.standard_normal(Di),
+    )
+    d["x0"] = rng.standard_normal((Bt, Di, N)) if x0 else None
+    return d
+
+
+def brute_states(h, a, b, B, x0):
+    """x_n from the unrolled closed form
+        x_n = (prod_{j<=n} f_j) x0 + sum_{k<=n} (prod_{j=k+1..n} f_j) i_k h_k B_k
+    evaluated term by term (O(L^2)), 0-based n."""
+    Bt, L, Di = h.shape
+    N = B.shape[-1]
+    f, i = expit(a), expit(b)
+    xs = np.zeros((Bt, L, Di, N))
+    for n in range(L):
+        lead = np.prod(f[:, : n + 1, :], axis=1)  # [Bt, Di]
+        acc = lead[:, :, None] * (x0 if x0 is not None else 0.0)
+        for k in range(n + 1):
+            decay = np.prod(f[:, k + 1: n + 1, :], axis=1)  # empty product = 1
+            acc = acc + (decay * i[:, k, :] * h[:, k, :])[:, :, None] * B[:, k, None, :]
+        xs[:, n] = acc
+    return xs
+
+
+def test_closed_form_brute_force():
+    d = rand_case(L=20, Di=4, N=16, seed=1)
+    ys, xf = oracle.scan_fwd(**d)
+    xs = brute_states(d["h"], d["a"], d["b"], d["B"], d["x0"])
+    N = d["B"].shape[-1]
+    y_ref = np.einsum("blds,bls->bld", xs, d["C"]) / np.sqrt(N) + d["D"] * d["h"]
+    np.testing.assert_allclose(xf, xs[:, -1], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ys, y_ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("N", [1, 16, 64])
+def test_dense_masked_matrix_form(N):
+    """y[:, c] = (M_c o (C B^T)) (i h)[:, c] / sqrt(N) + P_c (C x0_c) / sqrt(N) + D_c h[:, c]
+    with M_c[n, k] = prod_{j=k+1..n} f_j[c] (k <= n) and P_c[n] = prod_{j<=n} f_j[c]."""
+    d = rand_case(Bt=1, L=33, Di=3, N=N, seed=2 + N)
+    ys, _ = oracle.scan_fwd(**d)
+    f, i = expit(d["a"][0]), expit(d["b"][0])
+    Bm, Cm, x0 = d["B"][0], d["C"][0], d["x0"][0]
+    L = Bm.shape[0]
+    G = Cm @ Bm.T
+    for c in range(d["h"].shape[2]):
+        M = np.zeros((L, L))
+        for n in range(L):
+            for k in range(n + 1):
+                M[n, k] = np.prod(f[k + 1: n + 1, c])
+        P = np.cumprod(f[:, c])
+        y = (M * G) @ (i[:, c] * d["h"][0, :, c]) / np.sqrt(N)
+        y += P * (Cm @ x0[c]) / np.sqrt(N) + d["D"][c] * d["h"][0, :, c]
+        np.testing.assert_allclose(ys[0, :, c], y, rtol=1e-11, atol=1e-12)
+
+
+def test_constant_gates_geometric_series():
+    Bt, L, Di, N = 1, 50, 3, 16
+    rng = np.random.default_rng(3)
+    a0, b0, h0 = 1.3, -0.4, 0.7
+    Bv = rng.standard_normal(N)
+    x0 = rng.standard_normal((Bt, Di, N))
+    h = np.full((Bt, L, Di), h0)
+    a = np.full((Bt, L, Di), a0)
+    b = np.full((Bt, L, Di), b0)
+    B = np.broadcast_to(Bv, (Bt, L, N)).copy()
+    C = rng.standard_normal((Bt, L, N))
+    D = np.zeros(Di)
+    _, xf = oracle.scan_fwd(h, a, b, B, C, D, x0)
+    f, i = expit(a0), expit(b0)
+    ref = f ** L * x0 + (i * h0 * Bv * (1 - f ** L) / (1 - f))[None, None, :]
+    np.testing.assert_allclose(xf, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_decoupled_gates_write_under_near_full_retention():
+    """f = sigma(7), i = sigma(5): the steady state i h B/(1-f) is ~1090 x the write,
+    far above what a coupled gate (retention r, write w with r + w <= 1) can hold."""
+    Bt, L, Di, N = 1, 60000, 1, 16
+    h = np.ones((Bt, L, Di))
+    a = np.full((Bt, L, Di), 7.0)
+    b = np.full((Bt, L, Di), 5.0)
+    B = np.ones((Bt, L, N))
+    C = np.ones((Bt, L, N))
+    _, xf = oracle.scan_fwd(h, a, b, B, C, np.zeros(Di), None)
+    f, i = expit(7.0), expit(5.0)
+    steady = i / (1 - f)
+    exact = steady * (1 - f ** L)
+    np.testing.assert_allclose(xf, exact, rtol=1e-9)
+    assert xf.min() > 1000.0  # coupled designs are bounded by 1 here
+
+
+def test_first_order_iir_lfilter():
+    """N = 1, B = C = 1, constant gates: the state is the IIR filter
+    x_n = f x_{n-1} + i h_n, i.e. scipy.signal.lfilter([i], [1, -f], h, zi=[f x0])."""
+    Bt, L, Di, N = 1, 300, 2, 1
+    rng = np.random.default_rng(4)
+    h = rng.standard_normal((Bt, L, Di))
+    a0, b0 = 2.2, -1.1
+    a = np.full((Bt, L, Di), a0)
+    b = np.full((Bt, L, Di), b0)
+    B = np.ones((Bt, L, N))
+    C = np.ones((Bt, L, N))
+    D = rng.standard_normal(Di)
+    x0 = rng.standard_normal((Bt, Di, N))
+    ys, xf = oracle.scan_fwd(h, a, b, B, C, D, x0)
+    f, i = expit(a0), expit(b0)
+    for c in range(Di):
+        xr, _ = scipy.signal.lfilter([i], [1.0, -f], h[0, :, c], zi=[f * x0[0, c, 0]])
+        np.testing.assert_allclose(ys[0, :, c] - D[c] * h[0, :, c], xr, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(xf[0, c, 0], xr[-1], rtol=1e-12)
+
+
+@pytest.mark.parametrize("a_val", [np.inf, 40.0])
+def test_lossless_retention(a_val):
+    """f -> 1 and i = 0 (a = +inf or sigma(a) rounding to 1, b = -inf): state kept exactly."""
+    d = rand_case(Bt=2, L=40, Di=3, N=16, seed=5)
+    d["a"][:] = a_val
+    d["b"][:] = -np.inf
+    ys, xf = oracle.scan_fwd(**d)
+    assert np.array_equal(xf, d["x0"])
+    ref = np.einsum("bds,bls->bld", d["x0"], d["C"]) / 4.0 + d["D"] * d["h"]
+    np.testing.assert_allclose(ys, ref, rtol=1e-14, atol=1e-14)
+
+
+def test_pure_decay_bound():
+    """i = 0 (b = -inf): x_n = x0 prod f, and |x_n| strictly decreases (0 < f < 1)."""
+    d = rand_case(Bt=1, L=30, Di=4, N=16, seed=6, a_mu=2.0)
+    d["b"][:] = -np.inf
+    f = expit(d["a"])
+    prev = np.abs(d["x0"])
+    for n in range(1, d["h"].shape[1] + 1):
+        sub = {k: (v[:, :n] if k in ("h", "a", "b", "B", "C") else v) for k, v in d.items()}
+        _, xf = oracle.scan_fwd(**sub)
+        ref = d["x0"] * np.prod(f[:, :n], axis=1)[:, :, None]
+        np.testing.assert_allclose(xf, ref, rtol=1e-13)
+        assert np.all(np.abs(xf) < prev)
+        prev = np.abs(xf)
+
+
+def test_bibo_bound():
+    """|x_n[c,s]| <= |x0[c,s]| + max_k |i_k h_k B_k[s]| / (1 - max_k f_k)."""
+    d = rand_case(Bt=2, L=200, Di=6, N=16, seed=7, a_mu=3.0)
+    Bt, L, Di = d["h"].shape
+    f, i = expit(d["a"]), expit(d["b"])
+    for n in (1, 7, 50, 200):
+        sub = {k: (v[:, :n] if k in ("h", "a", "b", "B", "C") else v) for k, v in d.items()}
+        _, xf = oracle.scan_fwd(**sub)
+        drive = np.abs((i * d["h"])[:, :n, :, None] * d["B"][:, :n, None, :]).max(axis=1)
+        fmax = f[:, :n].max(axis=1)[:, :, None]
+        bound = np.abs(d["x0"]) + drive / (1 - fmax)
+        assert np.all(np.abs(xf) <= bound)
+
+
+def test_c_zero_feedthrough_only():
+    """C = 0: y = D h exactly (block: times SiLU(z)); with dx_final = 0 the gate and B
+    gradients vanish exactly."""
+    d = rand_case(Bt=2, L=17, Di=4, N=16, seed=8)
+    d["C"][:] = 0.0
+    ys, _ = oracle.scan_fwd(**d)
+    assert np.array_equal(ys, d["D"] * d["h"])
+    g = np.random.default_rng(9).standard_normal(d["h"].shape)
+    gr = oracle.scan_bwd(g=g, **d)
+    assert not gr["da"].any() and not gr["db"].any() and not gr["dB"].any()
+    np.testing.assert_allclose(gr["dh"], d["D"] * g, rtol=1e-15)
+
+
+def test_chaining_equals_single_call_and_affine_pairs():
+    """Sequential recurrence == affine scan: splitting the sequence at any point and
+    carrying the state (or composing (prod f, zero-start state) pairs) is exact up to
+    rounding."""
+    d = rand_case(Bt=2, L=64, Di=5, N=16, seed=10)
+    ys, xf = oracle.scan_fwd(**d)
+    for m in (1, 17, 32, 63):
+        first = {k: (v[:, :m] if k in ("h", "a", "b", "B", "C") else v) for k, v in d.items()}
+        rest = {k: (v[:, m:] if k in ("h", "a", "b", "B", "C") else v) for k, v in d.items()}
+        y1, x1 = oracle.scan_fwd(**first)
+        rest["x0"] = x1
+        y2, x2 = oracle.scan_fwd(**rest)
+        np.testing.assert_allclose(np.concatenate([y1, y2], axis=1), ys, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(x2, xf, rtol=1e-12, atol=1e-12)
+        # affine pairs: (P1, S1) o (P2, S2) applied to x0
+        zero1 = dict(first, x0=None)
+        zero2 = dict(rest, x0=None)
+        _, S1 = oracle.scan_fwd(**zero1)
+        _, S2 = oracle.scan_fwd(**zero2)
+        P1 = np.prod(expit(d["a"][:, :m]), axis=1)[:, :, None]
+        P2 = np.prod(expit(d["a"][:, m:]), axis=1)[:, :, None]
+        np.testing.assert_allclose(P2 * (P1 * d["x0"] + S1) + S2, xf, rtol=1e-12, atol=1e-12)
+
+
+def test_homogeneity_exact():
+    d = rand_case(Bt=1, L=40, Di=4, N=16, seed=11)
+    ys, xf = oracle.scan_fwd(**d)
+    d2 = dict(d, h=2 * d["h"], x0=2 * d["x0"])
+    ys2, xf2 = oracle.scan_fwd(**d2)
+    assert np.array_equal(ys2, 2 * ys) and np.array_equal(xf2, 2 * xf)
+
+
+def dot(x, y):
+    return float(np.sum(np.asarray(x) * np.asarray(y)))
+
+
+def test_euler_identities_of_reverse_mode():
+    """With gates fixed, ys and x_final are jointly linear in (h, x0), linear in C
+    (minus the feedthrough), linear in D through D h, and (x0 = 0) linear in B:
+        <dh,h> + <dx0,x0> = <g,ys> + <dxf,x_final>
+        <dC,C> = <g, ys - D h>,   <dD,D> = <g, D h>
+        x0 = 0, dxf = 0:  <dB,B> = <dC,C>"""
+    d = rand_case(Bt=2, L=30, Di=6, N=16, seed=12)
+    rng = np.random.default_rng(13)
+    g = rng.standard_normal(d["h"].shape)
+    dxf = rng.standard_normal(d["x0"].shape)
+    ys, xf = oracle.scan_fwd(**d)
+    gr = oracle.scan_bwd(g=g, dx_final=dxf, **d)
+    lhs = dot(gr["dh"], d["h"]) + dot(gr["dx0"], d["x0"])
+    assert lhs == pytest.approx(dot(g, ys) + dot(dxf, xf), rel=1e-11)
+    gr0 = oracle.scan_bwd(g=g, **d)
+    fb = d["D"] * d["h"]
+    assert dot(gr0["dC"], d["C"]) == pytest.approx(dot(g, ys - fb), rel=1e-11)
+    assert dot(gr0["dD"], d["D"]) == pytest.approx(dot(g, fb), rel=1e-11)
+    dz = dict(d, x0=None)
+    ysz, _ = oracle.scan_fwd(**dz)
+    grz = oracle.scan_bwd(g=g, **dz)
+    assert dot(grz["dB"], d["B"]) == pytest.approx(dot(g, ysz - fb), rel=1e-11)
+    assert dot(grz["dB"], d["B"]) == pytest.approx(dot(grz["dC"], d["C"]), rel=1e-11)
+
+
+def _fd_check(fun, args, grads, names, eps_rel=1e-6, rtol=1e-7, seed=0, max_per=40):
+    """Central finite differences of scalar fun(**args) against analytic grads."""
+    rng = np.random.default_rng(seed)
+    for name in names:
+        v = args[name]
+        flat = v.reshape(-1)
+        idx = np.arange(flat.size)
+        if flat.size > max_per:
+            idx = rng.choice(flat.size, size=max_per, replace=False)
+        fd = np.empty(idx.size)
+        for j, t in enumerate(idx):
+            old = flat[t]
+            eps = eps_rel * max(1.0, abs(old))
+            flat[t] = old + eps
+            fp = fun(**args)
+            flat[t] = old - eps
+            fm = fun(**args)
+            flat[t] = old
+            fd[j] = (fp - fm) / (2 * eps)
+        an = grads[name].reshape(-1)[idx]
+        scale = max(1.0, np.abs(an).max())
+        err = np.abs(fd - an).max() / scale
+        assert err < rtol, "%s: fd mismatch %.3e" % (name, err)
+
+
+def test_scan_gradients_finite_differences():
+    d = rand_case(Bt=2, L=16, Di=8, N=16, seed=14, a_mu=2.0)
+    rng = np.random.default_rng(15)
+    g = rng.standard_normal(d["h"].shape)
+    dxf = rng.standard_normal(d["x0"].shape)
+
+    def loss(**kw):
+        ys, xf = oracle.scan_fwd(**kw)
+        return dot(g, ys) + dot(dxf, xf)
+
+    gr = oracle.scan_bwd(g=g, dx_final=dxf, **d)
+    grads = {"h": gr["dh"], "a": gr["da"], "b": gr["db"], "B": gr["dB"], "C": gr["dC"],
+             "D": gr["dD"], "x0": gr["dx0"]}
+    _fd_check(loss, d, grads, list(grads))
+
+
+def test_block_gradients_finite_differences():
+    """Tiny block case (Bt=2, L=16, Di=8, N=16, K=4): every gradient of
+    <dy, y> + <dxf, x_final> against central differences."""
+    d = inputs.draw(2, 16, 8, 16, io="f32", seed=16, block=True, backward=True, x0=True,
+                    dx_final=True, conv_state=True)
+    d = {k: v.astype(np.float64) for k, v in d.items()}
+    dy, dxf = d.pop("dy"), d.pop("dx_final")
+    args = dict(u=d["u"], z=d["z"], w=d["conv_w"], a=d["a"], b=d["b"], B=d["B"], C=d["C"],
+                D=d["D"], x0=d["x0"], conv_state=d["conv_state"])
+
+    def loss(**kw):
+        y, xf, _ = oracle.block_fwd(**kw)
+        return dot(dy, y) + dot(dxf, xf)
+
+    gr = oracle.block_bwd(dy=dy, dx_final=dxf, **args)
+    grads = {"u": gr["du"], "z": gr["dz"], "w": gr["dw"], "a": gr["da"], "b": gr["db"],
+             "B": gr["dB"], "C": gr["dC"], "D": gr["dD"], "x0": gr["dx0"],
+             "conv_state": gr["dconv_state"]}
+    _fd_check(loss, args, grads, list(grads))
+
+
+def test_conv_silu_is_fir_filter():
+    """Causal depthwise conv with taps w[c, k] on u_{n-K+1+k} is the FIR filter
+    lfilter(w[c, ::-1], [1], [conv_state; u]) restricted to the last L outputs."""
+    Bt, L, Di, K = 2, 37, 5, 4
+    rng = np.random.default_rng(17)
+    u = rng.standard_normal((Bt, L, Di))
+    w = rng.standard_normal((Di, K)) * 0.5
+    cs = rng.standard_normal((Bt, K - 1, Di))
+    for state in (None, cs):
+        pre, h = oracle.conv_silu(u, w, state)
+        for bb in range(Bt):
+            for c in range(Di):
+                head = np.zeros(K - 1) if state is None else state[bb, :, c]
+                full = np.concatenate([head, u[bb, :, c]])
+                ref = scipy.signal.lfilter(w[c, ::-1], [1.0], full)[K - 1:]
+                np.testing.assert_allclose(pre[bb, :, c], ref, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(h, pre * expit(pre), rtol=1e-14)
+
+
+def test_block_wiring_special_case():
+    """f = 1, i = 0, x0 = 0 (a = +inf, b = -inf): the scan contributes nothing and
+    y = D SiLU(conv(u)) SiLU(z); conv_state_out = last K-1 rows of [conv_state; u]."""
+    Bt, L, Di, N, K = 2, 9, 6, 16, 4
+    rng = np.random.default_rng(18)
+    u, z = rng.standard_normal((Bt, L, Di)), rng.standard_normal((Bt, L, Di))
+    w = rng.standard_normal((Di, K))
+    cs = rng.standard_normal((Bt, K - 1, Di))
+    a = np.full((Bt, L, Di), np.inf)
+    b = np.full((Bt, L, Di), -np.inf)
+    B, C = rng.standard_normal((Bt, L, N)), rng.standard_normal((Bt, L, N))
+    D = rng.standard_normal(Di)
+    y, xf, cso = oracle.block_fwd(u, z, w, a, b, B, C, D, None, cs)
+    full = np.concatenate([cs, u], axis=1)
+    pre = np.zeros((Bt, L, Di))
+    for k in range(K):
+        pre += w[:, k] * full[:, k: k + L, :]
+    h = pre * expit(pre)
+    np.testing.assert_allclose(y, D * h * z * expit(z), rtol=1e-13, atol=1e-14)
+    assert not xf.any()
+    assert np.array_equal(cso, full[:, -(K - 1):, :])
+    # short sequence (L < K-1): the state still shifts through
+    y2, _, cso2 = oracle.block_fwd(u[:, :2], z[:, :2], w, a[:, :2], b[:, :2], B[:, :2],
+                                   C[:, :2], D, None, cs)
+    assert np.array_equal(cso2, np.concatenate([cs, u[:, :2]], axis=1)[:, -(K - 1):])
+
+
+def test_block_chaining_with_conv_state():
+    d = inputs.draw(2, 40, 6, 16, io="f32", seed=19, block=True, x0=True)
+    d = {k: v.astype(np.float64) for k, v in d.items()}
+    args = dict(u=d["u"], z=d["z"], w=d["conv_w"], a=d["a"], b=d["b"], B=d["B"], C=d["C"],
+                D=d["D"], x0=d["x0"])
+    y, xf, cso = oracle.block_fwd(**args)
+    m = 13
+    tk = ("u", "z", "a", "b", "B", "C")
+    y1, x1, c1 = oracle.block_fwd(**{k: (v[:, :m] if k in tk else v) for k, v in args.items()})
+    rest = {k: (v[:, m:] if k in tk else v) for k, v in args.items()}
+    rest.update(x0=x1, conv_state=c1)
+    y2, x2, c2 = oracle.block_fwd(**rest)
+    np.testing.assert_allclose(np.concatenate([y1, y2], axis=1), y, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(x2, xf, rtol=1e-12, atol=1e-13)
+    assert np.array_equal(c2, cso)
+
+
+def test_nonfinite_gate_conventions():
+    """sigma(+inf) = 1, sigma(-inf) = 0 exactly; NaN in a gate propagates to that channel."""
+    d = rand_case(Bt=1, L=6, Di=3, N=16, seed=20)
+    d["a"][0, 2, 1] = np.nan
+    ys, xf = oracle.scan_fwd(**d)
+    assert np.isnan(ys[0, 2:, 1]).all() and np.isnan(xf[0, 1]).all()
+    assert np.isfinite(ys[0, :, [0, 2]]).all() and np.isfinite(ys[0, :2, 1]).all()
+    d = rand_case(Bt=1, L=6, Di=3, N=16, seed=21)
+    d["a"][0, 3, :] = -np.inf  # f = 0: full reset at token 3
+    _, xf = oracle.scan_fwd(**d)
+    tail = {k: (v[:, 3:] if k in ("h", "a", "b", "B", "C") else v) for k, v in d.items()}
+    tail["x0"] = None
+    _, xt = oracle.scan_fwd(**tail)
+    np.testing.assert_allclose(xf, xt, rtol=1e-14)
