@@ -1,0 +1,220 @@
+"""Benchmark of the Naju scan hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of the training
+workload (batch 8, seqlen 2048, d_inner 1536, d_state 16, bf16 activations,
+fp32 state): the fused block forward (conv+SiLU front end, gates, scan,
+readout, SiLU(z) modulation, checkpoints) followed by the block backward
+(reverse-time adjoint scan, every gradient).  Inputs are synthetic, drawn by
+the seeded generator, and resident in HBM before timing starts; three input
+sets rotate so the 256 MB Infinity Cache cannot hold a step's working set.
+
+Also timed in the same run: the scan forward alone (the kernel with the
+70%-of-HBM-peak target), the block forward alone, and the CPU oracle on a
+bounded sample of the same workload (the cpu_baseline leg).
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "scan tokens/sec + achieved HBM GB/s (% peak), fwd and fwd+bwd, L=2048"
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "train_bf16_b8_l2048_d1536_n16"
+NSETS = 3
+
+
+def alg_bytes(kind, Bt, L, Di, N, e, K=4):
+    """Algorithmic HBM bytes of one call (what the method must move)."""
+    tok, st = Bt * L * Di, Bt * Di * N
+    if kind == "scan_fwd":     # read h, a, b; write y; B, C; x_final; D
+        return tok * 4 * e + Bt * L * N * 2 * e + st * 4 + Di * 4
+    if kind == "block_fwd":    # read u, z, a, b; write y; B, C; x_final; D, conv_w
+        return tok * 5 * e + Bt * L * N * 2 * e + st * 4 + Di * 4 + Di * K * 4
+    if kind == "block_bwd":    # read u, z, a, b, dy; write du, dz, da, db; B, C, dB, dC; D, dD, w, dw
+        return tok * 9 * e + Bt * L * N * 4 * e + Di * 4 * 2 + Di * K * 4 * 2
+    raise ValueError(kind)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--only", choices=["all", "scan_fwd", "step"], default="all",
+                    help="restrict the timed work (for profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the Naju scan path has no multi-GPU "
+              "implementation here (see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from selective_state_space_naju_amd import binding as nb
+    from selective_state_space_naju_amd import inputs
+
+    dev = torch.device("cuda:0")
+    w = inputs.WORKLOADS[WORKLOAD]
+    Bt, L, Di, N = w.Bt, w.L, w.Di, w.N
+    e = 2
+    L_ = nb.lib()
+    d = inputs.draw_workload(w)
+    bf = lambda k: torch.from_numpy(d[k]).to(torch.bfloat16).to(dev)  # noqa: E731
+    f32 = lambda k: torch.from_numpy(d[k]).to(dev)  # noqa: E731
+    base = {k: bf(k) for k in ("u", "z", "a", "b", "B", "C", "dy")}
+    D, cw = f32("D"), f32("conv_w")
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(NSETS - 1)]
+    dims = nb.make_dims(Bt, L, Di, N, nb.BF16)
+    stream = nb.stream_handle(dev)
+    p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None  # noqa: E731
+
+    def alloc_outs():
+        o = {k: torch.empty((Bt, L, Di), dtype=torch.bfloat16, device=dev)
+             for k in ("y", "du", "dz", "da", "db")}
+        o["xf"] = torch.empty((Bt, Di, N), dtype=torch.float32, device=dev)
+        o["dB"] = torch.empty((Bt, L, N), dtype=torch.bfloat16, device=dev)
+        o["dC"] = torch.empty((Bt, L, N), dtype=torch.bfloat16, device=dev)
+        o["dD"] = torch.empty((Di,), dtype=torch.float32, device=dev)
+        o["dw"] = torch.empty((Di, 4), dtype=torch.float32, device=dev)
+        o["ck"] = torch.empty(nb.ckpt_bytes(dims) // 4, dtype=torch.float32, device=dev)
+        return o
+
+    outs = [alloc_outs() for _ in range(NSETS)]
+    ws_f = nb.Workspace(nb.workspace_bytes(nb.OP_BLOCK_FWD, dims), dev)
+    ws_b = nb.Workspace(nb.workspace_bytes(nb.OP_BLOCK_BWD, dims), dev)
+    ws_s = nb.Workspace(nb.workspace_bytes(nb.OP_SCAN_FWD, dims), dev)
+
+    def block_fwd(i):
+        s, o = sets[i], outs[i]
+        nb.check(L_.naju_block_fwd(ctypes.byref(dims), p(s["u"]), p(s["z"]), p(cw), None,
+                                   p(s["a"]), p(s["b"]), p(s["B"]), p(s["C"]), p(D), None,
+                                   p(o["y"]), p(o["xf"]), None, p(o["ck"]), ws_f.ptr,
+                                   ws_f.nbytes, stream))
+
+    def block_bwd(i):
+        s, o = sets[i], outs[i]
+        nb.check(L_.naju_block_bwd(ctypes.byref(dims), p(s["u"]), p(s["z"]), p(cw), None,
+                                   p(s["a"]), p(s["b"]), p(s["B"]), p(s["C"]), p(D), None,
+                                   p(o["ck"]), p(s["dy"]), None, p(o["du"]), p(o["dz"]),
+                                   p(o["dw"]), None, p(o["da"]), p(o["db"]), p(o["dB"]),
+                                   p(o["dC"]), p(o["dD"]), None, ws_b.ptr, ws_b.nbytes, stream))
+
+    def scan_fwd(i):
+        s, o = sets[i], outs[i]
+        nb.check(L_.naju_scan_fwd(ctypes.byref(dims), p(s["u"]), p(s["a"]), p(s["b"]),
+                                  p(s["B"]), p(s["C"]), p(D), None, p(o["y"]), p(o["xf"]), None,
+                                  ws_s.ptr, ws_s.nbytes, stream))
+
+    def timed_launches(fn, count):
+        """Per-launch GPU durations (ms) from events on the launch stream."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(count)]
+        torch.cuda.synchronize()
+        for k in range(count):
+            ev[k][0].record()
+            fn(k % NSETS)
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev])
+
+    # ---------------------------------------------------------------- warmup
+    for k in range(args.warmup):
+        block_fwd(k % NSETS)
+        block_bwd(k % NSETS)
+        scan_fwd(k % NSETS)
+    torch.cuda.synchronize()
+
+    res = {}
+    # ---------------------------------------------------------- timed steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        block_fwd(k % NSETS)
+        block_bwd(k % NSETS)
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    if args.only == "step":
+        pass
+    # per-kernel timing (after the timed steps, same inputs)
+    n_ev = max(args.steps, 10)
+    t_sf = timed_launches(scan_fwd, n_ev) if args.only in ("all", "scan_fwd") else None
+    t_bf = timed_launches(block_fwd, n_ev) if args.only in ("all", "step") else None
+    t_bb = timed_launches(block_bwd, n_ev) if args.only in ("all", "step") else None
+    for ws in (ws_f, ws_b, ws_s):
+        if ws.error_flags():
+            raise RuntimeError("a cross-workgroup wait gave up: results invalid")
+
+    tokens = Bt * L
+    parts = {}
+    for name, tt, kind in (("scan_fwd", t_sf, "scan_fwd"), ("block_fwd", t_bf, "block_fwd"),
+                           ("block_bwd", t_bb, "block_bwd")):
+        if tt is None:
+            continue
+        ms = float(np.median(tt))
+        by = alg_bytes(kind, Bt, L, Di, N, e)
+        parts[name] = {"ms_median": round(ms, 4), "ms_mean": round(float(tt.mean()), 4),
+                       "tokens_per_s": round(tokens / (ms * 1e-3), 1),
+                       "alg_bytes": int(by), "GB_per_s": round(by / (ms * 1e-3) / 1e9, 1),
+                       "pct_hbm_peak": round(100 * by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+
+    # roofline of the forward scan kernel (one kernel per call)
+    rf = None
+    if "scan_fwd" in parts:
+        by = parts["scan_fwd"]["alg_bytes"]
+        ms = parts["scan_fwd"]["ms_mean"]
+        ach = by / (ms * 1e-3) / 1e9
+        rf = {"kernel": "fwd_kernel<bf16,16,scan>", "bound": "hbm", "achieved": round(ach, 1),
+              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+              "traffic": None}
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        sub = {k: v[:1] for k, v in d.items() if k not in ("D", "conv_w")}
+        cores = len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        oracle.block_fwd(sub["u"], sub["z"], d["conv_w"], sub["a"], sub["b"], sub["B"],
+                         sub["C"], d["D"])
+        oracle.block_bwd(sub["u"], sub["z"], d["conv_w"], sub["a"], sub["b"], sub["B"],
+                         sub["C"], d["D"], None, sub["dy"])
+        tc = time.perf_counter() - t0
+        cpu = {"value": round(L / tc, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+               "sample": "block fwd+bwd of batch row 0 (1 x 2048 tokens x 1536 channels, "
+                         "d_state 16), fp64, %.2f s" % tc}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens / t_step, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": Bt, "seq_len": L, "d_inner": Di,
+                   "d_state": N, "io": "bf16", "state": "f32",
+                   "step": "block fwd (with checkpoints) + block bwd"},
+        "roofline": rf,
+        "cpu_baseline": cpu,
+        "parts": parts,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

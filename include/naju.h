@@ -1,0 +1,192 @@
+/*
+ * naju.h -- C ABI of libnaju.so, the MI355X (gfx950) implementation of the
+ * Naju native-discrete selective state scan and of the mixer-block pieces
+ * fused around it.
+ *
+ * The operation (Naju reproduction README of arXiv 2607.21000, section
+ * "Core equations"): for each batch row and channel c, with state row
+ * x[c, 0..N-1] (N = d_state),
+ *
+ *     x_n[c,s] = f_n[c] x_{n-1}[c,s] + i_n[c] h_n[c] B_n[s],
+ *     f_n = sigma(a_n),  i_n = sigma(b_n)            (retain / write gates)
+ *     ys_n[c]  = (1/sqrt(N)) sum_s x_n[c,s] C_n[s] + D[c] h_n[c]
+ *
+ * using the post-update state in the readout.  The gates and h are given per
+ * (token, channel); B_n and C_n are one N-vector per (batch, token), shared by
+ * every channel (the page's "token-dependent B/C directions").
+ *
+ * The block entry points add the front end and the output modulation of the
+ * same page's block flowchart: h = SiLU(causal depthwise conv1d(u)) with
+ * d_conv taps and no bias, and y = ys * SiLU(z).  The convolution is a
+ * cross-correlation whose last tap multiplies the current token:
+ *     pre_n[c] = sum_{k<K} conv_w[c,k] u_{n-K+1+k}[c]
+ * with u_m for m < 0 taken from conv_state (zeros if conv_state is NULL).
+ *
+ * The backward entry points are the reverse mode of these definitions.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layouts   row-major, contiguous, no strides:
+ *              per (token, channel) tensors: [batch][seqlen][d_inner]
+ *              per token tensors B, C, dB, dC: [batch][seqlen][d_state]
+ *              states x0, x_final, dx_final, dx0: [batch][d_inner][d_state] fp32
+ *              D, dD: [d_inner] fp32;  conv_w, dconv_w: [d_inner][d_conv] fp32
+ *              conv_state, conv_state_out, dconv_state: [batch][d_conv-1][d_inner]
+ *                (the d_conv-1 inputs that precede u_0, oldest first), io dtype
+ *  Dtypes    activations and their gradients use dims->io (fp32 or bf16);
+ *            parameters, states, checkpoints and dD/dconv_w are fp32.  Device
+ *            arithmetic is fp32; bf16 results are rounded to nearest even.
+ *  Pointers  every data pointer is a device pointer (hipMalloc'd or a torch
+ *            tensor), aligned to its element size; outputs must not alias
+ *            inputs.  `dims` is a host pointer.  Optional pointers may be NULL
+ *            as documented per argument.
+ *  Ownership the caller owns every buffer.  The library never allocates device
+ *            memory; it uses only the caller's workspace.
+ *  Stream    `stream` is a hipStream_t (NULL = the default stream).  Every call
+ *            only enqueues work on that stream and returns; nothing is
+ *            synchronised.
+ *  Workspace `ws` of at least naju_workspace_bytes(op, dims) bytes, zero-filled
+ *            before its first use (naju_workspace_init, or any zero fill).
+ *            Each call leaves it in a reusable state when its work completes,
+ *            for further calls of the same entry point with the same dims.
+ *            Zero-fill it again before using it for another entry point or
+ *            other dims.  Calls that share one workspace must be ordered (same
+ *            stream or explicit dependencies); concurrent calls need separate
+ *            workspaces.
+ *  Errors    arguments are validated before anything is enqueued: any status
+ *            other than NAJU_OK and NAJU_EHIP means nothing was enqueued.
+ *            NAJU_EHIP reports a HIP launch error.  naju_last_error() returns a
+ *            thread-local message describing the last failure.
+ *  Sizes     batch, seqlen, d_inner >= 0 (any zero makes the call a no-op
+ *            except for the state outputs: with seqlen == 0, x_final = x0 and
+ *            conv_state_out = conv_state).  d_state in {16, 64}; d_conv == 4
+ *            for the block entry points.
+ */
+#ifndef NAJU_H
+#define NAJU_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    NAJU_OK = 0,
+    NAJU_EINVAL = 1,       /* bad argument: NULL pointer, bad size, misalignment */
+    NAJU_EUNSUPPORTED = 2, /* valid but not built: d_state or d_conv not instantiated */
+    NAJU_EWORKSPACE = 3,   /* ws NULL or smaller than naju_workspace_bytes() */
+    NAJU_EHIP = 4          /* the HIP runtime reported an error */
+} naju_status_t;
+
+typedef enum { NAJU_F32 = 0, NAJU_BF16 = 1 } naju_dtype_t;
+
+typedef enum {
+    NAJU_OP_SCAN_FWD = 0,
+    NAJU_OP_SCAN_BWD = 1,
+    NAJU_OP_BLOCK_FWD = 2,
+    NAJU_OP_BLOCK_BWD = 3
+} naju_op_t;
+
+typedef struct {
+    int64_t batch;   /* Bt */
+    int64_t seqlen;  /* L */
+    int64_t d_inner; /* Di: channels */
+    int64_t d_state; /* N: 16 or 64 */
+    int32_t d_conv;  /* K: 4 (block entry points; ignored by the scan ones) */
+    int32_t io;      /* naju_dtype_t of activations and their gradients */
+} naju_dims_t;
+
+/* Bytes of workspace the entry point `op` needs for `dims` (0 if dims invalid). */
+size_t naju_workspace_bytes(naju_op_t op, const naju_dims_t *dims);
+
+/* Bytes of the optional forward checkpoint buffer (fp32 chunk-boundary states
+ * written by the forward and read by the backward).  Its layout is private to
+ * the library; it is valid only for the same dims. */
+size_t naju_ckpt_bytes(const naju_dims_t *dims);
+
+/* Zero-fills a workspace on `stream` (with a kernel, so it may be captured). */
+naju_status_t naju_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Synchronises `stream`, then reads the workspace's device-side error word:
+ * *flags = 0 if every cross-workgroup wait of the previous calls completed,
+ * nonzero if one gave up after its bounded spin (results are then invalid). */
+naju_status_t naju_workspace_check(const void *ws, size_t ws_bytes, void *stream,
+                                   uint32_t *flags);
+
+/*
+ * Scan forward: y = ys (readout + feedthrough), x_final = x_L.
+ *   h, a, b   [Bt][L][Di] io          token activations, forget and write
+ *                                     gate pre-activations
+ *   B, C      [Bt][L][N]  io          write / read directions
+ *   D         [Di] fp32               direct feedthrough
+ *   x0        [Bt][Di][N] fp32 or NULL (= zeros)  initial state
+ *   y         [Bt][L][Di] io          output (written)
+ *   x_final   [Bt][Di][N] fp32 or NULL            final state (written)
+ *   ckpt      naju_ckpt_bytes() or NULL           checkpoints for the backward
+ */
+naju_status_t naju_scan_fwd(const naju_dims_t *dims, const void *h, const void *a,
+                            const void *b, const void *B, const void *C, const float *D,
+                            const float *x0, void *y, float *x_final, float *ckpt, void *ws,
+                            size_t ws_bytes, void *stream);
+
+/*
+ * Scan backward.  Inputs are the forward's inputs plus
+ *   ckpt      from naju_scan_fwd on the same inputs, or NULL (recomputed)
+ *   dy        [Bt][L][Di] io          dLoss/dy
+ *   dx_final  [Bt][Di][N] fp32 or NULL (= zeros)  dLoss/dx_final
+ * Outputs (written, not accumulated):
+ *   dh, da, db [Bt][L][Di] io;  dB, dC [Bt][L][N] io;  dD [Di] fp32;
+ *   dx0 [Bt][Di][N] fp32 or NULL (skipped)
+ */
+naju_status_t naju_scan_bwd(const naju_dims_t *dims, const void *h, const void *a,
+                            const void *b, const void *B, const void *C, const float *D,
+                            const float *x0, const float *ckpt, const void *dy,
+                            const float *dx_final, void *dh, void *da, void *db, void *dB,
+                            void *dC, float *dD, float *dx0, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/*
+ * Block forward: y = ScanReadout(SiLU(conv(u)), a, b, B, C, D) * SiLU(z).
+ *   u, z          [Bt][L][Di] io      conv input and modulation input
+ *   conv_w        [Di][K] fp32        depthwise taps (no bias)
+ *   conv_state    [Bt][K-1][Di] io or NULL (= zeros)  inputs preceding u_0
+ *   a, b, B, C, D, x0                 as naju_scan_fwd
+ *   y             [Bt][L][Di] io      output (written)
+ *   x_final       [Bt][Di][N] fp32 or NULL
+ *   conv_state_out [Bt][K-1][Di] io or NULL: last K-1 rows of [conv_state; u]
+ *   ckpt          naju_ckpt_bytes() or NULL
+ */
+naju_status_t naju_block_fwd(const naju_dims_t *dims, const void *u, const void *z,
+                             const float *conv_w, const void *conv_state, const void *a,
+                             const void *b, const void *B, const void *C, const float *D,
+                             const float *x0, void *y, float *x_final, void *conv_state_out,
+                             float *ckpt, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Block backward.  Inputs: the block forward's inputs, ckpt (or NULL), dy and
+ * dx_final (or NULL).  Outputs (written):
+ *   du, dz, da, db [Bt][L][Di] io;  dB, dC [Bt][L][N] io;
+ *   dconv_w [Di][K] fp32;  dD [Di] fp32;
+ *   dconv_state [Bt][K-1][Di] io or NULL;  dx0 [Bt][Di][N] fp32 or NULL
+ */
+naju_status_t naju_block_bwd(const naju_dims_t *dims, const void *u, const void *z,
+                             const float *conv_w, const void *conv_state, const void *a,
+                             const void *b, const void *B, const void *C, const float *D,
+                             const float *x0, const float *ckpt, const void *dy,
+                             const float *dx_final, void *du, void *dz, float *dconv_w,
+                             void *dconv_state, void *da, void *db, void *dB, void *dC,
+                             float *dD, float *dx0, void *ws, size_t ws_bytes, void *stream);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+const char *naju_last_error(void);
+
+/* Library version string. */
+const char *naju_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NAJU_H */

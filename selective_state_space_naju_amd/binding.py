@@ -1,0 +1,292 @@
+"""ctypes binding of libnaju.so (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels of ``libnaju.so``;
+this module checks tensor shapes/dtypes, allocates outputs and the
+workspace with PyTorch, and passes raw device pointers plus the current
+HIP stream through the C ABI declared in ``include/naju.h``.  If the
+library is missing the import of any entry point raises -- there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnaju.so")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = range(5)
+F32, BF16 = 0, 1
+OP_SCAN_FWD, OP_SCAN_BWD, OP_BLOCK_FWD, OP_BLOCK_BWD = range(4)
+D_CONV = 4
+
+# every function the header declares (the CPU tests check the exports)
+EXPORTS = ("naju_workspace_bytes", "naju_ckpt_bytes", "naju_workspace_init",
+           "naju_workspace_check", "naju_scan_fwd", "naju_scan_bwd", "naju_block_fwd",
+           "naju_block_bwd", "naju_last_error", "naju_version")
+
+
+class NajuError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("naju status %d: %s" % (status, msg))
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("d_inner", ctypes.c_int64), ("d_state", ctypes.c_int64),
+                ("d_conv", ctypes.c_int32), ("io", ctypes.c_int32)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libnaju.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libnaju.so not found at %s; build it with "
+                              "`python -m selective_state_space_naju_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        dp = ctypes.POINTER(Dims)
+        L.naju_workspace_bytes.argtypes = [ctypes.c_int, dp]
+        L.naju_workspace_bytes.restype = sz
+        L.naju_ckpt_bytes.argtypes = [dp]
+        L.naju_ckpt_bytes.restype = sz
+        L.naju_workspace_init.argtypes = [vp, sz, vp]
+        L.naju_workspace_init.restype = st
+        L.naju_workspace_check.argtypes = [vp, sz, vp, ctypes.POINTER(ctypes.c_uint32)]
+        L.naju_workspace_check.restype = st
+        L.naju_scan_fwd.argtypes = [dp] + [vp] * 11 + [sz, vp]
+        L.naju_scan_fwd.restype = st
+        L.naju_block_fwd.argtypes = [dp] + [vp] * 15 + [sz, vp]
+        L.naju_block_fwd.restype = st
+        L.naju_scan_bwd.argtypes = [dp] + [vp] * 18 + [sz, vp]
+        L.naju_scan_bwd.restype = st
+        L.naju_block_bwd.argtypes = [dp] + [vp] * 24 + [sz, vp]
+        L.naju_block_bwd.restype = st
+        L.naju_last_error.argtypes = []
+        L.naju_last_error.restype = ctypes.c_char_p
+        L.naju_version.argtypes = []
+        L.naju_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().naju_last_error().decode()
+
+
+def check(status: int) -> None:
+    if status != OK:
+        raise NajuError(status, last_error())
+
+
+def make_dims(batch, seqlen, d_inner, d_state, io, d_conv=D_CONV) -> Dims:
+    return Dims(int(batch), int(seqlen), int(d_inner), int(d_state), int(d_conv), int(io))
+
+
+def workspace_bytes(op: int, dims: Dims) -> int:
+    return int(lib().naju_workspace_bytes(op, ctypes.byref(dims)))
+
+
+def ckpt_bytes(dims: Dims) -> int:
+    return int(lib().naju_ckpt_bytes(ctypes.byref(dims)))
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def stream_handle(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class Workspace:
+    """A zero-initialised device workspace (reused across calls on one stream)."""
+
+    def __init__(self, nbytes: int, device):
+        n = max(256, (int(nbytes) + 255) // 256 * 256)
+        self.tensor = torch.zeros(n, dtype=torch.uint8, device=device)
+        self.nbytes = n
+
+    @property
+    def ptr(self):
+        return ctypes.c_void_p(self.tensor.data_ptr())
+
+    def error_flags(self) -> int:
+        out = ctypes.c_uint32(0)
+        check(lib().naju_workspace_check(self.ptr, self.nbytes, stream_handle(self.tensor.device),
+                                         ctypes.byref(out)))
+        return int(out.value)
+
+
+_ws_cache: dict = {}
+
+
+def workspace(op: int, dims: Dims, device) -> Workspace:
+    """Cached workspace per (device, stream, op, dims): a workspace is only ever
+    reused by calls with the same layout, on one stream."""
+    dev = torch.device(device)
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream, op, dims.batch, dims.seqlen,
+           dims.d_inner, dims.d_state, dims.d_conv, dims.io)
+    ws = _ws_cache.get(key)
+    if ws is None:
+        ws = Workspace(workspace_bytes(op, dims), dev)
+        _ws_cache[key] = ws
+    return ws
+
+
+def _io_of(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("activations must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _req(t, name, shape, dtype, device):
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, t.dtype))
+    if t.device != device:
+        raise ValueError("%s must be on %s" % (name, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _opt(t, name, shape, dtype, device):
+    return None if t is None else _req(t, name, shape, dtype, device)
+
+
+# ------------------------------------------------------------------ entry points
+def scan_fwd(h, a, b, B, C, D, x0=None, *, return_ckpt=False, ws=None):
+    """y, x_final (, ckpt) = naju_scan_fwd(h, a, b, B, C, D, x0)."""
+    Bt, L, Di = h.shape
+    N = B.shape[-1]
+    dt, dev = h.dtype, h.device
+    io = _io_of(h)
+    for nm, t in (("h", h), ("a", a), ("b", b)):
+        _req(t, nm, (Bt, L, Di), dt, dev)
+    _req(B, "B", (Bt, L, N), dt, dev)
+    _req(C, "C", (Bt, L, N), dt, dev)
+    _req(D, "D", (Di,), torch.float32, dev)
+    _opt(x0, "x0", (Bt, Di, N), torch.float32, dev)
+    dims = make_dims(Bt, L, Di, N, io)
+    y = torch.empty((Bt, L, Di), dtype=dt, device=dev)
+    xf = torch.empty((Bt, Di, N), dtype=torch.float32, device=dev)
+    ck = None
+    if return_ckpt:
+        ck = torch.empty(ckpt_bytes(dims) // 4, dtype=torch.float32, device=dev)
+    ws = ws or workspace(OP_SCAN_FWD, dims, dev)
+    check(lib().naju_scan_fwd(ctypes.byref(dims), _p(h), _p(a), _p(b), _p(B), _p(C), _p(D),
+                              _p(x0), _p(y), _p(xf), _p(ck), ws.ptr, ws.nbytes,
+                              stream_handle(dev)))
+    return (y, xf, ck) if return_ckpt else (y, xf)
+
+
+def block_fwd(u, z, conv_w, a, b, B, C, D, x0=None, conv_state=None, *, return_ckpt=False,
+              ws=None):
+    """y, x_final, conv_state_out (, ckpt) = naju_block_fwd(...)."""
+    Bt, L, Di = u.shape
+    N = B.shape[-1]
+    dt, dev = u.dtype, u.device
+    io = _io_of(u)
+    for nm, t in (("u", u), ("z", z), ("a", a), ("b", b)):
+        _req(t, nm, (Bt, L, Di), dt, dev)
+    _req(B, "B", (Bt, L, N), dt, dev)
+    _req(C, "C", (Bt, L, N), dt, dev)
+    _req(D, "D", (Di,), torch.float32, dev)
+    _req(conv_w, "conv_w", (Di, D_CONV), torch.float32, dev)
+    _opt(x0, "x0", (Bt, Di, N), torch.float32, dev)
+    _opt(conv_state, "conv_state", (Bt, D_CONV - 1, Di), dt, dev)
+    dims = make_dims(Bt, L, Di, N, io)
+    y = torch.empty((Bt, L, Di), dtype=dt, device=dev)
+    xf = torch.empty((Bt, Di, N), dtype=torch.float32, device=dev)
+    cso = torch.empty((Bt, D_CONV - 1, Di), dtype=dt, device=dev)
+    ck = None
+    if return_ckpt:
+        ck = torch.empty(ckpt_bytes(dims) // 4, dtype=torch.float32, device=dev)
+    ws = ws or workspace(OP_BLOCK_FWD, dims, dev)
+    check(lib().naju_block_fwd(ctypes.byref(dims), _p(u), _p(z), _p(conv_w), _p(conv_state),
+                               _p(a), _p(b), _p(B), _p(C), _p(D), _p(x0), _p(y), _p(xf),
+                               _p(cso), _p(ck), ws.ptr, ws.nbytes, stream_handle(dev)))
+    return (y, xf, cso, ck) if return_ckpt else (y, xf, cso)
+
+
+def scan_bwd(h, a, b, B, C, D, dy, x0=None, dx_final=None, ckpt=None, *, want_dx0=True,
+             ws=None):
+    """Gradients of naju_scan_fwd: dict(dh, da, db, dB, dC, dD, dx0)."""
+    Bt, L, Di = h.shape
+    N = B.shape[-1]
+    dt, dev = h.dtype, h.device
+    io = _io_of(h)
+    for nm, t in (("h", h), ("a", a), ("b", b), ("dy", dy)):
+        _req(t, nm, (Bt, L, Di), dt, dev)
+    _req(B, "B", (Bt, L, N), dt, dev)
+    _req(C, "C", (Bt, L, N), dt, dev)
+    _req(D, "D", (Di,), torch.float32, dev)
+    _opt(x0, "x0", (Bt, Di, N), torch.float32, dev)
+    _opt(dx_final, "dx_final", (Bt, Di, N), torch.float32, dev)
+    dims = make_dims(Bt, L, Di, N, io)
+    out = {k: torch.empty((Bt, L, Di), dtype=dt, device=dev) for k in ("dh", "da", "db")}
+    out["dB"] = torch.empty((Bt, L, N), dtype=dt, device=dev)
+    out["dC"] = torch.empty((Bt, L, N), dtype=dt, device=dev)
+    out["dD"] = torch.empty((Di,), dtype=torch.float32, device=dev)
+    out["dx0"] = torch.empty((Bt, Di, N), dtype=torch.float32, device=dev) if want_dx0 else None
+    ws = ws or workspace(OP_SCAN_BWD, dims, dev)
+    check(lib().naju_scan_bwd(ctypes.byref(dims), _p(h), _p(a), _p(b), _p(B), _p(C), _p(D),
+                              _p(x0), _p(ckpt), _p(dy), _p(dx_final), _p(out["dh"]),
+                              _p(out["da"]), _p(out["db"]), _p(out["dB"]), _p(out["dC"]),
+                              _p(out["dD"]), _p(out["dx0"]), ws.ptr, ws.nbytes,
+                              stream_handle(dev)))
+    return out
+
+
+def block_bwd(u, z, conv_w, a, b, B, C, D, dy, x0=None, dx_final=None, conv_state=None,
+              ckpt=None, *, want_dx0=True, want_dconv_state=True, ws=None):
+    """Gradients of naju_block_fwd: dict(du, dz, dconv_w, dconv_state, da, db, dB, dC, dD, dx0)."""
+    Bt, L, Di = u.shape
+    N = B.shape[-1]
+    dt, dev = u.dtype, u.device
+    io = _io_of(u)
+    for nm, t in (("u", u), ("z", z), ("a", a), ("b", b), ("dy", dy)):
+        _req(t, nm, (Bt, L, Di), dt, dev)
+    _req(B, "B", (Bt, L, N), dt, dev)
+    _req(C, "C", (Bt, L, N), dt, dev)
+    _req(D, "D", (Di,), torch.float32, dev)
+    _req(conv_w, "conv_w", (Di, D_CONV), torch.float32, dev)
+    _opt(x0, "x0", (Bt, Di, N), torch.float32, dev)
+    _opt(dx_final, "dx_final", (Bt, Di, N), torch.float32, dev)
+    _opt(conv_state, "conv_state", (Bt, D_CONV - 1, Di), dt, dev)
+    dims = make_dims(Bt, L, Di, N, io)
+    out = {k: torch.empty((Bt, L, Di), dtype=dt, device=dev) for k in ("du", "dz", "da", "db")}
+    out["dB"] = torch.empty((Bt, L, N), dtype=dt, device=dev)
+    out["dC"] = torch.empty((Bt, L, N), dtype=dt, device=dev)
+    out["dD"] = torch.empty((Di,), dtype=torch.float32, device=dev)
+    out["dconv_w"] = torch.empty((Di, D_CONV), dtype=torch.float32, device=dev)
+    out["dconv_state"] = (torch.empty((Bt, D_CONV - 1, Di), dtype=dt, device=dev)
+                          if want_dconv_state else None)
+    out["dx0"] = torch.empty((Bt, Di, N), dtype=torch.float32, device=dev) if want_dx0 else None
+    ws = ws or workspace(OP_BLOCK_BWD, dims, dev)
+    check(lib().naju_block_bwd(ctypes.byref(dims), _p(u), _p(z), _p(conv_w), _p(conv_state),
+                               _p(a), _p(b), _p(B), _p(C), _p(D), _p(x0), _p(ckpt), _p(dy),
+                               _p(dx_final), _p(out["du"]), _p(out["dz"]), _p(out["dconv_w"]),
+                               _p(out["dconv_state"]), _p(out["da"]), _p(out["db"]),
+                               _p(out["dB"]), _p(out["dC"]), _p(out["dD"]), _p(out["dx0"]),
+                               ws.ptr, ws.nbytes, stream_handle(dev)))
+    return out

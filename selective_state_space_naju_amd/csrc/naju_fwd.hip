@@ -1,0 +1,323 @@
+// naju_fwd.hip -- forward kernel of the Naju selective scan (scan and block).
+//
+// Recurrence and readout: "Core equations" of the Naju reproduction README
+// (arXiv 2607.21000); block front end / output modulation: that page's block
+// flowchart.  The sequence is cut into chunks; a chunk's effect on the state
+// is the affine map x -> P x + S (P = prod f, S = state reached from zero),
+// and composing these maps in order is exactly the sequential recurrence (the
+// page's "Scope" section calls the sequential loop mathematically equivalent
+// to the affine scan).
+//
+// Work decomposition (one launch):
+//   workgroup = W waves; one wave = CPW channels x T consecutive tokens; the W
+//   waves of a workgroup take W consecutive token chunks of the same channels.
+//   Lanes: LPC = N/16 lanes per channel, each holding 16 fp32 states in VGPRs.
+//   1. every wave runs the recurrence from a zero state over its T tokens,
+//      keeping the local readout ys_loc[j] and the running product P_j;
+//   2. the waves' (P, S) pairs are composed through LDS;
+//   3. wave 0 publishes the workgroup aggregate, then obtains the state
+//      entering the workgroup by decoupled look-back over its predecessors'
+//      published aggregates / inclusive states (tickets are taken in launch
+//      order, so every predecessor is already running and never waits on a
+//      successor);
+//   4. every wave adds the contribution of its entering state,
+//        y_j = ys_loc[j] + P_j (x_in . C_j) / sqrt(N),
+//      applies SiLU(z) for the block, and stores y.
+#include "naju_device.h"
+#include "naju_launch.h"
+
+namespace naju {
+
+template <typename IO, int N, bool BLOCK, int T, int W>
+__global__ __launch_bounds__(64 * W) void fwd_kernel(
+    const int64_t Bt, const int64_t L, const int64_t Di, const int n_tiles, const int n_chunks,
+    const float scale, const IO *__restrict__ hu, const IO *__restrict__ a,
+    const IO *__restrict__ bg, const IO *__restrict__ Bm, const IO *__restrict__ Cm,
+    const float *__restrict__ D, const float *__restrict__ x0, const IO *__restrict__ z,
+    const float *__restrict__ conv_w, const IO *__restrict__ conv_state, IO *__restrict__ y,
+    float *__restrict__ x_final, IO *__restrict__ conv_state_out, float *__restrict__ ckpt,
+    WsHeader *hdr, uint32_t *flags, float *agg, float *incl)
+{
+    constexpr int LPC = N / 16;   // lanes per channel
+    constexpr int CPW = 64 / LPC; // channels per wave
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+
+    __shared__ uint32_t s_ticket, s_epoch;
+    __shared__ float sP[W][64];
+    __shared__ float sS[W][16][64];
+    __shared__ float sX[16][64];
+
+    if (threadIdx.x == 0) {
+        s_ticket = add_agent(&hdr->ticket, 1u);
+        s_epoch = (ld_agent(&hdr->epoch) + 1u) & 0x3FFFFFFFu;
+    }
+    __syncthreads();
+    const uint32_t ticket = s_ticket;
+    const uint32_t ep = s_epoch;
+    const uint32_t per_chunk = (uint32_t)(Bt * n_tiles);
+    const int chunk = (int)(ticket / per_chunk);
+    const int rem = (int)(ticket % per_chunk);
+    const int bi = rem / n_tiles;
+    const int tile = rem % n_tiles;
+
+    const int sg = lane % LPC;
+    const int64_t c = (int64_t)tile * CPW + lane / LPC;
+    const bool valid = c < Di;
+    const int64_t n0 = (int64_t)chunk * (W * T) + (int64_t)wv * T;
+    const float Dc = valid ? D[c] : 0.f;
+
+    // ---------------------------------------------------------- block front end
+    float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f, um1 = 0.f, um2 = 0.f, um3 = 0.f;
+    if constexpr (BLOCK) {
+        if (valid) {
+            w0 = conv_w[c * 4 + 0];
+            w1 = conv_w[c * 4 + 1];
+            w2 = conv_w[c * 4 + 2];
+            w3 = conv_w[c * 4 + 3];
+            float halo[3];
+#pragma unroll
+            for (int k = 1; k <= 3; ++k) {
+                const int64_t m = n0 - k;
+                float v = 0.f;
+                if (m >= 0 && m < L)
+                    v = to_f(hu[((int64_t)bi * L + m) * Di + c]);
+                else if (m < 0 && conv_state)
+                    v = to_f(conv_state[((int64_t)bi * 3 + (m + 3)) * Di + c]);
+                halo[k - 1] = v;
+            }
+            um1 = halo[0];
+            um2 = halo[1];
+            um3 = halo[2];
+        }
+    }
+
+    // ------------------------------------------------------ 1. local recurrence
+    float x[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) x[s] = 0.f;
+    float P = 1.f;
+    float ysl[T], Pn[T];
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+        const int64_t n = n0 + j;
+        ysl[j] = 0.f;
+        Pn[j] = P;
+        if (n < L) {
+            const int64_t t = ((int64_t)bi * L + n) * Di + c;
+            float av = 0.f, bv = 0.f, hv = 0.f;
+            if (valid) {
+                av = to_f(a[t]);
+                bv = to_f(bg[t]);
+                if constexpr (BLOCK) {
+                    const float uv = to_f(hu[t]);
+                    const float pre = w0 * um3 + w1 * um2 + w2 * um1 + w3 * uv;
+                    um3 = um2;
+                    um2 = um1;
+                    um1 = uv;
+                    hv = pre * sigm(pre);
+                } else {
+                    hv = to_f(hu[t]);
+                }
+            }
+            const float f = sigm(av);
+            const float wr = sigm(bv) * hv;
+            const IO *Bn = Bm + ((int64_t)bi * L + n) * N + sg * 16;
+            const IO *Cn = Cm + ((int64_t)bi * L + n) * N + sg * 16;
+            float acc = 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                x[s] = fmaf(f, x[s], wr * to_f(Bn[s]));
+                acc = fmaf(x[s], to_f(Cn[s]), acc);
+            }
+            if constexpr (LPC > 1) {
+                acc += __shfl_xor(acc, 1);
+                acc += __shfl_xor(acc, 2);
+            }
+            P *= f;
+            ysl[j] = fmaf(scale, acc, Dc * hv);
+            Pn[j] = P;
+        }
+    }
+
+    // ------------------------------------------ 2. compose the waves' pairs
+    sP[wv][lane] = P;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) sS[wv][s][lane] = x[s];
+    __syncthreads();
+
+    // exclusive prefix of this wave inside the workgroup: x_w = Pe x_wg + Se
+    float Pe = 1.f, Se[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) Se[s] = 0.f;
+    for (int w = 0; w < wv; ++w) {
+        const float pw = sP[w][lane];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) Se[s] = fmaf(pw, Se[s], sS[w][s][lane]);
+        Pe *= pw;
+    }
+
+    // ------------------------------------- 3. look-back for the entering state
+    if (wv == 0) {
+        // workgroup aggregate (all W waves)
+        float Pt = 1.f, St[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) St[s] = 0.f;
+        for (int w = 0; w < W; ++w) {
+            const float pw = sP[w][lane];
+#pragma unroll
+            for (int s = 0; s < 16; ++s) St[s] = fmaf(pw, St[s], sS[w][s][lane]);
+            Pt *= pw;
+        }
+        const size_t me = ((size_t)bi * n_tiles + tile) * n_chunks + chunk;
+        float xin[16];
+        if (chunk == 0) {
+#pragma unroll
+            for (int s = 0; s < 16; ++s)
+                xin[s] = (x0 && valid) ? x0[(bi * Di + c) * N + sg * 16 + s] : 0.f;
+        } else {
+            float *ag = agg + me * (17 * 64);
+            st_agent(ag + lane, Pt);
+#pragma unroll
+            for (int s = 0; s < 16; ++s) st_agent(ag + (1 + s) * 64 + lane, St[s]);
+            wait_mem();
+            if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagAgg));
+            float accP = 1.f, accS[16];
+#pragma unroll
+            for (int s = 0; s < 16; ++s) accS[s] = 0.f;
+            size_t j = me - 1;
+            for (;;) {
+                const uint32_t st = wait_flag(&flags[j], ep, hdr);
+                if (st == kFlagIncl) {
+                    const float *in = incl + j * (16 * 64);
+#pragma unroll
+                    for (int s = 0; s < 16; ++s)
+                        xin[s] = fmaf(accP, ld_agent(in + s * 64 + lane), accS[s]);
+                    break;
+                }
+                const float *pa = agg + j * (17 * 64);
+                const float pj = ld_agent(pa + lane);
+#pragma unroll
+                for (int s = 0; s < 16; ++s) accS[s] = fmaf(accP, ld_agent(pa + (1 + s) * 64 + lane), accS[s]);
+                accP *= pj;
+                --j;  // chunk 0 always publishes an inclusive state, so j stays >= first
+            }
+        }
+        float *ic = incl + me * (16 * 64);
+        float xo[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            xo[s] = fmaf(Pt, xin[s], St[s]);
+            st_agent(ic + s * 64 + lane, xo[s]);
+        }
+        wait_mem();
+        if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagIncl));
+#pragma unroll
+        for (int s = 0; s < 16; ++s) sX[s][lane] = xin[s];
+        if (valid) {
+            if (chunk == n_chunks - 1 && x_final) {
+#pragma unroll
+                for (int s = 0; s < 16; ++s) x_final[(bi * Di + c) * N + sg * 16 + s] = xo[s];
+            }
+            if constexpr (BLOCK) {
+                if (chunk == n_chunks - 1 && conv_state_out && sg == 0) {
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) {
+                        const int64_t m = L - 3 + k;
+                        IO v = from_f<IO>(0.f);
+                        if (m >= 0)
+                            v = hu[((int64_t)bi * L + m) * Di + c];
+                        else if (conv_state)
+                            v = conv_state[((int64_t)bi * 3 + (m + 3)) * Di + c];
+                        conv_state_out[((int64_t)bi * 3 + k) * Di + c] = v;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ------------------------------------------ 4. correction, modulation, store
+    float xin[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) xin[s] = fmaf(Pe, sX[s][lane], Se[s]);
+    // checkpoint: the state entering this wave's T tokens
+    if (ckpt && valid && n0 < L) {
+        const int64_t wrow = (int64_t)chunk * W + wv;
+        const int64_t n_waves = (L + T - 1) / T;
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+            ckpt[(((int64_t)bi * n_waves + wrow) * N + sg * 16 + s) * Di + c] = xin[s];
+    }
+    if (y) {
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+            const int64_t n = n0 + j;
+            if (n < L) {
+                const IO *Cn = Cm + ((int64_t)bi * L + n) * N + sg * 16;
+                float dot = 0.f;
+#pragma unroll
+                for (int s = 0; s < 16; ++s) dot = fmaf(xin[s], to_f(Cn[s]), dot);
+                if constexpr (LPC > 1) {
+                    dot += __shfl_xor(dot, 1);
+                    dot += __shfl_xor(dot, 2);
+                }
+                float yv = fmaf(scale * Pn[j], dot, ysl[j]);
+                const int64_t t = ((int64_t)bi * L + n) * Di + c;
+                if (valid && sg == 0) {
+                    if constexpr (BLOCK) {
+                        const float zv = to_f(z[t]);
+                        yv *= zv * sigm(zv);
+                    }
+                    y[t] = from_f<IO>(yv);
+                }
+            }
+        }
+    }
+
+    // ------------------------------------------------ release the workspace
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t total = per_chunk * (uint32_t)n_chunks;
+        const uint32_t old = add_agent(&hdr->done, 1u);
+        if (old == total - 1) {
+            st_agent(&hdr->ticket, 0u);
+            st_agent(&hdr->done, 0u);
+            st_agent(&hdr->epoch, ep);
+        }
+    }
+}
+
+// ---------------------------------------------------------------- launcher
+template <typename IO, int N, bool BLOCK>
+static hipError_t launch_fwd_t(const FwdArgs &g, hipStream_t stream)
+{
+    constexpr int T = kFwdT, W = kFwdW;
+    const FwdPlan pl = fwd_plan(g.Bt, g.L, g.Di, g.N);
+    WsHeader *hdr = (WsHeader *)g.ws;
+    uint32_t *flags = (uint32_t *)((char *)g.ws + pl.off_flags);
+    float *agg = (float *)((char *)g.ws + pl.off_agg);
+    float *incl = (float *)((char *)g.ws + pl.off_incl);
+    hipLaunchKernelGGL((fwd_kernel<IO, N, BLOCK, T, W>), dim3(pl.n_wg), dim3(64 * W), 0, stream,
+                       g.Bt, g.L, g.Di, pl.n_tiles, pl.n_chunks, g.scale, (const IO *)g.hu,
+                       (const IO *)g.a, (const IO *)g.b, (const IO *)g.B, (const IO *)g.C, g.D,
+                       g.x0, (const IO *)g.z, g.conv_w, (const IO *)g.conv_state, (IO *)g.y,
+                       g.x_final, (IO *)g.conv_state_out, g.ckpt, hdr, flags, agg, incl);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs &g, hipStream_t stream)
+{
+    if (g.io == 0) {
+        if (g.N == 16) return g.block ? launch_fwd_t<float, 16, true>(g, stream)
+                                      : launch_fwd_t<float, 16, false>(g, stream);
+        return g.block ? launch_fwd_t<float, 64, true>(g, stream)
+                       : launch_fwd_t<float, 64, false>(g, stream);
+    }
+    if (g.N == 16) return g.block ? launch_fwd_t<bf16, 16, true>(g, stream)
+                                  : launch_fwd_t<bf16, 16, false>(g, stream);
+    return g.block ? launch_fwd_t<bf16, 64, true>(g, stream)
+                   : launch_fwd_t<bf16, 64, false>(g, stream);
+}
+
+}  // namespace naju

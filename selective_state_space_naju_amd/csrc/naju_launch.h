@@ -1,0 +1,130 @@
+// naju_launch.h -- host-side plans (grid shapes, workspace layout) shared by
+// the C-ABI layer and the kernel launchers of libnaju.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace naju {
+
+// Forward decomposition: a wave owns kFwdT tokens of 64/LPC channels, a
+// workgroup kFwdW consecutive waves along the sequence.
+constexpr int kFwdT = 32;
+constexpr int kFwdW = 8;
+// Backward: same wave shape (checkpoints are taken per forward wave).
+constexpr int kBwdT = 32;
+constexpr int kBwdW = 8;
+constexpr int kBwdTB = 8;  // tokens recomputed per sub-block
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct FwdPlan {
+    int n_tiles;      // channel tiles of 64/LPC channels
+    int n_chunks;     // workgroup chunks of kFwdT*kFwdW tokens
+    int64_t n_wg;     // workgroups = tickets
+    int64_t n_waves;  // kFwdT-token chunks (checkpoint rows) per batch row
+    size_t off_flags, off_agg, off_incl, bytes;
+};
+
+inline FwdPlan fwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N)
+{
+    FwdPlan p{};
+    const int64_t cpw = 64 / (N / 16);
+    p.n_tiles = (int)((Di + cpw - 1) / cpw);
+    p.n_chunks = (int)((L + kFwdT * kFwdW - 1) / (kFwdT * kFwdW));
+    p.n_wg = Bt * p.n_tiles * p.n_chunks;
+    p.n_waves = (L + kFwdT - 1) / kFwdT;
+    p.off_flags = 256;
+    p.off_agg = align256(p.off_flags + 4 * (size_t)p.n_wg);
+    p.off_incl = align256(p.off_agg + 17 * 64 * 4 * (size_t)p.n_wg);
+    p.bytes = align256(p.off_incl + 16 * 64 * 4 * (size_t)p.n_wg);
+    return p;
+}
+
+// checkpoint: the state entering every kFwdT-token chunk, [Bt][n_waves][N][Di] fp32
+inline size_t ckpt_bytes(int64_t Bt, int64_t L, int64_t Di, int64_t N)
+{
+    return (size_t)Bt * (size_t)((L + kFwdT - 1) / kFwdT) * (size_t)N * (size_t)Di * 4;
+}
+
+struct BwdPlan {
+    int n_tiles, n_chunks;
+    int64_t n_wg, n_waves;
+    size_t off_flags, off_agg, off_incl;  // reverse look-back (same shapes as forward)
+    size_t off_bc;    // dB/dC partials   [Bt][L][n_tiles][2N] fp32
+    size_t off_dd;    // dD partials      [Bt][n_waves][Di] fp32
+    size_t off_dw;    // dconv_w partials [Bt][n_waves][Di][4] fp32
+    size_t off_edge;  // block: per wave boundary  [Bt][n_waves][6][Di] fp32
+                      //   rows 0-2: dpre of the wave's first 3 tokens
+                      //   rows 3-5: in-wave partial du of its last 3 tokens
+    size_t off_ckpt;  // recomputed checkpoints when the caller passes none
+    size_t off_fwd;   // workspace of the checkpoint-only forward
+    size_t bytes;
+};
+
+inline BwdPlan bwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N, bool block)
+{
+    BwdPlan p{};
+    const FwdPlan f = fwd_plan(Bt, L, Di, N);
+    p.n_tiles = f.n_tiles;
+    p.n_chunks = f.n_chunks;
+    p.n_wg = f.n_wg;
+    p.n_waves = f.n_waves;
+    p.off_flags = f.off_flags;
+    p.off_agg = f.off_agg;
+    p.off_incl = f.off_incl;
+    p.off_bc = f.bytes;
+    p.off_dd = align256(p.off_bc + (size_t)Bt * L * p.n_tiles * 2 * N * 4);
+    p.off_dw = align256(p.off_dd + (size_t)Bt * p.n_waves * Di * 4);
+    p.off_edge = align256(p.off_dw + (block ? (size_t)Bt * p.n_waves * Di * 4 * 4 : 0));
+    p.off_ckpt = align256(p.off_edge + (block ? (size_t)Bt * p.n_waves * 6 * Di * 4 : 0));
+    p.off_fwd = align256(p.off_ckpt + ckpt_bytes(Bt, L, Di, N));
+    p.bytes = align256(p.off_fwd + f.bytes);
+    return p;
+}
+
+struct FwdArgs {
+    int io, N;
+    bool block;
+    int64_t Bt, L, Di;
+    float scale;
+    const void *hu, *a, *b, *B, *C;
+    const float *D, *x0;
+    const void *z;
+    const float *conv_w;
+    const void *conv_state;
+    void *y;
+    float *x_final;
+    void *conv_state_out;
+    float *ckpt;
+    void *ws;  // forward workspace (fwd_plan layout)
+};
+
+struct BwdArgs {
+    int io, N;
+    bool block;
+    int64_t Bt, L, Di;
+    float scale;
+    const void *hu, *a, *b, *B, *C;
+    const float *D, *x0;
+    const void *z;
+    const float *conv_w;
+    const void *conv_state;
+    const float *ckpt;  // required here (the API layer recomputes it if absent)
+    const void *dy;
+    const float *dx_final;
+    void *dhu, *da, *db, *dB, *dC, *dz;
+    float *dD, *dx0, *dconv_w;
+    void *dconv_state;
+    void *ws;  // backward workspace (bwd_plan layout)
+};
+
+hipError_t launch_fwd(const FwdArgs &g, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs &g, hipStream_t stream);
+hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
+hipError_t launch_empty_seq(int io, int64_t Bt, int64_t Di, int64_t N, const float *x0,
+                            float *x_final, const void *conv_state, void *conv_state_out,
+                            hipStream_t stream);
+
+}  // namespace naju

@@ -1,0 +1,119 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/naju.h declares, the binding's argument counts match the header, and
+argument validation rejects bad calls before anything is enqueued (no GPU is
+touched by any call here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_state_space_naju_amd import binding as nb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "naju.h")
+
+
+def header_prototypes():
+    """name -> number of parameters, for every function declared in naju.h."""
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    protos = {}
+    for m in re.finditer(r"\b(naju_\w+)\s*\(([^;{]*?)\)\s*;", src, flags=re.S):
+        name, params = m.group(1), m.group(2).strip()
+        protos[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return protos
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(nb.LIB_PATH):
+        pytest.fail("libnaju.so is not built (run __graft_entry__.build())")
+    return nb.lib()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    protos = header_prototypes()
+    assert set(protos) == set(nb.EXPORTS)
+    for name in protos:
+        assert hasattr(lib, name), name
+
+
+def test_binding_argument_counts_match_header(lib):
+    for name, n in header_prototypes().items():
+        assert len(getattr(lib, name).argtypes) == n, name
+
+
+def test_version(lib):
+    assert b"gfx950" in lib.naju_version()
+
+
+def dims(**kw):
+    d = dict(batch=2, seqlen=300, d_inner=100, d_state=16, io=nb.BF16)
+    d.update(kw)
+    return nb.make_dims(d["batch"], d["seqlen"], d["d_inner"], d["d_state"], d["io"],
+                        d.get("d_conv", 4))
+
+
+FAKE = 0x100000  # a 256-byte aligned non-null address; never dereferenced
+
+
+def call_scan_fwd(lib, d, **over):
+    args = dict(h=FAKE, a=FAKE, b=FAKE, B=FAKE, C=FAKE, D=FAKE, x0=None, y=FAKE, xf=None,
+                ck=None, ws=FAKE, wsb=1 << 40)
+    args.update(over)
+    v = [args[k] for k in ("h", "a", "b", "B", "C", "D", "x0", "y", "xf", "ck", "ws")]
+    return lib.naju_scan_fwd(ctypes.byref(d) if d is not None else None, *v, args["wsb"], None)
+
+
+def test_validation_errors_scan_fwd(lib):
+    assert call_scan_fwd(lib, None) == nb.EINVAL
+    assert call_scan_fwd(lib, dims(batch=-1)) == nb.EINVAL
+    assert call_scan_fwd(lib, dims(d_state=32)) == nb.EUNSUPPORTED
+    assert call_scan_fwd(lib, dims(d_state=0)) == nb.EINVAL
+    assert call_scan_fwd(lib, dims(io=7)) == nb.EINVAL
+    assert call_scan_fwd(lib, dims(), h=None) == nb.EINVAL
+    assert "h is NULL" in nb.last_error()
+    assert call_scan_fwd(lib, dims(), C=FAKE + 1) == nb.EINVAL
+    assert "aligned" in nb.last_error()
+    assert call_scan_fwd(lib, dims(), ws=None) == nb.EWORKSPACE
+    assert call_scan_fwd(lib, dims(), wsb=16) == nb.EWORKSPACE
+    assert call_scan_fwd(lib, dims(), ws=FAKE + 64) == nb.EINVAL
+    # empty problems are valid no-ops (nothing to enqueue)
+    assert call_scan_fwd(lib, dims(batch=0), h=None, ws=None) == nb.OK
+    assert call_scan_fwd(lib, dims(d_inner=0), h=None, ws=None) == nb.OK
+
+
+def test_validation_errors_block(lib):
+    d = dims(d_conv=3)
+    v = [FAKE] * 15
+    assert lib.naju_block_fwd(ctypes.byref(d), *v, 1 << 40, None) == nb.EUNSUPPORTED
+    d = dims(d_conv=0)
+    assert lib.naju_block_fwd(ctypes.byref(d), *v, 1 << 40, None) == nb.EINVAL
+    d = dims()
+    v2 = list(v)
+    v2[1] = None  # z
+    assert lib.naju_block_fwd(ctypes.byref(d), *v2, 1 << 40, None) == nb.EINVAL
+    assert "z is NULL" in nb.last_error()
+    vb = [FAKE] * 24
+    vb[13] = None  # du
+    assert lib.naju_block_bwd(ctypes.byref(d), *vb, 1 << 40, None) == nb.EINVAL
+    assert "du is NULL" in nb.last_error()
+
+
+def test_workspace_and_ckpt_sizes(lib):
+    d = dims(batch=8, seqlen=2048, d_inner=1536)
+    for op in range(4):
+        assert nb.workspace_bytes(op, d) > 256
+    assert nb.workspace_bytes(nb.OP_SCAN_BWD, d) > nb.workspace_bytes(nb.OP_SCAN_FWD, d)
+    # checkpoints: one fp32 state per 32-token chunk
+    assert nb.ckpt_bytes(d) == 8 * (2048 // 32) * 16 * 1536 * 4
+    assert nb.workspace_bytes(nb.OP_SCAN_FWD, dims(d_state=48)) == 0
+    assert lib.naju_workspace_bytes(9, ctypes.byref(d)) == 0
+
+
+def test_binding_requires_library_file(monkeypatch, tmp_path):
+    monkeypatch.setattr(nb, "_lib", None)
+    monkeypatch.setattr(nb, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        nb.lib()

@@ -1,0 +1,209 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases span several channel tiles and sequence chunks with ragged tails
+(d_inner not a multiple of 64, seqlen not a multiple of 32/256), both io
+types and both state sizes, with and without initial/conv states.  Edge
+cases: a single token, empty sequences, non-finite gates.  Tolerance:
+normwise relative error max|gpu - ref| / max|ref| <= 1e-4 (fp32 io) and
+<= 2e-2 (bf16 io, fp32 state).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import TOL, assert_close, dev, f32_dev, host, to_dev
+from selective_state_space_naju_amd import binding as nb
+from selective_state_space_naju_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm device")
+    nb.lib()
+
+
+SMALL = [
+    # Bt, L, Di, N, io
+    (2, 300, 100, 16, "f32"),
+    (2, 300, 100, 16, "bf16"),
+    (1, 77, 40, 64, "f32"),
+    (2, 530, 70, 64, "bf16"),
+    (3, 1, 64, 16, "f32"),
+    (1, 513, 129, 16, "bf16"),
+]
+
+
+def ids(c):
+    return "b%d_l%d_d%d_n%d_%s" % c
+
+
+def scan_inputs(Bt, L, Di, N, io, seed, **kw):
+    d = inputs.draw(Bt, L, Di, N, io=io, seed=seed, x0=True, backward=True, dx_final=True, **kw)
+    return d
+
+
+@pytest.mark.parametrize("case", SMALL, ids=ids)
+def test_scan_fwd_parity(case):
+    Bt, L, Di, N, io = case
+    d = scan_inputs(Bt, L, Di, N, io, seed=11)
+    print("scan_fwd", case, flush=True)
+    ys, xf = oracle.scan_fwd(d["h"], d["a"], d["b"], d["B"], d["C"], d["D"], d["x0"])
+    t = {k: to_dev(d[k], io) for k in ("h", "a", "b", "B", "C")}
+    y, xg, ck = nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], f32_dev(d["D"]),
+                            f32_dev(d["x0"]), return_ckpt=True)
+    torch.cuda.synchronize()
+    assert_close("y", host(y), ys, TOL[io])
+    assert_close("x_final", host(xg), xf, TOL[io])
+    # zero initial state
+    ys0, xf0 = oracle.scan_fwd(d["h"], d["a"], d["b"], d["B"], d["C"], d["D"], None)
+    y0, xg0 = nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], f32_dev(d["D"]))
+    assert_close("y(x0=0)", host(y0), ys0, TOL[io])
+    assert_close("xf(x0=0)", host(xg0), xf0, TOL[io])
+
+
+@pytest.mark.parametrize("case", SMALL, ids=ids)
+def test_block_fwd_parity(case):
+    Bt, L, Di, N, io = case
+    d = scan_inputs(Bt, L, Di, N, io, seed=12, block=True, conv_state=True)
+    print("block_fwd", case, flush=True)
+    yo, xfo, cso = oracle.block_fwd(d["u"], d["z"], d["conv_w"], d["a"], d["b"], d["B"], d["C"],
+                                    d["D"], d["x0"], d["conv_state"])
+    t = {k: to_dev(d[k], io) for k in ("u", "z", "a", "b", "B", "C", "conv_state")}
+    y, xf, cs = nb.block_fwd(t["u"], t["z"], f32_dev(d["conv_w"]), t["a"], t["b"], t["B"], t["C"],
+                             f32_dev(d["D"]), f32_dev(d["x0"]), t["conv_state"])
+    torch.cuda.synchronize()
+    assert_close("y", host(y), yo, TOL[io])
+    assert_close("x_final", host(xf), xfo, TOL[io])
+    assert np.array_equal(host(cs), cso)
+    # no conv_state / no x0
+    yo2, xfo2, cso2 = oracle.block_fwd(d["u"], d["z"], d["conv_w"], d["a"], d["b"], d["B"],
+                                       d["C"], d["D"])
+    y2, xf2, cs2 = nb.block_fwd(t["u"], t["z"], f32_dev(d["conv_w"]), t["a"], t["b"], t["B"],
+                                t["C"], f32_dev(d["D"]))
+    torch.cuda.synchronize()
+    assert_close("y(no state)", host(y2), yo2, TOL[io])
+    assert_close("xf(no state)", host(xf2), xfo2, TOL[io])
+    assert np.array_equal(host(cs2), cso2)
+
+
+def _grad_checks(names, got, ref, io):
+    for k in names:
+        assert_close(k, host(got[k]), ref[k], TOL[io])
+
+
+@pytest.mark.parametrize("case", SMALL, ids=ids)
+@pytest.mark.parametrize("use_ckpt", [True, False], ids=["ckpt", "recompute"])
+def test_scan_bwd_parity(case, use_ckpt):
+    Bt, L, Di, N, io = case
+    d = scan_inputs(Bt, L, Di, N, io, seed=13)
+    print("scan_bwd", case, use_ckpt, flush=True)
+    ref = oracle.scan_bwd(d["h"], d["a"], d["b"], d["B"], d["C"], d["D"], d["x0"], d["dy"],
+                          d["dx_final"])
+    t = {k: to_dev(d[k], io) for k in ("h", "a", "b", "B", "C", "dy")}
+    D, x0, dxf = f32_dev(d["D"]), f32_dev(d["x0"]), f32_dev(d["dx_final"])
+    ck = None
+    if use_ckpt:
+        _, _, ck = nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], D, x0, return_ckpt=True)
+    g = nb.scan_bwd(t["h"], t["a"], t["b"], t["B"], t["C"], D, t["dy"], x0, dxf, ck)
+    torch.cuda.synchronize()
+    _grad_checks(("dh", "da", "db", "dB", "dC", "dD", "dx0"), g, ref, io)
+
+
+@pytest.mark.parametrize("case", SMALL, ids=ids)
+@pytest.mark.parametrize("use_ckpt", [True, False], ids=["ckpt", "recompute"])
+def test_block_bwd_parity(case, use_ckpt):
+    Bt, L, Di, N, io = case
+    d = scan_inputs(Bt, L, Di, N, io, seed=14, block=True, conv_state=True)
+    print("block_bwd", case, use_ckpt, flush=True)
+    ref = oracle.block_bwd(d["u"], d["z"], d["conv_w"], d["a"], d["b"], d["B"], d["C"], d["D"],
+                           d["x0"], d["dy"], d["dx_final"], d["conv_state"])
+    ref["du"], ref["dconv_w"] = ref["du"], ref["dw"]
+    t = {k: to_dev(d[k], io) for k in ("u", "z", "a", "b", "B", "C", "dy", "conv_state")}
+    D, x0, dxf, w = (f32_dev(d["D"]), f32_dev(d["x0"]), f32_dev(d["dx_final"]),
+                     f32_dev(d["conv_w"]))
+    ck = None
+    if use_ckpt:
+        *_, ck = nb.block_fwd(t["u"], t["z"], w, t["a"], t["b"], t["B"], t["C"], D, x0,
+                              t["conv_state"], return_ckpt=True)
+    g = nb.block_bwd(t["u"], t["z"], w, t["a"], t["b"], t["B"], t["C"], D, t["dy"], x0, dxf,
+                     t["conv_state"], ck)
+    torch.cuda.synchronize()
+    _grad_checks(("du", "dz", "da", "db", "dB", "dC", "dD", "dx0", "dconv_w", "dconv_state"),
+                 g, ref, io)
+
+
+def test_empty_sequence_and_empty_batch():
+    d = inputs.draw(2, 1, 64, 16, io="f32", seed=15, x0=True, block=True, conv_state=True)
+    t = {k: to_dev(d[k], "f32") for k in ("u", "z", "a", "b", "B", "C", "conv_state")}
+    e = {k: v[:, :0].contiguous() for k, v in t.items() if k != "conv_state"}
+    x0 = f32_dev(d["x0"])
+    y, xf, cs = nb.block_fwd(e["u"], e["z"], f32_dev(d["conv_w"]), e["a"], e["b"], e["B"], e["C"],
+                             f32_dev(d["D"]), x0, t["conv_state"])
+    torch.cuda.synchronize()
+    assert y.numel() == 0
+    assert torch.equal(xf, x0) and torch.equal(cs, t["conv_state"])
+    y, xf = nb.scan_fwd(e["u"], e["a"], e["b"], e["B"], e["C"], f32_dev(d["D"]))
+    torch.cuda.synchronize()
+    assert not xf.any()
+    z3 = torch.empty((0, 5, 64), device=dev())
+    y, xf = nb.scan_fwd(z3, z3, z3, torch.empty((0, 5, 16), device=dev()),
+                        torch.empty((0, 5, 16), device=dev()), f32_dev(d["D"]))
+    assert y.shape == (0, 5, 64)
+
+
+def test_lossless_retention_and_feedthrough():
+    """a = +inf, b = -inf: x_final == x0 exactly; C = 0: y = D h (one rounding)."""
+    Bt, L, Di, N = 2, 300, 96, 16
+    d = inputs.draw(Bt, L, Di, N, io="f32", seed=16, x0=True)
+    t = {k: to_dev(d[k], "f32") for k in ("h", "B", "C")}
+    a = torch.full((Bt, L, Di), float("inf"), device=dev())
+    b = torch.full((Bt, L, Di), float("-inf"), device=dev())
+    x0 = f32_dev(d["x0"])
+    y, xf = nb.scan_fwd(t["h"], a, b, t["B"], t["C"], f32_dev(d["D"]), x0)
+    torch.cuda.synchronize()
+    assert torch.equal(xf, x0)
+    ys, _ = oracle.scan_fwd(d["h"], np.full((Bt, L, Di), np.inf), np.full((Bt, L, Di), -np.inf),
+                            d["B"], d["C"], d["D"], d["x0"])
+    assert_close("y", host(y), ys, TOL["f32"])
+    Cz = torch.zeros_like(t["C"])
+    y2, _ = nb.scan_fwd(t["h"], to_dev(d["a"], "f32"), to_dev(d["b"], "f32"), t["B"], Cz,
+                        f32_dev(d["D"]), x0)
+    torch.cuda.synchronize()
+    ref = d["D"].astype(np.float32) * d["h"]
+    assert np.array_equal(host(y2), ref.astype(np.float64))
+
+
+def test_nonfinite_gates_follow_oracle():
+    """f = 0 (a = -inf) resets the state; NaN in a gate stays in its channel."""
+    Bt, L, Di, N = 1, 100, 64, 16
+    d = inputs.draw(Bt, L, Di, N, io="f32", seed=17, x0=True)
+    d["a"][0, 40, :8] = -np.inf
+    d["a"][0, 70, 9] = np.nan
+    ys, xf = oracle.scan_fwd(d["h"], d["a"], d["b"], d["B"], d["C"], d["D"], d["x0"])
+    t = {k: to_dev(d[k], "f32") for k in ("h", "a", "b", "B", "C")}
+    y, xg = nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], f32_dev(d["D"]), f32_dev(d["x0"]))
+    torch.cuda.synchronize()
+    yg = host(y)
+    assert np.isnan(yg[0, 70:, 9]).all() and not np.isnan(np.delete(yg, 9, axis=2)).any()
+    assert not np.isnan(yg[0, :70, 9]).any()
+    m = ~np.isnan(ys)
+    assert_close("y", yg[m], ys[m], TOL["f32"])
+
+
+def test_repeat_runs_agree_and_workspace_clean():
+    Bt, L, Di, N = 2, 2048, 256, 16
+    d = inputs.draw(Bt, L, Di, N, io="bf16", seed=18)
+    t = {k: to_dev(d[k], "bf16") for k in ("h", "a", "b", "B", "C")}
+    ws = nb.Workspace(nb.workspace_bytes(nb.OP_SCAN_FWD, nb.make_dims(Bt, L, Di, N, nb.BF16)),
+                      dev())
+    outs = [nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], f32_dev(d["D"]), ws=ws)
+            for _ in range(3)]
+    torch.cuda.synchronize()
+    assert ws.error_flags() == 0
+    for y, xf in outs[1:]:
+        assert (y.float() - outs[0][0].float()).abs().max().item() <= 1e-2 * outs[0][0].float().abs().max().item()
+        assert torch.allclose(xf, outs[0][1], rtol=1e-5, atol=1e-5)

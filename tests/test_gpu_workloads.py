@@ -1,0 +1,121 @@
+"""GPU parity at the full sizes of the five workloads, in the launch
+configuration the benchmark times.
+
+Where the fp64 oracle finishes in seconds it checks every output; for the
+two largest scans it recomputes a random sample of channels one by one
+(channels are independent in the forward; B and C are shared).  The
+L=8192 workload is also run as four chained calls of 2048 tokens with the
+state carried over, which must agree with the single call.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import TOL, assert_close, f32_dev, host, to_dev
+from selective_state_space_naju_amd import binding as nb
+from selective_state_space_naju_amd import inputs
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+W = inputs.WORKLOADS
+
+
+def _dev_all(d, io, keys):
+    return {k: to_dev(d[k], io) for k in keys if k in d}
+
+
+def _sample(Di, n, seed):
+    return np.sort(np.random.default_rng(seed).choice(Di, size=n, replace=False))
+
+
+def test_scan_f32_l256_full():
+    w = W["scan_f32_b1_l256_d192_n16"]
+    d = inputs.draw_workload(w, backward=True)
+    print(w.name, flush=True)
+    t = _dev_all(d, "f32", ("h", "a", "b", "B", "C", "dy"))
+    D = f32_dev(d["D"])
+    y, xf, ck = nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], D, return_ckpt=True)
+    g = nb.scan_bwd(t["h"], t["a"], t["b"], t["B"], t["C"], D, t["dy"], ckpt=ck)
+    torch.cuda.synchronize()
+    ys, xs = oracle.scan_fwd(d["h"], d["a"], d["b"], d["B"], d["C"], d["D"])
+    assert_close("y", host(y), ys, TOL["f32"])
+    assert_close("x_final", host(xf), xs, TOL["f32"])
+    ref = oracle.scan_bwd(d["h"], d["a"], d["b"], d["B"], d["C"], d["D"], None, d["dy"])
+    for k in ("dh", "da", "db", "dB", "dC", "dD", "dx0"):
+        assert_close(k, host(g[k]), ref[k], TOL["f32"])
+
+
+def test_scan_bf16_l2048_full():
+    w = W["block_bf16_b8_l2048_d1536_n16"]
+    d = inputs.draw_workload(w, block=False)
+    print(w.name, "scan", flush=True)
+    t = _dev_all(d, "bf16", ("h", "a", "b", "B", "C"))
+    y, xf = nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], f32_dev(d["D"]))
+    torch.cuda.synchronize()
+    ys, xs = oracle.scan_fwd(d["h"], d["a"], d["b"], d["B"], d["C"], d["D"])
+    assert_close("y", host(y), ys, TOL["bf16"])
+    assert_close("x_final", host(xf), xs, TOL["bf16"])
+
+
+def test_block_bf16_l2048_fwd_bwd_full():
+    w = W["train_bf16_b8_l2048_d1536_n16"]
+    d = inputs.draw_workload(w)
+    print(w.name, flush=True)
+    t = _dev_all(d, "bf16", ("u", "z", "a", "b", "B", "C", "dy"))
+    D, cw = f32_dev(d["D"]), f32_dev(d["conv_w"])
+    y, xf, cs, ck = nb.block_fwd(t["u"], t["z"], cw, t["a"], t["b"], t["B"], t["C"], D,
+                                 return_ckpt=True)
+    g = nb.block_bwd(t["u"], t["z"], cw, t["a"], t["b"], t["B"], t["C"], D, t["dy"], ckpt=ck)
+    torch.cuda.synchronize()
+    yo, xfo, _ = oracle.block_fwd(d["u"], d["z"], d["conv_w"], d["a"], d["b"], d["B"], d["C"],
+                                  d["D"])
+    assert_close("y", host(y), yo, TOL["bf16"])
+    assert_close("x_final", host(xf), xfo, TOL["bf16"])
+    ref = oracle.block_bwd(d["u"], d["z"], d["conv_w"], d["a"], d["b"], d["B"], d["C"], d["D"],
+                           None, d["dy"])
+    ref["dconv_w"] = ref["dw"]
+    for k in ("du", "dz", "da", "db", "dB", "dC", "dD", "dx0", "dconv_w", "dconv_state"):
+        assert_close(k, host(g[k]), ref[k], TOL["bf16"])
+
+
+def test_scan_bf16_l8192_n64_sampled_and_chained():
+    w = W["scan_bf16_b4_l8192_d4096_n64"]
+    d = inputs.draw_workload(w)
+    print(w.name, flush=True)
+    t = _dev_all(d, "bf16", ("h", "a", "b", "B", "C"))
+    D = f32_dev(d["D"])
+    y, xf = nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], D)
+    # four chained calls of 2048 tokens
+    x = None
+    ys = []
+    Lc = w.L // w.chain
+    for i in range(w.chain):
+        sl = {k: v[:, i * Lc:(i + 1) * Lc].contiguous() for k, v in t.items()}
+        yi, x = nb.scan_fwd(sl["h"], sl["a"], sl["b"], sl["B"], sl["C"], D, x)
+        ys.append(yi)
+    yc = torch.cat(ys, dim=1)
+    torch.cuda.synchronize()
+    sel = _sample(w.Di, 64, 1)
+    yo, xo = oracle.scan_fwd(d["h"][:, :, sel], d["a"][:, :, sel], d["b"][:, :, sel], d["B"],
+                             d["C"], d["D"][sel])
+    assert_close("y", host(y[:, :, sel]), yo, TOL["bf16"])
+    assert_close("x_final", host(xf[:, sel]), xo, TOL["bf16"])
+    assert_close("y(chain)", host(yc[:, :, sel]), yo, TOL["bf16"])
+    assert_close("x_final(chain)", host(x[:, sel]), xo, TOL["bf16"])
+    # chain == single call over every channel
+    assert_close("chain/single y", host(yc), host(y), TOL["bf16"])
+    assert_close("chain/single x", host(x), host(xf), 1e-4)
+
+
+def test_scan_bf16_l65536_sampled():
+    w = W["scan_bf16_b1_l65536_d2048_n16"]
+    d = inputs.draw_workload(w)
+    print(w.name, flush=True)
+    t = _dev_all(d, "bf16", ("h", "a", "b", "B", "C"))
+    y, xf = nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], f32_dev(d["D"]))
+    torch.cuda.synchronize()
+    sel = _sample(w.Di, 128, 2)
+    yo, xo = oracle.scan_fwd(d["h"][:, :, sel], d["a"][:, :, sel], d["b"][:, :, sel], d["B"],
+                             d["C"], d["D"][sel])
+    assert_close("y", host(y[:, :, sel]), yo, TOL["bf16"])
+    assert_close("x_final", host(xf[:, sel]), xo, TOL["bf16"])
