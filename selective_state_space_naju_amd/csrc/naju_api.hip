@@ -95,7 +95,7 @@ static naju_status_t check_dims(const naju_dims_t *d, bool block)
     const double toks = (double)d->batch * (double)d->seqlen * (double)d->d_inner;
     if (toks > 9.0e15) return fail(NAJU_EINVAL, "tensor too large");
     if (d->seqlen > (int64_t)1 << 40) return fail(NAJU_EINVAL, "seqlen too large");
-    const FwdPlan p = fwd_plan(d->batch, d->seqlen, d->d_inner, d->d_state);
+    const FwdPlan p = fwd_plan(d->batch, d->seqlen, d->d_inner, d->d_state, kMfmaW);
     if ((double)p.n_wg >= 4.0e9) return fail(NAJU_EINVAL, "problem needs too many workgroups");
     return NAJU_OK;
 }
@@ -126,7 +126,7 @@ static size_t ws_bytes_for(naju_op_t op, const naju_dims_t *d)
 {
     const bool block = (op == NAJU_OP_BLOCK_FWD || op == NAJU_OP_BLOCK_BWD);
     if (op == NAJU_OP_SCAN_FWD || op == NAJU_OP_BLOCK_FWD)
-        return fwd_plan(d->batch, d->seqlen, d->d_inner, d->d_state).bytes;
+        return fwd_ws_bytes(d->batch, d->seqlen, d->d_inner, d->d_state);
     return bwd_plan(d->batch, d->seqlen, d->d_inner, d->d_state, block).bytes;
 }
 

@@ -470,31 +470,49 @@ __global__ void bc_reduce_kernel(const int64_t rows, const int n_tiles, const in
         dC[row * N + (s - N)] = from_f<IO>(acc);
 }
 
-// dD[c] = sum over (batch, wave) rows in order; dconv_w likewise.  One wave
-// per 64 channels; each lane owns one channel.
-__global__ void dd_reduce_kernel(const int64_t rows, const int64_t Di,
-                                 const float *__restrict__ dd_part,
-                                 const float *__restrict__ dw_part, float *__restrict__ dD,
-                                 float *__restrict__ dconv_w)
+// dD[c] = sum over (batch, wave) rows, dconv_w likewise.  A workgroup of 16
+// waves owns 64 channels; wave w sums rows w, w+16, w+32, ... and the 16 wave
+// partials are added in wave order (fixed order: deterministic).
+__global__ __launch_bounds__(1024) void dd_reduce_kernel(const int64_t rows, const int64_t Di,
+                                                         const float *__restrict__ dd_part,
+                                                         const float *__restrict__ dw_part,
+                                                         float *__restrict__ dD,
+                                                         float *__restrict__ dconv_w)
 {
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= Di) return;
-    float acc = 0.f;
-    for (int64_t r = 0; r < rows; ++r) acc += dd_part[r * Di + c];
-    dD[c] = acc;
-    if (dconv_w) {
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-        for (int64_t r = 0; r < rows; ++r) {
-            const float *p = dw_part + (r * Di + c) * 4;
-            a0 += p[0];
-            a1 += p[1];
-            a2 += p[2];
-            a3 += p[3];
+    __shared__ float red[16][5][64];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, s4 = 0.f;
+    if (c < Di) {
+#pragma unroll 4
+        for (int64_t r = wv; r < rows; r += 16) {
+            s0 += dd_part[r * Di + c];
+            if (dconv_w) {
+                const float4 q = *(const float4 *)(dw_part + (r * Di + c) * 4);
+                s1 += q.x;
+                s2 += q.y;
+                s3 += q.z;
+                s4 += q.w;
+            }
         }
-        dconv_w[c * 4 + 0] = a0;
-        dconv_w[c * 4 + 1] = a1;
-        dconv_w[c * 4 + 2] = a2;
-        dconv_w[c * 4 + 3] = a3;
+    }
+    red[wv][0][lane] = s0;
+    red[wv][1][lane] = s1;
+    red[wv][2][lane] = s2;
+    red[wv][3][lane] = s3;
+    red[wv][4][lane] = s4;
+    __syncthreads();
+    if (wv == 0 && c < Di) {
+        float t[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < 16; ++w)
+            for (int k = 0; k < 5; ++k) t[k] += red[w][k][lane];
+        dD[c] = t[0];
+        if (dconv_w) {
+            dconv_w[c * 4 + 0] = t[1];
+            dconv_w[c * 4 + 1] = t[2];
+            dconv_w[c * 4 + 2] = t[3];
+            dconv_w[c * 4 + 3] = t[4];
+        }
     }
 }
 
@@ -571,7 +589,7 @@ static hipError_t launch_bwd_t(const BwdArgs &g, hipStream_t stream)
                            (IO *)g.dC);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(dd_reduce_kernel, dim3((unsigned)((g.Di + 63) / 64)), dim3(64), 0, stream,
+    hipLaunchKernelGGL(dd_reduce_kernel, dim3((unsigned)((g.Di + 63) / 64)), dim3(1024), 0, stream,
                        g.Bt * pl.n_waves, g.Di, (const float *)dd, (const float *)dw, g.dD,
                        BLOCK ? g.dconv_w : (float *)nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -23,6 +23,8 @@
 //   4. every wave adds the contribution of its entering state,
 //        y_j = ys_loc[j] + P_j (x_in . C_j) / sqrt(N),
 //      applies SiLU(z) for the block, and stores y.
+#include <stdlib.h>
+
 #include "naju_device.h"
 #include "naju_launch.h"
 
@@ -306,8 +308,22 @@ static hipError_t launch_fwd_t(const FwdArgs &g, hipStream_t stream)
     return hipGetLastError();
 }
 
+// The matrix-core variant serves bf16 activations with d_state 16 when B and
+// C allow 16-byte loads; NAJU_FWD_VARIANT=rr forces the register recurrence.
+static bool use_mfma(const FwdArgs &g)
+{
+    static const bool forced_rr = [] {
+        const char *v = getenv("NAJU_FWD_VARIANT");
+        return v && v[0] == 'r' && v[1] == 'r';
+    }();
+    const auto al16 = [](const void *p) { return ((uintptr_t)p % 16) == 0; };
+    return !forced_rr && g.io == 1 && g.N == 16 && g.Di % 8 == 0 && al16(g.B) && al16(g.C) &&
+           al16(g.hu) && al16(g.a) && al16(g.b);
+}
+
 hipError_t launch_fwd(const FwdArgs &g, hipStream_t stream)
 {
+    if (use_mfma(g)) return launch_fwd_mfma(g, stream);
     if (g.io == 0) {
         if (g.N == 16) return g.block ? launch_fwd_t<float, 16, true>(g, stream)
                                       : launch_fwd_t<float, 16, false>(g, stream);

@@ -1,0 +1,659 @@
+// naju_fwd_mfma.hip -- matrix-core forward of the Naju selective scan for bf16
+// activations and d_state 16 (scan and block).
+//
+// Same recurrence/readout ("Core equations" of the Naju reproduction README,
+// arXiv 2607.21000), same workgroup decomposition and decoupled look-back as
+// naju_fwd.hip; only the work inside a wave's 32-token chunk changes.  With
+// the chunk-local running product P_n = prod_{j<=n} f_j (per channel) and the
+// rescaled writes W'_k = w_k / P_k,
+//     x_n = P_n (x_in + sum_{k<=n} W'_k B_k)
+//     y_n = P_n ( sum_{k<=n} G[n,k] W'_k  +  C_n x_in / sqrt(N) ) + D h_n,
+//     G  = tril(C B^T) / sqrt(N)   (32 x 32, shared by every channel)
+// so the three contractions of a chunk -- G @ W', C @ x_in^T and the chunk's
+// state increment W'^T B -- run on MFMA (v_mfma_f32_32x32x16_bf16), while the
+// VALU only forms the gates, P and W' and applies the epilogue.  Operands are
+// split into bf16 hi + lo parts (x = hi + lo to ~2^-17 relative), so the
+// products keep close to fp32 accuracy with fp32 accumulation.
+//
+// Lane layout: lane l owns column l%32 of each 32-wide MFMA tile and, in its
+// half h = l/32, the 16 chunk tokens {8q + 4h + r}.  That set is both the
+// lane's row set in the 32x32 accumulator and (by choosing the K-slot order)
+// its K-slots in the A/B operands, so gates, W', P and the outputs of a token
+// all live in the lane that needs them.
+//
+// Safety: the factorisation needs 1/P over the chunk to stay in range.  A wave
+// whose chunk has prod(1/f) > 2^64 or a non-finite input falls back to the
+// plain register recurrence for that chunk (exact for any input).
+#include "naju_device.h"
+#include "naju_launch.h"
+
+namespace naju {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split(float v, __bf16 &hi, __bf16 &lo)
+{
+    hi = (__bf16)v;
+    lo = (__bf16)(v - (float)hi);
+}
+
+__device__ __forceinline__ __bf16 as_bf(bf16 v) { return __builtin_bit_cast(__bf16, v); }
+
+// ------------------------------------------------------------------ fallback
+// Register recurrence of one wave's chunk in lane = channel layout (64
+// channels), used when the rescaled form is unsafe.  Aggregate from a zero
+// state: x -> P x + S.
+template <bool BLOCK>
+__device__ __forceinline__ void rr_aggregate(int64_t L, int64_t Di, int bi, int64_t c, bool valid,
+                                             int64_t n0, const bf16 *hu, const bf16 *a,
+                                             const bf16 *bg, const bf16 *Bm, const float *conv_w,
+                                             const bf16 *conv_state, float &P, float (&S)[16])
+{
+    float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f, um1 = 0.f, um2 = 0.f, um3 = 0.f;
+    if (BLOCK && valid) {
+        w0 = conv_w[c * 4 + 0];
+        w1 = conv_w[c * 4 + 1];
+        w2 = conv_w[c * 4 + 2];
+        w3 = conv_w[c * 4 + 3];
+        float hv[3];
+        for (int k = 1; k <= 3; ++k) {
+            const int64_t m = n0 - k;
+            float v = 0.f;
+            if (m >= 0 && m < L)
+                v = to_f(hu[((int64_t)bi * L + m) * Di + c]);
+            else if (m < 0 && conv_state)
+                v = to_f(conv_state[((int64_t)bi * 3 + (m + 3)) * Di + c]);
+            hv[k - 1] = v;
+        }
+        um1 = hv[0];
+        um2 = hv[1];
+        um3 = hv[2];
+    }
+    P = 1.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) S[s] = 0.f;
+    for (int j = 0; j < 32; ++j) {
+        const int64_t n = n0 + j;
+        if (n >= L) break;
+        const int64_t t = ((int64_t)bi * L + n) * Di + c;
+        float av = 0.f, bv = 0.f, hv = 0.f;
+        if (valid) {
+            av = to_f(a[t]);
+            bv = to_f(bg[t]);
+            if (BLOCK) {
+                const float uv = to_f(hu[t]);
+                const float pre = w0 * um3 + w1 * um2 + w2 * um1 + w3 * uv;
+                um3 = um2;
+                um2 = um1;
+                um1 = uv;
+                hv = pre * sigm(pre);
+            } else {
+                hv = to_f(hu[t]);
+            }
+        }
+        const float f = valid ? sigm(av) : 1.f;
+        const float wr = valid ? sigm(bv) * hv : 0.f;
+        const bf16 *Bn = Bm + ((int64_t)bi * L + n) * 16;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) S[s] = fmaf(f, S[s], wr * to_f(Bn[s]));
+        P *= f;
+    }
+}
+
+// Full recurrence with readout from the entering state; writes y.
+template <bool BLOCK>
+__device__ __forceinline__ void rr_output(int64_t L, int64_t Di, int bi, int64_t c, bool valid,
+                                          int64_t n0, float scale, const bf16 *hu, const bf16 *a,
+                                          const bf16 *bg, const bf16 *Bm, const bf16 *Cm,
+                                          const float *D, const bf16 *z, const float *conv_w,
+                                          const bf16 *conv_state, const float (&xin)[16], bf16 *y)
+{
+    float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f, um1 = 0.f, um2 = 0.f, um3 = 0.f;
+    if (BLOCK && valid) {
+        w0 = conv_w[c * 4 + 0];
+        w1 = conv_w[c * 4 + 1];
+        w2 = conv_w[c * 4 + 2];
+        w3 = conv_w[c * 4 + 3];
+        float hv[3];
+        for (int k = 1; k <= 3; ++k) {
+            const int64_t m = n0 - k;
+            float v = 0.f;
+            if (m >= 0 && m < L)
+                v = to_f(hu[((int64_t)bi * L + m) * Di + c]);
+            else if (m < 0 && conv_state)
+                v = to_f(conv_state[((int64_t)bi * 3 + (m + 3)) * Di + c]);
+            hv[k - 1] = v;
+        }
+        um1 = hv[0];
+        um2 = hv[1];
+        um3 = hv[2];
+    }
+    const float Dc = valid ? D[c] : 0.f;
+    float x[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) x[s] = xin[s];
+    for (int j = 0; j < 32; ++j) {
+        const int64_t n = n0 + j;
+        if (n >= L) break;
+        const int64_t t = ((int64_t)bi * L + n) * Di + c;
+        float av = 0.f, bv = 0.f, hv = 0.f;
+        if (valid) {
+            av = to_f(a[t]);
+            bv = to_f(bg[t]);
+            if (BLOCK) {
+                const float uv = to_f(hu[t]);
+                const float pre = w0 * um3 + w1 * um2 + w2 * um1 + w3 * uv;
+                um3 = um2;
+                um2 = um1;
+                um1 = uv;
+                hv = pre * sigm(pre);
+            } else {
+                hv = to_f(hu[t]);
+            }
+        }
+        const float f = valid ? sigm(av) : 1.f;
+        const float wr = valid ? sigm(bv) * hv : 0.f;
+        const bf16 *Bn = Bm + ((int64_t)bi * L + n) * 16;
+        const bf16 *Cn = Cm + ((int64_t)bi * L + n) * 16;
+        float acc = 0.f;
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            x[s] = fmaf(f, x[s], wr * to_f(Bn[s]));
+            acc = fmaf(x[s], to_f(Cn[s]), acc);
+        }
+        float yv = fmaf(scale, acc, Dc * hv);
+        if (valid) {
+            if (BLOCK) {
+                const float zv = to_f(z[t]);
+                yv *= zv * sigm(zv);
+            }
+            y[t] = from_f<bf16>(yv);
+        }
+    }
+}
+
+// ------------------------------------------------------------------- kernel
+// Persistent: one workgroup per CU takes tickets (workgroup chunks of 64
+// channels x 256 tokens, chunk-major so look-back predecessors always hold
+// smaller tickets) until none are left.  The h/a/b tile of the next ticket is
+// copied HBM -> LDS with global_load_lds_dwordx4 (no VGPRs involved) while the
+// current one runs its matrix products, look-back and epilogue.
+constexpr int kRows = kFwdT * kMfmaW;  // tokens per workgroup chunk
+
+template <bool BLOCK>
+__global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
+    const int64_t Bt, const int64_t L, const int64_t Di, const int n_tiles, const int n_chunks,
+    const float scale, const bf16 *__restrict__ hu, const bf16 *__restrict__ a,
+    const bf16 *__restrict__ bg, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
+    const float *__restrict__ D, const float *__restrict__ x0, const bf16 *__restrict__ z,
+    const float *__restrict__ conv_w, const bf16 *__restrict__ conv_state, bf16 *__restrict__ y,
+    float *__restrict__ x_final, bf16 *__restrict__ conv_state_out, float *__restrict__ ckpt,
+    WsHeader *hdr, uint32_t *flags, float *agg, float *incl)
+{
+    constexpr int N = 16, T = kFwdT, W = kMfmaW;
+    static_assert(T == 32, "one 32x32 MFMA tile of tokens per wave");
+    const int wv = threadIdx.x >> 6;
+
+    __shared__ __attribute__((aligned(1024))) bf16 sIn[3][kRows][64];  // h|u, a, b
+    __shared__ __attribute__((aligned(1024))) bf16 sBC[2][kRows][16];  // B, C rows
+    __shared__ uint32_t s_next, s_epoch;
+    __shared__ float sP[W][64];
+    __shared__ float sS[W][16][64];
+    __shared__ float sX[16][64];
+
+    const uint32_t per_chunk = (uint32_t)(Bt * n_tiles);
+    const uint32_t total = per_chunk * (uint32_t)n_chunks;
+    const int64_t n_waves = (L + T - 1) / T;
+    const bf16 *srcs[3] = {hu, a, bg};
+
+    // copy the h|u, a, b tile and the B, C rows of ticket tk into LDS (this
+    // wave's 32 rows)
+    auto prefetch = [&](uint32_t tk, int lane) {
+        const int ch = (int)(tk / per_chunk);
+        const int rm = (int)(tk % per_chunk);
+        const int b_ = rm / n_tiles;
+        const int64_t cb = (int64_t)(rm % n_tiles) * 64 + 8 * (lane & 7);
+        const int64_t cg = cb < Di ? cb : 0;  // whole 8-channel groups: Di % 8 == 0
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            int64_t n = (int64_t)ch * kRows + 32 * wv + 8 * k + (lane >> 3);
+            if (n >= L) n = L - 1;  // rows past the end are never used
+            const int64_t off = ((int64_t)b_ * L + n) * Di + cg;
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(srcs[t] + off),
+                    (__attribute__((address_space(3))) void *)&sIn[t][32 * wv + 8 * k][0], 16, 0,
+                    0);
+        }
+        int64_t n = (int64_t)ch * kRows + 32 * wv + (lane >> 1);
+        if (n >= L) n = L - 1;
+        const int64_t boff = ((int64_t)b_ * L + n) * N + 8 * (lane & 1);
+        __builtin_amdgcn_global_load_lds((const void *)(Bm + boff),
+                                         (__attribute__((address_space(3))) void *)&sBC[0][32 * wv][0],
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(Cm + boff),
+                                         (__attribute__((address_space(3))) void *)&sBC[1][32 * wv][0],
+                                         16, 0, 0);
+    };
+
+    if (threadIdx.x == 0) {
+        s_next = add_agent(&hdr->ticket, 1u);
+        s_epoch = (ld_agent(&hdr->epoch) + 1u) & 0x3FFFFFFFu;
+    }
+    __syncthreads();
+    uint32_t cur = s_next;
+    const uint32_t ep = s_epoch;
+    if (cur >= total) return;
+    prefetch(cur, threadIdx.x & 63);
+
+    for (;;) {
+        wait_mem();
+        __syncthreads();  // the tile of `cur` is in LDS; s_next consumed
+        if (threadIdx.x == 0) s_next = add_agent(&hdr->ticket, 1u);
+        // lane-dependent values are re-derived every ticket (kept out of
+        // loop-invariant code motion, which would otherwise pin dozens of
+        // per-lane addresses in registers across the whole loop)
+        int lane = threadIdx.x & 63;
+        asm volatile("" : "+v"(lane));
+        const int col = lane & 31;
+        const int hh = lane >> 5;
+
+        const int chunk = (int)(cur / per_chunk);
+        const int rem = (int)(cur % per_chunk);
+        const int bi = rem / n_tiles;
+        const int tile = rem % n_tiles;
+        const int64_t cbase = (int64_t)tile * 64;
+        const int64_t n0 = (int64_t)chunk * kRows + (int64_t)wv * T;
+        const int64_t tokbase = (int64_t)bi * L;
+        auto tok = [&](int i) -> int { return 8 * (i >> 2) + 4 * hh + (i & 3); };
+
+        // ------------------------------------------------ token-shared operands
+        bf16x8 Bop, Cop, Csc;
+        {
+            if (n0 + col < L) {
+                const uint4 qb = *(const uint4 *)&sBC[0][32 * wv + col][8 * hh];
+                const uint4 qc = *(const uint4 *)&sBC[1][32 * wv + col][8 * hh];
+                Bop = __builtin_bit_cast(bf16x8, qb);
+                Cop = __builtin_bit_cast(bf16x8, qc);
+            } else {
+#pragma unroll
+                for (int s = 0; s < 8; ++s) Bop[s] = Cop[s] = (__bf16)0.f;
+            }
+#pragma unroll
+            for (int s = 0; s < 8; ++s) Csc[s] = (__bf16)((float)Cop[s] * scale);
+        }
+        bf16x8 Bsv[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            bf16 v = 0;
+            if (col < N && n0 + tok(i) < L) v = sBC[0][32 * wv + tok(i)][col];
+            Bsv[i >> 3][i & 7] = as_bf(v);
+        }
+
+        // ------------------------------------------------------ gates, W', P
+        float Pv[2][16], FT[2][16];
+        bf16x8 Whi[2][2], Wlo[2][2];
+        float Ptot[2];
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t c = cbase + col + 32 * j;
+            const bool valid = c < Di;
+            const float Dc = valid ? D[c] : 0.f;
+            float cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f;
+            if (BLOCK && valid) {
+                cw0 = conv_w[c * 4 + 0];
+                cw1 = conv_w[c * 4 + 1];
+                cw2 = conv_w[c * 4 + 2];
+                cw3 = conv_w[c * 4 + 3];
+            }
+            float invf[16], wr[16], hv[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int rg = 32 * wv + 8 * q + 4 * hh;  // tile row of the group's first token
+                const int64_t g0 = n0 + 8 * q + 4 * hh;
+                float uw[7];
+                if (BLOCK) {
+#pragma unroll
+                    for (int k = 0; k < 7; ++k) {
+                        const int r = rg - 3 + k;
+                        const int64_t m = g0 - 3 + k;
+                        float v = 0.f;
+                        if (r >= 0) {
+                            v = to_f(sIn[0][r][32 * j + col]);
+                        } else if (valid) {
+                            if (m >= 0)
+                                v = to_f(hu[(tokbase + m) * Di + c]);
+                            else if (m >= -3 && conv_state)
+                                v = to_f(conv_state[((int64_t)bi * 3 + (m + 3)) * Di + c]);
+                        }
+                        uw[k] = (m < L) ? v : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * q + r;
+                    const int64_t n = g0 + r;
+                    float e = 0.f, ib = 0.f, h = 0.f;
+                    if (valid && n < L) {
+                        e = ex2(-to_f(sIn[1][rg + r][32 * j + col]) * kLog2e);
+                        ib = sigm(to_f(sIn[2][rg + r][32 * j + col]));
+                        if (BLOCK) {
+                            const float pre = cw0 * uw[r] + cw1 * uw[r + 1] + cw2 * uw[r + 2] +
+                                              cw3 * uw[r + 3];
+                            h = pre * sigm(pre);
+                        } else {
+                            h = to_f(sIn[0][rg + r][32 * j + col]);
+                        }
+                    }
+                    invf[i] = 1.f + e;
+                    wr[i] = ib * h;
+                    hv[i] = h;
+                    FT[j][i] = Dc * h;
+                }
+            }
+            float tot[4], cum[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float run = 1.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    run *= invf[4 * q + r];
+                    cum[4 * q + r] = run;
+                }
+                tot[q] = run;
+            }
+            float ptot[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ptot[q] = __shfl_xor(tot[q], 32);
+            float E[4], acc = 1.f;
+#pragma unroll
+            for (int g = 0; g < 8; ++g) {
+                const bool mine = (g & 1) == hh;
+                const float Tg = mine ? tot[g >> 1] : ptot[g >> 1];
+                if (mine) E[g >> 1] = acc;
+                acc *= Tg;
+            }
+            ok = ok && (acc <= 18446744073709551616.f);  // 2^64; false for NaN
+            Ptot[j] = rcp(acc);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float invP = E[i >> 2] * cum[i];
+                const float wp = wr[i] * invP;
+                ok = ok && (__builtin_fabsf(wp) < 1e30f) && (__builtin_fabsf(hv[i]) < 1e30f);
+                Pv[j][i] = rcp(invP);
+                FT[j][i] *= invP;  // y = P (G W' + C x_in + D h / P)
+                __bf16 hi, lo;
+                split(wp, hi, lo);
+                Whi[j][i >> 3][i & 7] = hi;
+                Wlo[j][i >> 3][i & 7] = lo;
+            }
+        }
+        const bool wave_ok = __all(ok);
+        __syncthreads();  // every wave is done with sIn; s_next is visible
+        const uint32_t nxt = s_next;
+        if (nxt < total) prefetch(nxt, lane);
+
+        // ------------------------------------- chunk aggregates (P_T, S) -> LDS
+        f32x16 Y[2];
+        if (wave_ok) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                f32x16 sacc = {};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    sacc = mfma(Whi[j][kb], Bsv[kb], sacc);
+                    sacc = mfma(Wlo[j][kb], Bsv[kb], sacc);
+                }
+                if (col < N) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) sS[wv][col][32 * j + tok(i)] = sacc[i];
+                }
+                if (hh == 0) sP[wv][32 * j + col] = Ptot[j];
+            }
+        } else {
+            float P, S[16];
+            rr_aggregate<BLOCK>(L, Di, bi, cbase + lane, cbase + lane < Di, n0, hu, a, bg, Bm,
+                                conv_w, conv_state, P, S);
+            sP[wv][lane] = P;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) sS[wv][s][lane] = S[s];
+        }
+        __syncthreads();
+        if (wave_ok) {
+            const float pt = sP[wv][lane];
+#pragma unroll
+            for (int s = 0; s < 16; ++s) sS[wv][s][lane] *= pt;
+        }
+        __syncthreads();
+
+        // ----------------------------------------- intra-chunk term G @ W'
+        if (wave_ok) {
+            f32x16 g = {};
+            g = mfma(Bop, Cop, g);  // g[i] = C_{col} . B_{tok(i)} = G[col][tok(i)]
+            bf16x8 Ghi[2], Glo[2];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float v = (tok(i) <= col) ? g[i] * scale : 0.f;
+                __bf16 hi, lo;
+                split(v, hi, lo);
+                Ghi[i >> 3][i & 7] = hi;
+                Glo[i >> 3][i & 7] = lo;
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                f32x16 acc;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[i] = FT[j][i];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    acc = mfma(Ghi[kb], Whi[j][kb], acc);
+                    acc = mfma(Ghi[kb], Wlo[j][kb], acc);
+                    acc = mfma(Glo[kb], Whi[j][kb], acc);
+                }
+                Y[j] = acc;
+            }
+        }
+
+        const int64_t c_lane = cbase + lane;
+        const bool valid_lane = c_lane < Di;
+
+        // -------------------------------- look-back for the entering state
+        if (wv == 0) {
+            float Pt = 1.f, St[16];
+#pragma unroll
+            for (int s = 0; s < 16; ++s) St[s] = 0.f;
+            for (int w = 0; w < W; ++w) {
+                const float pw = sP[w][lane];
+#pragma unroll
+                for (int s = 0; s < 16; ++s) St[s] = fmaf(pw, St[s], sS[w][s][lane]);
+                Pt *= pw;
+            }
+            const size_t me = ((size_t)bi * n_tiles + tile) * n_chunks + chunk;
+            float xin[16];
+            if (chunk == 0) {
+#pragma unroll
+                for (int s = 0; s < 16; ++s)
+                    xin[s] = (x0 && valid_lane) ? x0[(bi * Di + c_lane) * N + s] : 0.f;
+            } else {
+                float *ag = agg + me * (17 * 64);
+                st_agent(ag + lane, Pt);
+#pragma unroll
+                for (int s = 0; s < 16; ++s) st_agent(ag + (1 + s) * 64 + lane, St[s]);
+                wait_mem();
+                if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagAgg));
+                float accP = 1.f, accS[16];
+#pragma unroll
+                for (int s = 0; s < 16; ++s) accS[s] = 0.f;
+                size_t jx = me - 1;
+                for (;;) {
+                    const uint32_t st = wait_flag(&flags[jx], ep, hdr);
+                    if (st == kFlagIncl) {
+                        const float *in = incl + jx * (16 * 64);
+#pragma unroll
+                        for (int s = 0; s < 16; ++s)
+                            xin[s] = fmaf(accP, ld_agent(in + s * 64 + lane), accS[s]);
+                        break;
+                    }
+                    const float *pa = agg + jx * (17 * 64);
+                    const float pj = ld_agent(pa + lane);
+#pragma unroll
+                    for (int s = 0; s < 16; ++s)
+                        accS[s] = fmaf(accP, ld_agent(pa + (1 + s) * 64 + lane), accS[s]);
+                    accP *= pj;
+                    --jx;
+                }
+            }
+            float *ic = incl + me * (16 * 64);
+            float xo[16];
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                xo[s] = fmaf(Pt, xin[s], St[s]);
+                st_agent(ic + s * 64 + lane, xo[s]);
+            }
+            wait_mem();
+            if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagIncl));
+#pragma unroll
+            for (int s = 0; s < 16; ++s) sX[s][lane] = xin[s];
+            if (valid_lane) {
+                if (chunk == n_chunks - 1 && x_final) {
+#pragma unroll
+                    for (int s = 0; s < 16; ++s) x_final[(bi * Di + c_lane) * N + s] = xo[s];
+                }
+                if (BLOCK && chunk == n_chunks - 1 && conv_state_out) {
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) {
+                        const int64_t m = L - 3 + k;
+                        bf16 v = 0;
+                        if (m >= 0)
+                            v = hu[(tokbase + m) * Di + c_lane];
+                        else if (conv_state)
+                            v = conv_state[((int64_t)bi * 3 + (m + 3)) * Di + c_lane];
+                        conv_state_out[((int64_t)bi * 3 + k) * Di + c_lane] = v;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // --------------------- this wave's entering state (lane = channel):
+        // the workgroup's entering state carried through the waves before it
+        float xin[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) xin[s] = sX[s][lane];
+        for (int w = 0; w < wv; ++w) {
+            const float pw = sP[w][lane];
+#pragma unroll
+            for (int s = 0; s < 16; ++s) xin[s] = fmaf(pw, xin[s], sS[w][s][lane]);
+        }
+        __syncthreads();  // every wave has read sS before it is reused below
+        if (ckpt && valid_lane && n0 < L) {
+            const int64_t wrow = (int64_t)chunk * W + wv;
+#pragma unroll
+            for (int s = 0; s < 16; ++s)
+                ckpt[(((int64_t)bi * n_waves + wrow) * N + s) * Di + c_lane] = xin[s];
+        }
+
+        if (!wave_ok) {
+            if (y)
+                rr_output<BLOCK>(L, Di, bi, c_lane, valid_lane, n0, scale, hu, a, bg, Bm, Cm, D,
+                                 z, conv_w, conv_state, xin, y);
+        } else if (y) {
+#pragma unroll
+            for (int s = 0; s < 16; ++s) sS[wv][s][lane] = xin[s];
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                bf16x8 xh, xl;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    __bf16 hi, lo;
+                    split(sS[wv][8 * hh + k][32 * j + col], hi, lo);
+                    xh[k] = hi;
+                    xl[k] = lo;
+                }
+                Y[j] = mfma(Csc, xh, Y[j]);
+                Y[j] = mfma(Csc, xl, Y[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int64_t c = cbase + col + 32 * j;
+                if (c < Di) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int64_t n = n0 + tok(i);
+                        if (n < L) {
+                            const int64_t t = (tokbase + n) * Di + c;
+                            float yv = Pv[j][i] * Y[j][i];
+                            if (BLOCK) {
+                                const float zv = to_f(z[t]);
+                                yv *= zv * sigm(zv);
+                            }
+                            y[t] = from_f<bf16>(yv);
+                        }
+                    }
+                }
+            }
+        }
+
+        __syncthreads();  // sP/sS/sX are reused by the next ticket
+        if (threadIdx.x == 0) {
+            const uint32_t old = add_agent(&hdr->done, 1u);
+            if (old == total - 1) {
+                st_agent(&hdr->ticket, 0u);
+                st_agent(&hdr->done, 0u);
+                st_agent(&hdr->epoch, ep);
+            }
+        }
+        cur = nxt;
+        if (cur >= total) break;
+    }
+}
+
+static int cu_count()
+{
+    static int n = [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        return v;
+    }();
+    return n;
+}
+
+hipError_t launch_fwd_mfma(const FwdArgs &g, hipStream_t stream)
+{
+    const FwdPlan pl = fwd_plan(g.Bt, g.L, g.Di, g.N, kMfmaW);
+    WsHeader *hdr = (WsHeader *)g.ws;
+    uint32_t *flags = (uint32_t *)((char *)g.ws + pl.off_flags);
+    float *agg = (float *)((char *)g.ws + pl.off_agg);
+    float *incl = (float *)((char *)g.ws + pl.off_incl);
+    const int64_t slots = 2 * (int64_t)cu_count();  // two workgroups per CU
+    const int64_t grid = pl.n_wg < slots ? pl.n_wg : slots;
+    if (g.block)
+        hipLaunchKernelGGL(fwd_mfma_kernel<true>, dim3(grid), dim3(64 * kMfmaW), 0, stream, g.Bt,
+                           g.L, g.Di, pl.n_tiles, pl.n_chunks, g.scale, (const bf16 *)g.hu,
+                           (const bf16 *)g.a, (const bf16 *)g.b, (const bf16 *)g.B,
+                           (const bf16 *)g.C, g.D, g.x0, (const bf16 *)g.z, g.conv_w,
+                           (const bf16 *)g.conv_state, (bf16 *)g.y, g.x_final,
+                           (bf16 *)g.conv_state_out, g.ckpt, hdr, flags, agg, incl);
+    else
+        hipLaunchKernelGGL(fwd_mfma_kernel<false>, dim3(grid), dim3(64 * kMfmaW), 0, stream,
+                           g.Bt, g.L, g.Di, pl.n_tiles, pl.n_chunks, g.scale, (const bf16 *)g.hu,
+                           (const bf16 *)g.a, (const bf16 *)g.b, (const bf16 *)g.B,
+                           (const bf16 *)g.C, g.D, g.x0, (const bf16 *)g.z, g.conv_w,
+                           (const bf16 *)g.conv_state, (bf16 *)g.y, g.x_final,
+                           (bf16 *)g.conv_state_out, g.ckpt, hdr, flags, agg, incl);
+    return hipGetLastError();
+}
+
+}  // namespace naju

@@ -12,6 +12,9 @@ namespace naju {
 // workgroup kFwdW consecutive waves along the sequence.
 constexpr int kFwdT = 32;
 constexpr int kFwdW = 8;
+// The matrix-core forward uses 4-wave workgroups (two fit on a CU, so one can
+// compute while the other waits in its look-back).
+constexpr int kMfmaW = 4;
 // Backward: same wave shape (checkpoints are taken per forward wave).
 constexpr int kBwdT = 32;
 constexpr int kBwdW = 8;
@@ -27,12 +30,12 @@ struct FwdPlan {
     size_t off_flags, off_agg, off_incl, bytes;
 };
 
-inline FwdPlan fwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N)
+inline FwdPlan fwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N, int W = kFwdW)
 {
     FwdPlan p{};
     const int64_t cpw = 64 / (N / 16);
     p.n_tiles = (int)((Di + cpw - 1) / cpw);
-    p.n_chunks = (int)((L + kFwdT * kFwdW - 1) / (kFwdT * kFwdW));
+    p.n_chunks = (int)((L + kFwdT * W - 1) / (kFwdT * W));
     p.n_wg = Bt * p.n_tiles * p.n_chunks;
     p.n_waves = (L + kFwdT - 1) / kFwdT;
     p.off_flags = 256;
@@ -40,6 +43,14 @@ inline FwdPlan fwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N)
     p.off_incl = align256(p.off_agg + 17 * 64 * 4 * (size_t)p.n_wg);
     p.bytes = align256(p.off_incl + 16 * 64 * 4 * (size_t)p.n_wg);
     return p;
+}
+
+// workspace bytes of a forward call, whichever kernel variant serves it
+inline size_t fwd_ws_bytes(int64_t Bt, int64_t L, int64_t Di, int64_t N)
+{
+    const size_t a = fwd_plan(Bt, L, Di, N, kFwdW).bytes;
+    const size_t b = N == 16 ? fwd_plan(Bt, L, Di, N, kMfmaW).bytes : 0;
+    return a > b ? a : b;
 }
 
 // checkpoint: the state entering every kFwdT-token chunk, [Bt][n_waves][N][Di] fp32
@@ -80,7 +91,7 @@ inline BwdPlan bwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N, bool block
     p.off_edge = align256(p.off_dw + (block ? (size_t)Bt * p.n_waves * Di * 4 * 4 : 0));
     p.off_ckpt = align256(p.off_edge + (block ? (size_t)Bt * p.n_waves * 6 * Di * 4 : 0));
     p.off_fwd = align256(p.off_ckpt + ckpt_bytes(Bt, L, Di, N));
-    p.bytes = align256(p.off_fwd + f.bytes);
+    p.bytes = align256(p.off_fwd + fwd_ws_bytes(Bt, L, Di, N));
     return p;
 }
 
@@ -121,6 +132,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs &g, hipStream_t stream);
+hipError_t launch_fwd_mfma(const FwdArgs &g, hipStream_t stream);  // bf16, d_state 16
 hipError_t launch_bwd(const BwdArgs &g, hipStream_t stream);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_empty_seq(int io, int64_t Bt, int64_t Di, int64_t N, const float *x0,

@@ -207,3 +207,35 @@ def test_repeat_runs_agree_and_workspace_clean():
     for y, xf in outs[1:]:
         assert (y.float() - outs[0][0].float()).abs().max().item() <= 1e-2 * outs[0][0].float().abs().max().item()
         assert torch.allclose(xf, outs[0][1], rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("block", [False, True], ids=["scan", "block"])
+def test_bf16_fallback_chunks(block):
+    """bf16 / d_state 16 runs on the matrix-core path; chunks whose prod(1/f) leaves
+    the safe range (a = -inf, or a drawn wide so f is often tiny) or that hold a NaN
+    gate are recomputed by the register recurrence.  Both kinds mix in one call."""
+    Bt, L, Di, N = 2, 700, 160, 16
+    d = inputs.draw(Bt, L, Di, N, io="bf16", seed=19, x0=True, block=block, conv_state=block)
+    d["a"][0, 100, :10] = -np.inf                      # f = 0: full reset
+    d["a"][1, 300:364, 64:] = inputs.bf16_round(       # wide gates: prod(1/f) overflows
+        (np.random.default_rng(3).standard_normal((64, Di - 64)) * 6 - 6).astype(np.float32))
+    d["a"][1, 500, 5] = np.nan
+    print("fallback", block, flush=True)
+    hk = "u" if block else "h"
+    t = {k: to_dev(d[k], "bf16") for k in (hk, "a", "b", "B", "C") + (("z", "conv_state") if block else ())}
+    D, x0 = f32_dev(d["D"]), f32_dev(d["x0"])
+    if block:
+        ys, xf, _ = oracle.block_fwd(d["u"], d["z"], d["conv_w"], d["a"], d["b"], d["B"], d["C"],
+                                     d["D"], d["x0"], d["conv_state"])
+        y, xg, _ = nb.block_fwd(t["u"], t["z"], f32_dev(d["conv_w"]), t["a"], t["b"], t["B"], t["C"],
+                                D, x0, t["conv_state"])
+    else:
+        ys, xf = oracle.scan_fwd(d["h"], d["a"], d["b"], d["B"], d["C"], d["D"], d["x0"])
+        y, xg = nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], D, x0)
+    torch.cuda.synchronize()
+    yg, xgh = host(y), host(xg)
+    assert np.array_equal(np.isnan(yg), np.isnan(ys))
+    m = ~np.isnan(ys)
+    assert_close("y", yg[m], ys[m], TOL["bf16"])
+    mx = ~np.isnan(xf)
+    assert_close("x_final", xgh[mx], xf[mx], TOL["bf16"])
