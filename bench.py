@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -46,14 +47,36 @@ def alg_bytes(kind, Bt, L, Di, N, e, K=4):
     raise ValueError(kind)
 
 
+def measured_traffic(md_name, sources):
+    """Per-launch HBM bytes from a committed rocprofv3 counter summary, or None when
+    there is none or the kernel sources changed since the counters were taken."""
+    if not md_name:
+        return None
+    path = os.path.join(ROOT, "profiles", md_name)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256_16"):
+            k, v = line.split(":", 1)
+            fields[k] = v.split()[0]
+    h = hashlib.sha256()
+    for f in sources:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if fields.get("source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
-    ap.add_argument("--only", choices=["all", "scan_fwd", "step"], default="all",
-                    help="restrict the timed work (for profiling runs)")
+    ap.add_argument("--only", choices=["all", "scan_fwd", "step", "copy"], default="all",
+                    help="restrict the timed work (for profiling runs); 'copy' runs a plain "
+                         "1 GiB device copy, the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Naju scan path has no multi-GPU "
@@ -65,6 +88,21 @@ def main():
     from selective_state_space_naju_amd import inputs
 
     dev = torch.device("cuda:0")
+    if args.only == "copy":
+        nbytes = 1 << 30
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
+                          "ms": round(dt * 1e3, 4), "GB_per_s": round(2 * nbytes / dt / 1e9, 1)}))
+        return
     w = inputs.WORKLOADS[WORKLOAD]
     Bt, L, Di, N = w.Bt, w.L, w.Di, w.N
     e = 2
@@ -130,24 +168,25 @@ def main():
 
     # ---------------------------------------------------------------- warmup
     for k in range(args.warmup):
-        block_fwd(k % NSETS)
-        block_bwd(k % NSETS)
-        scan_fwd(k % NSETS)
+        if args.only in ("all", "step"):
+            block_fwd(k % NSETS)
+            block_bwd(k % NSETS)
+        if args.only in ("all", "scan_fwd"):
+            scan_fwd(k % NSETS)
     torch.cuda.synchronize()
 
-    res = {}
     # ---------------------------------------------------------- timed steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        block_fwd(k % NSETS)
-        block_bwd(k % NSETS)
-    torch.cuda.synchronize()
-    t_step = (time.perf_counter() - t0) / args.steps
-    if args.only == "step":
-        pass
+    t_step = float("nan")
+    if args.only in ("all", "step"):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            block_fwd(k % NSETS)
+            block_bwd(k % NSETS)
+        torch.cuda.synchronize()
+        t_step = (time.perf_counter() - t0) / args.steps
     # per-kernel timing (after the timed steps, same inputs)
-    n_ev = max(args.steps, 10)
+    n_ev = args.steps if args.only != "all" else max(args.steps, 10)
     t_sf = timed_launches(scan_fwd, n_ev) if args.only in ("all", "scan_fwd") else None
     t_bf = timed_launches(block_fwd, n_ev) if args.only in ("all", "step") else None
     t_bb = timed_launches(block_bwd, n_ev) if args.only in ("all", "step") else None
@@ -168,15 +207,29 @@ def main():
                        "alg_bytes": int(by), "GB_per_s": round(by / (ms * 1e-3) / 1e9, 1),
                        "pct_hbm_peak": round(100 * by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
 
-    # roofline of the forward scan kernel (one kernel per call)
-    rf = None
-    if "scan_fwd" in parts:
-        by = parts["scan_fwd"]["alg_bytes"]
-        ms = parts["scan_fwd"]["ms_mean"]
+    def roofline(part, kernel, traffic_md=None, sources=()):
+        by = parts[part]["alg_bytes"]
+        ms = parts[part]["ms_mean"]
         ach = by / (ms * 1e-3) / 1e9
-        rf = {"kernel": "fwd_kernel<bf16,16,scan>", "bound": "hbm", "achieved": round(ach, 1),
-              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-              "traffic": None}
+        return {"kernel": kernel, "bound": "hbm", "achieved": round(ach, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(traffic_md, sources),
+                "ms_per_launch": round(ms, 4), "alg_bytes_per_launch": int(by)}
+
+    fwd_src = ("selective_state_space_naju_amd/csrc/naju_fwd_mfma.hip",
+               "selective_state_space_naju_amd/csrc/naju_device.h",
+               "selective_state_space_naju_amd/csrc/naju_launch.h")
+    rf_scan = (roofline("scan_fwd", "naju::fwd_mfma_kernel<false> (naju_scan_fwd)",
+                        "hbm_traffic_fwd_mfma_scan_bf16_b8_l2048_d1536_n16.md", fwd_src)
+               if "scan_fwd" in parts else None)
+    # dominant part of the timed step
+    rf = rf_scan
+    if "block_bwd" in parts and "block_fwd" in parts:
+        if parts["block_bwd"]["ms_mean"] >= parts["block_fwd"]["ms_mean"]:
+            rf = roofline("block_bwd", "naju_block_bwd call: naju::bwd_kernel<bf16,16,block> "
+                          "+ 3 reduction kernels")
+        else:
+            rf = roofline("block_fwd", "naju::fwd_mfma_kernel<true> (naju_block_fwd)")
 
     cpu = None
     if not args.no_cpu:
@@ -195,12 +248,12 @@ def main():
 
     out = {
         "metric": METRIC,
-        "value": round(tokens / t_step, 1),
+        "value": round(tokens / t_step, 1) if t_step == t_step else None,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(t_step * 1e3, 4),
+        "ms_per_step": round(t_step * 1e3, 4) if t_step == t_step else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -210,6 +263,7 @@ def main():
                    "d_state": N, "io": "bf16", "state": "f32",
                    "step": "block fwd (with checkpoints) + block bwd"},
         "roofline": rf,
+        "roofline_scan_fwd": rf_scan,
         "cpu_baseline": cpu,
         "parts": parts,
     }
