@@ -226,7 +226,7 @@ def main():
     rf = rf_scan
     if "block_bwd" in parts and "block_fwd" in parts:
         if parts["block_bwd"]["ms_mean"] >= parts["block_fwd"]["ms_mean"]:
-            rf = roofline("block_bwd", "naju_block_bwd call: naju::bwd_kernel<bf16,16,block> "
+            rf = roofline("block_bwd", "naju_block_bwd call: naju::bwd_mfma_kernel<true> + fix-up "
                           "+ 3 reduction kernels")
         else:
             rf = roofline("block_fwd", "naju::fwd_mfma_kernel<true> (naju_block_fwd)")

@@ -26,6 +26,8 @@
 //           token sums (dD, dconv_w) as per-wave partials.  Small follow-up
 //           kernels reduce the partials in a fixed order (deterministic) and
 //           complete the convolution transpose across wave boundaries.
+#include <stdlib.h>
+
 #include "naju_device.h"
 #include "naju_launch.h"
 
@@ -559,6 +561,9 @@ __global__ void edge_fix_kernel(const int64_t Bt, const int64_t L, const int64_t
     }
 }
 
+template <typename IO>
+static hipError_t launch_bwd_finish(const BwdArgs &g, hipStream_t stream);
+
 template <typename IO, int N, bool BLOCK>
 static hipError_t launch_bwd_t(const BwdArgs &g, hipStream_t stream)
 {
@@ -581,6 +586,22 @@ static hipError_t launch_bwd_t(const BwdArgs &g, hipStream_t stream)
                        incl, bc, dd, dw, edge);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    return launch_bwd_finish<IO>(g, stream);
+}
+
+// dB/dC from the per-tile partials, dD/dconv_w from the per-wave partials, and
+// the conv transpose at wave edges (all in a fixed order).
+template <typename IO>
+static hipError_t launch_bwd_finish(const BwdArgs &g, hipStream_t stream)
+{
+    const int N = g.N;
+    const BwdPlan pl = bwd_plan(g.Bt, g.L, g.Di, g.N, g.block);
+    char *ws = (char *)g.ws;
+    float *bc = (float *)(ws + pl.off_bc);
+    float *dd = (float *)(ws + pl.off_dd);
+    float *dw = (float *)(ws + pl.off_dw);
+    float *edge = (float *)(ws + pl.off_edge);
+    hipError_t e;
     {
         const int64_t rows = g.Bt * g.L;
         const int64_t tot = rows * 2 * N;
@@ -591,9 +612,9 @@ static hipError_t launch_bwd_t(const BwdArgs &g, hipStream_t stream)
     }
     hipLaunchKernelGGL(dd_reduce_kernel, dim3((unsigned)((g.Di + 63) / 64)), dim3(1024), 0, stream,
                        g.Bt * pl.n_waves, g.Di, (const float *)dd, (const float *)dw, g.dD,
-                       BLOCK ? g.dconv_w : (float *)nullptr);
+                       g.block ? g.dconv_w : (float *)nullptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if constexpr (BLOCK) {
+    if (g.block) {
         const int64_t tot = g.Bt * pl.n_waves * g.Di;
         hipLaunchKernelGGL((edge_fix_kernel<IO>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0,
                            stream, g.Bt, g.L, g.Di, pl.n_waves, g.conv_w, (const float *)edge,
@@ -603,8 +624,25 @@ static hipError_t launch_bwd_t(const BwdArgs &g, hipStream_t stream)
     return hipSuccess;
 }
 
+// The matrix-core variant serves bf16 activations with d_state 16 when B and C
+// allow 16-byte loads; NAJU_BWD_VARIANT=rr forces the register recurrence.
+static bool use_bwd_mfma(const BwdArgs &g)
+{
+    static const bool forced_rr = [] {
+        const char *v = getenv("NAJU_BWD_VARIANT");
+        return v && v[0] == 'r' && v[1] == 'r';
+    }();
+    return !forced_rr && g.io == 1 && g.N == 16 && ((uintptr_t)g.B % 16) == 0 &&
+           ((uintptr_t)g.C % 16) == 0;
+}
+
 hipError_t launch_bwd(const BwdArgs &g, hipStream_t stream)
 {
+    if (use_bwd_mfma(g)) {
+        hipError_t e = launch_bwd_mfma(g, stream);
+        if (e != hipSuccess) return e;
+        return launch_bwd_finish<bf16>(g, stream);
+    }
     if (g.io == 0) {
         if (g.N == 16) return g.block ? launch_bwd_t<float, 16, true>(g, stream)
                                       : launch_bwd_t<float, 16, false>(g, stream);

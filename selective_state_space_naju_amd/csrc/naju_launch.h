@@ -71,6 +71,10 @@ struct BwdPlan {
                       //   rows 3-5: in-wave partial du of its last 3 tokens
     size_t off_ckpt;  // recomputed checkpoints when the caller passes none
     size_t off_fwd;   // workspace of the checkpoint-only forward
+    // matrix-core backward: chunks its rescaled form cannot take
+    size_t off_fixmask;  // [Bt][n_tiles][n_waves] u32 channel-group bits
+    size_t off_fixlist;  // [Bt][n_tiles][n_waves] u32 keys
+    size_t off_fixmu;    // [Bt][n_waves][N][Di] fp32 entering adjoints
     size_t bytes;
 };
 
@@ -78,20 +82,26 @@ inline BwdPlan bwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N, bool block
 {
     BwdPlan p{};
     const FwdPlan f = fwd_plan(Bt, L, Di, N);
+    // look-back regions sized for the finer of the two chunkings (128 tokens)
+    const FwdPlan f4 = fwd_plan(Bt, L, Di, N, kMfmaW);
     p.n_tiles = f.n_tiles;
     p.n_chunks = f.n_chunks;
     p.n_wg = f.n_wg;
     p.n_waves = f.n_waves;
-    p.off_flags = f.off_flags;
-    p.off_agg = f.off_agg;
-    p.off_incl = f.off_incl;
-    p.off_bc = f.bytes;
+    p.off_flags = f4.off_flags;
+    p.off_agg = f4.off_agg;
+    p.off_incl = f4.off_incl;
+    p.off_bc = f4.bytes;
     p.off_dd = align256(p.off_bc + (size_t)Bt * L * p.n_tiles * 2 * N * 4);
     p.off_dw = align256(p.off_dd + (size_t)Bt * p.n_waves * Di * 4);
     p.off_edge = align256(p.off_dw + (block ? (size_t)Bt * p.n_waves * Di * 4 * 4 : 0));
     p.off_ckpt = align256(p.off_edge + (block ? (size_t)Bt * p.n_waves * 6 * Di * 4 : 0));
     p.off_fwd = align256(p.off_ckpt + ckpt_bytes(Bt, L, Di, N));
-    p.bytes = align256(p.off_fwd + fwd_ws_bytes(Bt, L, Di, N));
+    const size_t n_keys = (size_t)Bt * (size_t)((Di + 63) / 64) * (size_t)p.n_waves;
+    p.off_fixmask = align256(p.off_fwd + fwd_ws_bytes(Bt, L, Di, N));
+    p.off_fixlist = align256(p.off_fixmask + 4 * n_keys);
+    p.off_fixmu = align256(p.off_fixlist + 4 * n_keys);
+    p.bytes = align256(p.off_fixmu + (N == 16 ? ckpt_bytes(Bt, L, Di, N) : 0));
     return p;
 }
 
@@ -134,6 +144,7 @@ struct BwdArgs {
 hipError_t launch_fwd(const FwdArgs &g, hipStream_t stream);
 hipError_t launch_fwd_mfma(const FwdArgs &g, hipStream_t stream);  // bf16, d_state 16
 hipError_t launch_bwd(const BwdArgs &g, hipStream_t stream);
+hipError_t launch_bwd_mfma(const BwdArgs &g, hipStream_t stream);  // bf16, d_state 16
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_empty_seq(int io, int64_t Bt, int64_t Di, int64_t N, const float *x0,
                             float *x_final, const void *conv_state, void *conv_state_out,

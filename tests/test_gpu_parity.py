@@ -239,3 +239,40 @@ def test_bf16_fallback_chunks(block):
     assert_close("y", yg[m], ys[m], TOL["bf16"])
     mx = ~np.isnan(xf)
     assert_close("x_final", xgh[mx], xf[mx], TOL["bf16"])
+
+
+@pytest.mark.parametrize("block", [False, True], ids=["scan", "block"])
+def test_bf16_bwd_fallback_chunks(block):
+    """Backward on the matrix-core path with chunks it must hand to the plain reverse
+    recurrence (f = 0 resets, very wide forget gates), mixed with ordinary chunks."""
+    Bt, L, Di, N = 2, 300, 128, 16
+    d = inputs.draw(Bt, L, Di, N, io="bf16", seed=23, x0=True, backward=True, dx_final=True,
+                    block=block, conv_state=block)
+    d["a"][0, 40, :5] = -np.inf
+    d["a"][1, 130:160, 70:] = inputs.bf16_round(
+        (np.random.default_rng(4).standard_normal((30, Di - 70)) * 6 - 6).astype(np.float32))
+    print("bwd fallback", block, flush=True)
+    D, x0, dxf = f32_dev(d["D"]), f32_dev(d["x0"]), f32_dev(d["dx_final"])
+    if block:
+        ref = oracle.block_bwd(d["u"], d["z"], d["conv_w"], d["a"], d["b"], d["B"], d["C"], d["D"],
+                               d["x0"], d["dy"], d["dx_final"], d["conv_state"])
+        ref["dconv_w"] = ref["dw"]
+        t = {k: to_dev(d[k], "bf16") for k in ("u", "z", "a", "b", "B", "C", "dy", "conv_state")}
+        g = nb.block_bwd(t["u"], t["z"], f32_dev(d["conv_w"]), t["a"], t["b"], t["B"], t["C"], D,
+                         t["dy"], x0, dxf, t["conv_state"])
+        names = ("du", "dz", "da", "db", "dB", "dC", "dD", "dx0", "dconv_w", "dconv_state")
+    else:
+        ref = oracle.scan_bwd(d["h"], d["a"], d["b"], d["B"], d["C"], d["D"], d["x0"], d["dy"],
+                              d["dx_final"])
+        t = {k: to_dev(d[k], "bf16") for k in ("h", "a", "b", "B", "C", "dy")}
+        g = nb.scan_bwd(t["h"], t["a"], t["b"], t["B"], t["C"], D, t["dy"], x0, dxf)
+        names = ("dh", "da", "db", "dB", "dC", "dD", "dx0")
+    torch.cuda.synchronize()
+    _grad_checks(names, g, ref, "bf16")
+    # the workspace was left clean: a second call agrees with the first
+    g2 = (nb.block_bwd(t["u"], t["z"], f32_dev(d["conv_w"]), t["a"], t["b"], t["B"], t["C"], D,
+                       t["dy"], x0, dxf, t["conv_state"]) if block else
+          nb.scan_bwd(t["h"], t["a"], t["b"], t["B"], t["C"], D, t["dy"], x0, dxf))
+    torch.cuda.synchronize()
+    for k in names:
+        assert_close(k + "(2nd)", host(g2[k]), host(g[k]), 1e-2)
