@@ -562,7 +562,7 @@ __global__ void edge_fix_kernel(const int64_t Bt, const int64_t L, const int64_t
 }
 
 template <typename IO>
-static hipError_t launch_bwd_finish(const BwdArgs &g, hipStream_t stream);
+static hipError_t launch_bwd_finish(const BwdArgs &g, int n_parts, hipStream_t stream);
 
 template <typename IO, int N, bool BLOCK>
 static hipError_t launch_bwd_t(const BwdArgs &g, hipStream_t stream)
@@ -586,13 +586,13 @@ static hipError_t launch_bwd_t(const BwdArgs &g, hipStream_t stream)
                        incl, bc, dd, dw, edge);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_bwd_finish<IO>(g, stream);
+    return launch_bwd_finish<IO>(g, pl.n_tiles, stream);
 }
 
-// dB/dC from the per-tile partials, dD/dconv_w from the per-wave partials, and
-// the conv transpose at wave edges (all in a fixed order).
+// dB/dC from the n_parts per-token partials, dD/dconv_w from the per-wave
+// partials, and the conv transpose at wave edges (all in a fixed order).
 template <typename IO>
-static hipError_t launch_bwd_finish(const BwdArgs &g, hipStream_t stream)
+static hipError_t launch_bwd_finish(const BwdArgs &g, int n_parts, hipStream_t stream)
 {
     const int N = g.N;
     const BwdPlan pl = bwd_plan(g.Bt, g.L, g.Di, g.N, g.block);
@@ -606,7 +606,7 @@ static hipError_t launch_bwd_finish(const BwdArgs &g, hipStream_t stream)
         const int64_t rows = g.Bt * g.L;
         const int64_t tot = rows * 2 * N;
         hipLaunchKernelGGL((bc_reduce_kernel<IO>), dim3((unsigned)((tot + 255) / 256)), dim3(256),
-                           0, stream, rows, pl.n_tiles, 2 * N, (const float *)bc, (IO *)g.dB,
+                           0, stream, rows, n_parts, 2 * N, (const float *)bc, (IO *)g.dB,
                            (IO *)g.dC);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -632,8 +632,13 @@ static bool use_bwd_mfma(const BwdArgs &g)
         const char *v = getenv("NAJU_BWD_VARIANT");
         return v && v[0] == 'r' && v[1] == 'r';
     }();
-    return !forced_rr && g.io == 1 && g.N == 16 && ((uintptr_t)g.B % 16) == 0 &&
-           ((uintptr_t)g.C % 16) == 0;
+    if (forced_rr || g.io != 1 || g.N != 16 || ((uintptr_t)g.B % 16) != 0 ||
+        ((uintptr_t)g.C % 16) != 0)
+        return false;
+    // buffer ranges of 32 token rows and 32-bit fix-list keys
+    const MfmaBwdShape m = mfma_bwd_shape(g.Bt, g.L, g.Di);
+    return g.Di < ((int64_t)1 << 24) &&
+           (double)g.Bt * m.n_super * (double)((g.L + 31) / 32) < 4.0e9;
 }
 
 hipError_t launch_bwd(const BwdArgs &g, hipStream_t stream)
@@ -641,7 +646,7 @@ hipError_t launch_bwd(const BwdArgs &g, hipStream_t stream)
     if (use_bwd_mfma(g)) {
         hipError_t e = launch_bwd_mfma(g, stream);
         if (e != hipSuccess) return e;
-        return launch_bwd_finish<bf16>(g, stream);
+        return launch_bwd_finish<bf16>(g, mfma_bwd_shape(g.Bt, g.L, g.Di).n_super, stream);
     }
     if (g.io == 0) {
         if (g.N == 16) return g.block ? launch_bwd_t<float, 16, true>(g, stream)

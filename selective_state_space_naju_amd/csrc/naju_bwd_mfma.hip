@@ -2,33 +2,36 @@
 // bf16 activations and d_state 16 (scan and block).
 //
 // Differentiates the "Core equations" of the Naju reproduction README (arXiv
-// 2607.21000) and its block flowchart.  Inside a wave's 32-token chunk, with
-// the chunk-local running product P_n = prod_{j<=n} f_j, the rescaled writes
-// W' = w/P, the rescaled readout gradients Gp = g P (g = dLoss/dys), the
-// shared token-by-token matrix G[m,k] = C_m.B_k/sqrt(N), the entering state
-// x_in (forward checkpoint) and Mu = P_last mu_in (the adjoint flowing in from
-// after the chunk, rescaled), every gradient is a product of token x token
-// matrices with per-channel columns, or a contraction over channels:
+// 2607.21000) and its block flowchart.  Inside a wave's 32-token chunk, per
+// channel, with the chunk-local running product P_n = prod_{j<=n} f_j, the
+// rescaled writes W' = w/P, the readout gradients g = dLoss/dys and Gp = g P,
+// the token x token matrix G[m,k] = C_m.B_k/sqrt(N) (shared by all channels),
+// the entering state x_in (forward checkpoint), the adjoint mu_in arriving
+// after the chunk's last token and Mu = P_last mu_in:
 //
-//   dw_k  = (1/P_k) [ (G^T_{m>=k} Gp)_k + U_k ],        U_k = B_k . Mu
-//   f_n dLoss/df_n = T1_n + T24_n + T3                  (da = sigma(-a) * that)
-//     T1_n  = sum_{m>=n} Gp_m V_m,                       V_m = C_m . x_in / sqrt(N)
-//     T24_n = sum_{j<n} ( c_j - r_j + W'_j U_j )
-//       r_n = Gp_n (G_{k<n} W')_n,   c_n = W'_n (G^T_{m>n} Gp)_n
-//     T3    = Mu . x_in
-//   dC_m  = ( Gp X_in + tril(H) B )_m / sqrt(N),         H = Gp W'^T (over channels)
-//   dB_k  = ( tril(H)^T C )_k / sqrt(N) + (W' Mu)_k
-//   mu_out = Gp^T C / sqrt(N) + P_last mu_in             (the reverse carry)
+//   Z_n    = (G_{k<=n} W')_n + C_n.x_in/sqrt(N)          (ys_n = P_n Z_n + D h_n)
+//   dw_k   = (1/P_k) [ (G^T_{m>=k} Gp)_k + B_k.Mu ]      (adjoint of w = sigma(b) h)
+//   mu_out = Gp^T C/sqrt(N) + Mu                          (adjoint entering the chunk)
+//   dC_m   = ( Gp X_in + tril(H) B )_m / sqrt(N),          H = Gp W'^T over channels
+//   dB_k   = ( tril(H)^T C )_k / sqrt(N) + (W' Mu)_k
 //
-// All of these run on v_mfma_f32_32x32x16_bf16 with the same lane/K-slot
-// order as the forward (lane l owns column l%32 and the 16 chunk tokens
-// {8q + 4h + r}, h = l/32).  Carried quantities (x_in, Mu, the carry's Gp)
-// use bf16 hi + lo operand pairs; per-token products use one bf16 operand.
+// and the gate gradient follows from Phi_n = f_n dLoss/df_n, which obeys
+//   Phi_0 = mu_out . x_in,   Phi_{n+1} = Phi_n - ( g_n (ys_n - D h_n) - w_n dw_n )
+// (from lambda_n . x_n = g_n (ys_n - D h_n) + Phi_{n+1} and x_n - f_n x_{n-1} =
+// w_n B_n), so da_n = sigma(-a_n) Phi_n is an exclusive prefix sum over the
+// chunk.  Every contraction runs on v_mfma_f32_32x32x16_bf16 with the forward's
+// lane order (lane l owns column l%32 and the 16 chunk tokens {8q + 4h + r},
+// h = l/32); carried quantities (x_in, Mu, Gp) use bf16 hi + lo operand pairs.
 //
-// A wave whose chunk has prod(1/f) > 2^64 or a non-finite input cannot use the
-// rescaled form.  It still publishes its exact reverse carry (which only needs
-// Gp = g P), records itself in a list with its entering adjoint, and a small
-// follow-up kernel recomputes its gradients with the plain reverse recurrence.
+// A workgroup owns 128 tokens (four token-waves) of a super-tile of n_sub
+// 32-channel tiles, visited in turn; its dB/dC partial over those channels is
+// accumulated in the matrix registers and written once.  Activations are read
+// and written through buffer resources whose range ends at the last valid
+// token, so ragged tails need no branches.  A wave whose chunk has
+// prod(1/f) > 2^64 or a non-finite value cannot use the rescaled form: it
+// still publishes its exact reverse carry, records itself with its entering
+// adjoint, and a follow-up kernel recomputes its gradients with the plain
+// reverse recurrence.
 #include "naju_device.h"
 #include "naju_launch.h"
 
@@ -36,8 +39,12 @@ namespace naju {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 namespace {
+
+constexpr int kTW = 4;                  // token-waves per workgroup (128 tokens)
+constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every range used here
 
 __device__ __forceinline__ f32x16 mma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
 {
@@ -50,8 +57,6 @@ __device__ __forceinline__ void split2(float v, __bf16 &hi, __bf16 &lo)
     lo = (__bf16)(v - (float)hi);
 }
 
-__device__ __forceinline__ __bf16 asbf(bf16 v) { return __builtin_bit_cast(__bf16, v); }
-
 // Bit pattern of element s of a bf16x8.  Goes through the whole vector: a
 // bit_cast of a single __bf16 vector element to an integer is mis-lowered by
 // this compiler (every element reads as element 0).
@@ -62,43 +67,72 @@ __device__ __forceinline__ bf16 bits_of(const bf16x8 &v, int s)
     return (bf16)(w >> (16 * (s & 1)));
 }
 
-constexpr int kTW = 4;  // token-waves per workgroup (128 tokens)
-constexpr int kCG = 2;  // channel groups of 32 per workgroup (64 channels)
+// Raw buffer over [p, p + bytes): loads past the end return 0, stores past the
+// end are dropped (the hardware range check of a stride-0 buffer).
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ float ldb(rsrc_t r, uint32_t off)
+{
+    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0) << 16);
+}
+__device__ __forceinline__ void stb(rsrc_t r, uint32_t off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(v), r, off, 0, 0);
+}
+
+// Value held by lane l ^ 32.  v_permlane32_swap exchanges the upper half of
+// its first operand with the lower half of its second; with both operands
+// equal, each half then finds its partner's value in the other result.
+__device__ __forceinline__ float xhalf(float v, bool upper)
+{
+    const uint32_t u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(upper ? r[0] : r[1]);
+}
 
 }  // namespace
 
 template <bool BLOCK>
-__global__ __launch_bounds__(512, 1) void bwd_mfma_kernel(
-    const int64_t Bt, const int64_t L, const int64_t Di, const int n_tiles, const int n_chunks,
-    const int64_t n_waves, const float scale, const bf16 *__restrict__ hu,
-    const bf16 *__restrict__ a, const bf16 *__restrict__ bg, const bf16 *__restrict__ Bm,
-    const bf16 *__restrict__ Cm, const float *__restrict__ D, const bf16 *__restrict__ z,
-    const float *__restrict__ conv_w, const bf16 *__restrict__ conv_state,
-    const float *__restrict__ ckpt, const bf16 *__restrict__ dy,
-    const float *__restrict__ dx_final, bf16 *__restrict__ dhu, bf16 *__restrict__ da,
-    bf16 *__restrict__ db, bf16 *__restrict__ dz, float *__restrict__ dx0, WsHeader *hdr,
-    uint32_t *flags, float *agg, float *incl, float *__restrict__ bc_part,
+__global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
+    const int64_t Bt, const int64_t L, const int64_t Di, const int n_tiles, const int n_sub,
+    const int n_super, const int n_chunks, const int64_t n_waves, const float scale,
+    const bf16 *__restrict__ hu, const bf16 *__restrict__ a, const bf16 *__restrict__ bg,
+    const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, const float *__restrict__ D,
+    const bf16 *__restrict__ z, const float *__restrict__ conv_w,
+    const bf16 *__restrict__ conv_state, const float *__restrict__ ckpt,
+    const bf16 *__restrict__ dy, const float *__restrict__ dx_final, bf16 *__restrict__ dhu,
+    bf16 *__restrict__ da, bf16 *__restrict__ db, bf16 *__restrict__ dz, float *dx0,
+    WsHeader *hdr, uint32_t *flags, float *agg, float *incl, float *__restrict__ bc_part,
     float *__restrict__ dd_part, float *__restrict__ dw_part, float *__restrict__ edge,
     uint32_t *fix_mask, uint32_t *fix_list, float *fix_mu)
 {
     constexpr int N = 16, T = 32;
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
-    const int tw = wv & (kTW - 1);  // token-wave
-    const int grp = wv / kTW;       // channel group
+    // token-wave (wave-uniform; readfirstlane lets the compiler keep everything
+    // derived from it -- token ranges, buffer descriptors -- in scalar registers)
+    const int tw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31;
     const int hh = lane >> 5;
+    const bool upper = hh != 0;
 
     __shared__ uint32_t s_ticket, s_epoch;
-    __shared__ float sQ[kTW][64];
-    __shared__ float sR[kTW][16][64];
-    __shared__ float sMu[16][64];
-    __shared__ __attribute__((aligned(16))) bf16 sGpT[8][32][32];  // [wave][token][channel]
-    __shared__ __attribute__((aligned(16))) bf16 sWpT[8][32][32];
-    __shared__ float sXin[8][32][17];  // [wave][channel][state] (+1 pad)
-    __shared__ float sMuw[8][32][17];
-    __shared__ float sDiag[kTW][32];
-    __shared__ float sDBC[kTW][32][32];  // group-1 partial dB|dC per token
+    // reverse carries of the four waves and the adjoint entering the workgroup's
+    // last token
+    __shared__ float sQ[kTW][32];
+    __shared__ float sR[kTW][16][32];
+    __shared__ float sMu[16][32];
+    // per-token factors consumed once, after the matrix products: sigma(-a) and
+    // dy SiLU'(z)  [wave][slot][lane]
+    __shared__ float sSA[kTW][16][64];
+    __shared__ float sGZ[BLOCK ? kTW : 1][16][64];
+    // per-wave transposes for the channel contractions (bf16, padded rows)
+    __shared__ __attribute__((aligned(16))) bf16 sGT[kTW][32][40];  // Gp  [token][channel]
+    __shared__ __attribute__((aligned(16))) bf16 sWT[kTW][32][40];  // W'  [token][channel]
+    __shared__ __attribute__((aligned(16))) bf16 sXT[kTW][16][40];  // x_in [state][channel]
+    __shared__ __attribute__((aligned(16))) bf16 sMT[kTW][16][40];  // Mu   [state][channel]
 
     if (threadIdx.x == 0) {
         s_ticket = add_agent(&hdr->ticket, 1u);
@@ -107,531 +141,560 @@ __global__ __launch_bounds__(512, 1) void bwd_mfma_kernel(
     __syncthreads();
     const uint32_t ticket = s_ticket;
     const uint32_t ep = s_epoch;
-    const uint32_t per_chunk = (uint32_t)(Bt * n_tiles);
+    const uint32_t per_chunk = (uint32_t)(Bt * n_super);
     const int chunk = n_chunks - 1 - (int)(ticket / per_chunk);
     const int rem = (int)(ticket % per_chunk);
-    const int bi = rem / n_tiles;
-    const int tile = rem % n_tiles;
+    const int bi = rem / n_super;
+    const int sup = rem % n_super;
     const int64_t n0 = (int64_t)chunk * (kTW * T) + (int64_t)tw * T;
     const int64_t wrow = (int64_t)chunk * kTW + tw;
     const bool active = n0 < L;
-    const int64_t c = (int64_t)tile * 64 + grp * 32 + col;
-    const bool valid = c < Di;
+    const int Lw = active ? (int)(L - n0 < T ? L - n0 : T) : 0;  // valid tokens of this wave
     const int64_t tokbase = (int64_t)bi * L;
-    const float Dc = valid ? D[c] : 0.f;
     auto tok = [&](int i) -> int { return 8 * (i >> 2) + 4 * hh + (i & 3); };
-    auto tval = [&](int i) -> bool { return n0 + tok(i) < L; };
-
-    float cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f;
-    if (BLOCK && valid) {
-        cw0 = conv_w[c * 4 + 0];
-        cw1 = conv_w[c * 4 + 1];
-        cw2 = conv_w[c * 4 + 2];
-        cw3 = conv_w[c * 4 + 3];
-    }
-    // u at absolute token m (conv_state for m < 0, zero past the end)
-    auto u_at = [&](int64_t m) -> float {
-        if (!valid || m >= L) return 0.f;
-        if (m >= 0) return to_f(hu[(tokbase + m) * Di + c]);
-        if (m >= -3 && conv_state) return to_f(conv_state[((int64_t)bi * 3 + (m + 3)) * Di + c]);
-        return 0.f;
-    };
+    auto tval = [&](int i) -> bool { return tok(i) < Lw; };
 
     // ------------------------------------------------ token-shared operands
-    bf16x8 Bop, Cop, Csc, Bsv[2], Csv[2];
+    // Bop/Cop: A/B-operand rows (token col, states 8h..8h+7); Bsv/Csv: the
+    // transposed operands (tokens tok(i)) -- Csv holds state col in columns
+    // 0..15, Bsv state col-16 in columns 16..31, so dB and dC accumulate into the
+    // two halves of one matrix.  C is used pre-scaled (scale = 1/4 is exact in
+    // bf16).
+    bf16x8 Bop, Csc, Bsv[2], Csv[2];
     {
-        const int64_t n = n0 + col;
-        if (n < L) {
-            Bop = __builtin_bit_cast(bf16x8, *(const uint4 *)(Bm + (tokbase + n) * N + 8 * hh));
-            Cop = __builtin_bit_cast(bf16x8, *(const uint4 *)(Cm + (tokbase + n) * N + 8 * hh));
-        } else {
-#pragma unroll
-            for (int s = 0; s < 8; ++s) Bop[s] = Cop[s] = (__bf16)0.f;
-        }
+        const rsrc_t rB = make_rsrc(Bm + (tokbase + (active ? n0 : 0)) * N, (uint32_t)Lw * N * 2);
+        const rsrc_t rC = make_rsrc(Cm + (tokbase + (active ? n0 : 0)) * N, (uint32_t)Lw * N * 2);
+        const uint32_t ro = (uint32_t)(col * N + 8 * hh) * 2;
+        Bop = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rB, ro, 0, 0));
+        const bf16x8 Cop =
+            __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rC, ro, 0, 0));
 #pragma unroll
         for (int s = 0; s < 8; ++s) Csc[s] = (__bf16)((float)Cop[s] * scale);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            bf16 vb = 0, vc = 0;
-            if (col < N && tval(i)) {
-                vb = Bm[(tokbase + n0 + tok(i)) * N + col];
-                vc = Cm[(tokbase + n0 + tok(i)) * N + col];
-            }
-            Bsv[i >> 3][i & 7] = asbf(vb);
-            Csv[i >> 3][i & 7] = (__bf16)(to_f(vc) * scale);
-        }
-    }
-    // G in A-layout (rows = this lane's column token): g1[i] = B_tok(i).C_col,
-    // g2[i] = C_tok(i).B_col
-    bf16x8 GA[2], GTA[2];
-    {
-        f32x16 zero = {};
-        const f32x16 g1 = mma(Bop, Cop, zero);
-        const f32x16 g2 = mma(Cop, Bop, zero);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            GA[i >> 3][i & 7] = (__bf16)((tok(i) <= col) ? g1[i] * scale : 0.f);
-            GTA[i >> 3][i & 7] = (__bf16)((tok(i) >= col) ? g2[i] * scale : 0.f);
-            if (grp == 0 && tok(i) == col) sDiag[tw][col] = g1[i] * scale;
+            const uint32_t o = (uint32_t)(tok(i) * N + (col & 15)) * 2;
+            Bsv[i >> 3][i & 7] = (__bf16)ldb(rB, col >= N ? o : kOOB);
+            Csv[i >> 3][i & 7] = (__bf16)(ldb(rC, col < N ? o : kOOB) * scale);
         }
     }
 
-    // ------------------------------------------------------------ gates
-    float Pv[16];
-    bf16x8 WB[2], GpH[2], GpL[2];
-    bool ok = true;
-    {
-        float invf[16], wr[16], gg[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t g0 = n0 + 8 * q + 4 * hh;
-            float uw[7];
-            if (BLOCK) {
-#pragma unroll
-                for (int k = 0; k < 7; ++k) uw[k] = u_at(g0 - 3 + k);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 4 * q + r;
-                const int64_t n = g0 + r;
-                float e = 0.f, ib = 0.f, h = 0.f, gv = 0.f;
-                if (valid && n < L) {
-                    const int64_t t = (tokbase + n) * Di + c;
-                    e = ex2(-to_f(a[t]) * kLog2e);
-                    ib = sigm(to_f(bg[t]));
-                    gv = to_f(dy[t]);
-                    if (BLOCK) {
-                        const float pre = cw0 * uw[r] + cw1 * uw[r + 1] + cw2 * uw[r + 2] +
-                                          cw3 * uw[r + 3];
-                        h = pre * sigm(pre);
-                        const float zv = to_f(z[t]);
-                        gv *= zv * sigm(zv);
-                    } else {
-                        h = to_f(hu[t]);
-                    }
-                }
-                invf[i] = 1.f + e;
-                wr[i] = ib * h;
-                gg[i] = gv;
-                ok = ok && (__builtin_fabsf(h) < 1e30f) && (__builtin_fabsf(gv) < 1e30f);
-            }
-        }
-        float tot[4], cum[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            float run = 1.f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                run *= invf[4 * q + r];
-                cum[4 * q + r] = run;
-            }
-            tot[q] = run;
-        }
-        float ptot[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) ptot[q] = __shfl_xor(tot[q], 32);
-        float E[4], acc = 1.f;
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            const bool mine = (g & 1) == hh;
-            const float Tg = mine ? tot[g >> 1] : ptot[g >> 1];
-            if (mine) E[g >> 1] = acc;
-            acc *= Tg;
-        }
-        ok = ok && (acc <= 18446744073709551616.f);  // 2^64; false for NaN
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float invP = E[i >> 2] * cum[i];
-            const float P = rcp(invP);
-            Pv[i] = P;
-            const float wp = wr[i] * invP;
-            ok = ok && (__builtin_fabsf(wp) < 1e30f);
-            WB[i >> 3][i & 7] = (__bf16)wp;
-            __bf16 hi, lo;
-            split2(gg[i] * P, hi, lo);
-            GpH[i >> 3][i & 7] = hi;
-            GpL[i >> 3][i & 7] = lo;
-        }
-    }
-    const bool wave_ok = __all(ok);
+    f32x16 dBC = {};  // dB (columns 0..15) | dC / scale (columns 16..31) of this wave's tokens
+    const int n_sub_here = (n_tiles - sup * n_sub) < n_sub ? (n_tiles - sup * n_sub) : n_sub;
 
-    // ---------------------------- reverse carry pair (Q, R) of this wave -> LDS
-    {
-        f32x16 r = {};
+    for (int st = 0; st < n_sub_here; ++st) {
+        // lane-derived values are re-derived every tile: kept out of loop-invariant
+        // code motion, which would pin dozens of them (masks, offsets) in registers
+        // across the whole loop
+        int ln = threadIdx.x & 63;
+        asm volatile("" : "+v"(ln));
+        const int lane = ln, col = ln & 31, hh = ln >> 5;
+        const bool upper = hh != 0;
+        auto tok = [&](int i) -> int { return 8 * (i >> 2) + 4 * hh + (i & 3); };
+        auto tval = [&](int i) -> bool { return tok(i) < Lw; };
+        const int tile = sup * n_sub + st;
+        const int64_t c = (int64_t)tile * 32 + col;
+        const bool valid = c < Di;
+        const int64_t ebase = (tokbase + (active ? n0 : 0)) * Di + (int64_t)tile * 32;
+        // Element access of every [Bt][L][Di] tensor: slot i = 4q + r is token
+        // 8q + 4h + r.  One buffer per 8-token group q (built on the scalar unit,
+        // ending at the last valid token) and the lane offsets of rows 4h + r.
+        const uint32_t row2 = (uint32_t)Di * 2;
+        uint32_t vr[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            r = mma(GpH[kb], Csv[kb], r);
-            r = mma(GpL[kb], Csv[kb], r);
-        }
-        if (col < N) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sR[tw][col][grp * 32 + tok(i)] = r[i];
-        }
-        if (hh == 1) sQ[tw][grp * 32 + col] = Pv[15];  // P at the chunk's last token
-    }
-    // staging for the channel contractions and the entering state
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        sGpT[wv][tok(i)][col] = bits_of(GpH[i >> 3], i & 7);
-        sWpT[wv][tok(i)][col] = bits_of(WB[i >> 3], i & 7);
-    }
-    {
-        const float *ck = ckpt + ((int64_t)bi * n_waves + wrow) * N * Di + c;
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            sXin[wv][col][8 * hh + k] = (active && valid) ? ck[(int64_t)(8 * hh + k) * Di] : 0.f;
-    }
-    __syncthreads();
+        for (int r = 0; r < 4; ++r) vr[r] = valid ? (uint32_t)((4 * hh + r) * Di + col) * 2 : kOOB;
+        auto grs = [&](const bf16 *t, int q) -> rsrc_t {
+            const int rows = Lw - 8 * q;
+            return make_rsrc(t + ebase + (int64_t)(8 * q) * Di, rows > 0 ? (uint32_t)rows * row2 : 0u);
+        };
+        auto LD = [&](const bf16 *t, int i) -> float { return ldb(grs(t, i >> 2), vr[i & 3]); };
+        auto ST = [&](bf16 *t, int i, float v) { stb(grs(t, i >> 2), vr[i & 3], v); };
 
-    // ----------------------------------- reverse look-back (wave 0, 64 channels)
-    if (wv == 0) {
-        float Qt = 1.f, Rt[16];
-#pragma unroll
-        for (int s = 0; s < 16; ++s) Rt[s] = 0.f;
-        for (int w = kTW - 1; w >= 0; --w) {
-            const float qw = sQ[w][lane];
-#pragma unroll
-            for (int s = 0; s < 16; ++s) Rt[s] = fmaf(qw, Rt[s], sR[w][s][lane]);
-            Qt *= qw;
-        }
-        const int64_t cl = (int64_t)tile * 64 + lane;
-        const bool vl = cl < Di;
-        const size_t me = ((size_t)bi * n_tiles + tile) * n_chunks + chunk;
-        float mu[16];
-        if (chunk == n_chunks - 1) {
-#pragma unroll
-            for (int s = 0; s < 16; ++s) mu[s] = (dx_final && vl) ? dx_final[(bi * Di + cl) * N + s] : 0.f;
-        } else {
-            float *ag = agg + me * (17 * 64);
-            st_agent(ag + lane, Qt);
-#pragma unroll
-            for (int s = 0; s < 16; ++s) st_agent(ag + (1 + s) * 64 + lane, Rt[s]);
-            wait_mem();
-            if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagAgg));
-            float accQ = 1.f, accR[16];
-#pragma unroll
-            for (int s = 0; s < 16; ++s) accR[s] = 0.f;
-            size_t j = me + 1;
-            for (;;) {
-                const uint32_t st = wait_flag(&flags[j], ep, hdr);
-                if (st == kFlagIncl) {
-                    const float *in = incl + j * (16 * 64);
-#pragma unroll
-                    for (int s = 0; s < 16; ++s) mu[s] = fmaf(accQ, ld_agent(in + s * 64 + lane), accR[s]);
-                    break;
-                }
-                const float *pa = agg + j * (17 * 64);
-                const float qj = ld_agent(pa + lane);
-#pragma unroll
-                for (int s = 0; s < 16; ++s) accR[s] = fmaf(accQ, ld_agent(pa + (1 + s) * 64 + lane), accR[s]);
-                accQ *= qj;
-                ++j;
-            }
-        }
-        float *ic = incl + me * (16 * 64);
-#pragma unroll
-        for (int s = 0; s < 16; ++s) {
-            const float mo = fmaf(Qt, mu[s], Rt[s]);
-            st_agent(ic + s * 64 + lane, mo);
-            if (chunk == 0 && dx0 && vl) dx0[(bi * Di + cl) * N + s] = mo;
-        }
-        wait_mem();
-        if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagIncl));
-#pragma unroll
-        for (int s = 0; s < 16; ++s) sMu[s][lane] = mu[s];
-    }
-    __syncthreads();
-
-    // --------------- this wave's entering adjoint, Mu = P_last mu_in, T3 = Mu.x_in
-    float T3;
-    {
-        const int ch = grp * 32 + col;
-        float mu[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) mu[k] = sMu[8 * hh + k][ch];
-        for (int w = kTW - 1; w > tw; --w) {  // adjoint passes the later waves first
-            const float qw = sQ[w][ch];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) mu[k] = fmaf(qw, mu[k], sR[w][8 * hh + k][ch]);
-        }
-        const float pl = sQ[tw][ch];
-        float t3 = 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float m = pl * mu[k];
-            sMuw[wv][col][8 * hh + k] = m;
-            t3 = fmaf(m, sXin[wv][col][8 * hh + k], t3);
-            if (!wave_ok && active && valid)
-                fix_mu[(((int64_t)bi * n_waves + wrow) * N + 8 * hh + k) * Di + c] = mu[k];
-        }
-        T3 = t3 + __shfl_xor(t3, 32);
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    f32x16 dBr = {}, dCr = {};
-    if (!wave_ok) {
-        if (lane == 0 && active) {
-            const uint32_t key = (uint32_t)(((int64_t)bi * n_tiles + tile) * n_waves + wrow);
-            const uint32_t old = __hip_atomic_fetch_or(&fix_mask[key], 1u << grp, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-            if (old == 0) {
-                const uint32_t idx = add_agent(&hdr->pad[0], 1u);
-                fix_list[idx] = key;
-            }
-        }
-    } else if (active) {
-        // operands carrying the entering state / adjoint (hi + lo)
-        bf16x8 Xh, Xl, Mh, Ml;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            __bf16 h1, l1, h2, l2;
-            split2(sXin[wv][col][8 * hh + k], h1, l1);
-            split2(sMuw[wv][col][8 * hh + k], h2, l2);
-            Xh[k] = h1;
-            Xl[k] = l1;
-            Mh[k] = h2;
-            Ml[k] = l2;
-        }
-        f32x16 zero = {};
-        f32x16 V = mma(Csc, Xh, zero);
-        V = mma(Csc, Xl, V);
-        f32x16 U = mma(Bop, Mh, zero);
-        U = mma(Bop, Ml, U);
-        f32x16 P1 = zero, P2 = zero;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            P1 = mma(GTA[kb], GpH[kb], P1);
-            P1 = mma(GTA[kb], GpL[kb], P1);
-            P2 = mma(GA[kb], WB[kb], P2);
-        }
-
-        // per-token factors, recomputed from the inputs
-        bf16x8 GVb[2], X4b[2];
-        float dwv[16], dhv[16], dpre[16], dsp[16];
-        float dDp = 0.f;
-        float dwa0 = 0.f, dwa1 = 0.f, dwa2 = 0.f, dwa3 = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t g0 = n0 + 8 * q + 4 * hh;
-            float uw[7];
-            if (BLOCK) {
-#pragma unroll
-                for (int k = 0; k < 7; ++k) uw[k] = u_at(g0 - 3 + k);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 4 * q + r;
-                const int64_t n = g0 + r;
-                float fa = 1.f, sa = 0.f, ib = 0.f, ibm = 0.f, h = 0.f, gv = 0.f, dyv = 0.f;
-                float zs = 0.f, zd = 0.f, pre_d = 0.f, pre = 0.f;
-                if (valid && n < L) {
-                    const int64_t t = (tokbase + n) * Di + c;
-                    sigm2(to_f(a[t]), fa, sa);
-                    sigm2(to_f(bg[t]), ib, ibm);
-                    gv = to_f(dy[t]);
-                    if (BLOCK) {
-                        pre = cw0 * uw[r] + cw1 * uw[r + 1] + cw2 * uw[r + 2] + cw3 * uw[r + 3];
-                        float sp, sm;
-                        sigm2(pre, sp, sm);
-                        h = pre * sp;
-                        pre_d = sp * fmaf(pre, sm, 1.f);  // SiLU'(pre)
-                        const float zv = to_f(z[t]);
-                        float zp, zm;
-                        sigm2(zv, zp, zm);
-                        zs = zv * zp;
-                        zd = zp * fmaf(zv, zm, 1.f);  // SiLU'(z)
-                        dyv = gv;
-                        gv *= zs;
-                    } else {
-                        h = to_f(hu[t]);
-                    }
-                }
-                const float P = Pv[i];
-                const float invP = rcp(P);
-                const float wp = ib * h * invP;
-                const float gp = gv * P;
-                const float dg = sDiag[tw][tok(i)];
-                const float dw = invP * (P1[i] + U[i]);
-                const float rr = gp * (P2[i] - dg * wp);
-                const float cc = wp * (P1[i] - dg * gp);
-                X4b[i >> 3][i & 7] = (__bf16)(cc - rr + wp * U[i]);
-                GVb[i >> 3][i & 7] = (__bf16)(gp * V[i]);
-                dwv[i] = dw;
-                dsp[i] = sa;  // sigma(-a) kept for da
-                const float dbv = dw * h * ib * ibm;
-                const float dh = fmaf(dw, ib, Dc * gv);
-                dDp = fmaf(gv, h, dDp);
-                if (valid && n < L) {
-                    const int64_t t = (tokbase + n) * Di + c;
-                    db[t] = from_f<bf16>(dbv);
-                    if (BLOCK) {
-                        const float ys = fmaf(P, P2[i] + V[i], Dc * h);
-                        dz[t] = from_f<bf16>(dyv * ys * zd);
-                    } else {
-                        dhu[t] = from_f<bf16>(dh);
-                    }
-                }
-                dhv[i] = dh;
-                dpre[i] = BLOCK ? dh * pre_d : 0.f;
-                if (BLOCK) {
-                    dwa0 = fmaf(dpre[i], uw[r], dwa0);
-                    dwa1 = fmaf(dpre[i], uw[r + 1], dwa1);
-                    dwa2 = fmaf(dpre[i], uw[r + 2], dwa2);
-                    dwa3 = fmaf(dpre[i], uw[r + 3], dwa3);
-                }
-            }
-        }
-        (void)dwv;
-        (void)dhv;
-        // da = sigma(-a) (T1 + T24 + T3)
+        // ------------------------------------------------------- phase A
+        // gates and readout gradients; the wave's reverse carry (P_last, R)
+        float invP[16], g[16];
+        bf16x8 GpH[2], GpL[2];
+        bool ok = true;
         {
-            f32x16 T = zero;
-            bf16x8 ONEU[2], ONEL[2];
+            float invf[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                ONEU[i >> 3][i & 7] = (__bf16)(tok(i) >= col ? 1.f : 0.f);
-                ONEL[i >> 3][i & 7] = (__bf16)(tok(i) < col ? 1.f : 0.f);
+                const float av = LD(a, i);
+                float dv = LD(dy, i);
+                const float e = tval(i) ? ex2(-av * kLog2e) : 0.f;
+                invf[i] = 1.f + e;
+                sSA[tw][i][lane] = e * rcp(invf[i]);  // sigma(-a)
+                if (BLOCK) {
+                    const float zv = LD(z, i);
+                    const float ez = ex2(-zv * kLog2e);
+                    const float sz = rcp(1.f + ez);
+                    const float szm = ez < __builtin_huge_valf() ? ez * sz : 1.f;  // sigma(-z)
+                    sGZ[tw][i][lane] = dv * sz * fmaf(zv, szm, 1.f);  // dy SiLU'(z)
+                    dv *= zv * sz;                                     // dy SiLU(z)
+                }
+                g[i] = dv;
             }
+            float tot[4], cum[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float run = 1.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    run *= invf[4 * q + r];
+                    cum[4 * q + r] = run;
+                }
+                tot[q] = run;
+            }
+            float E[4], acc = 1.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float pt = xhalf(tot[q], upper);  // partner group (q, 1-h)
+                // token order of the groups: (0,0) (0,1) (1,0) (1,1) ...
+                E[q] = upper ? acc * pt : acc;
+                acc *= tot[q] * pt;
+            }
+            ok = acc <= 18446744073709551616.f;  // 2^64; false for NaN
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                invP[i] = E[i >> 2] * cum[i];
+                const float P = rcp(invP[i]);
+                const float gp = g[i] * P;
+                ok = ok && (__builtin_fabsf(gp) < 1e30f);
+                __bf16 hi, lo;
+                split2(gp, hi, lo);
+                GpH[i >> 3][i & 7] = hi;
+                GpL[i >> 3][i & 7] = lo;
+            }
+        }
+        {
+            f32x16 r = {};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                T = mma(ONEU[kb], GVb[kb], T);
-                T = mma(ONEL[kb], X4b[kb], T);
+                r = mma(Csv[kb], GpH[kb], r);  // rows: state, columns: channel
+                r = mma(Csv[kb], GpL[kb], r);
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (valid && tval(i)) {
-                    const int64_t t = (tokbase + n0 + tok(i)) * Di + c;
-                    da[t] = from_f<bf16>(dsp[i] * (T[i] + T3));
+            for (int i = 0; i < 8; ++i) sR[tw][tok(i)][col] = r[i];
+            if (upper) sQ[tw][col] = rcp(invP[15]);  // P at the wave's last token
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sGT[tw][tok(i)][col] = bits_of(GpH[i >> 3], i & 7);
+        }
+        __syncthreads();
+
+        // ------------------------- reverse look-back (wave 0, 32 channels)
+        // lane (col, h) carries states 8h..8h+7 of channel col
+        if (tw == 0) {
+            float Qt = 1.f, Rt[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) Rt[k] = 0.f;
+            for (int w = kTW - 1; w >= 0; --w) {
+                const float qw = sQ[w][col];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) Rt[k] = fmaf(qw, Rt[k], sR[w][8 * hh + k][col]);
+                Qt *= qw;
+            }
+            const size_t me = ((size_t)bi * n_tiles + tile) * n_chunks + chunk;
+            float mu[8];
+            if (chunk == n_chunks - 1) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    mu[k] = (dx_final && valid) ? dx_final[(bi * Di + c) * N + 8 * hh + k] : 0.f;
+            } else {
+                float *ag = agg + me * (17 * 32);
+                if (!upper) st_agent(ag + col, Qt);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) st_agent(ag + (1 + 8 * hh + k) * 32 + col, Rt[k]);
+                wait_mem();
+                if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagAgg));
+                float accQ = 1.f, accR[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) accR[k] = 0.f;
+                size_t j = me + 1;
+                for (;;) {
+                    const uint32_t stt = wait_flag(&flags[j], ep, hdr);
+                    if (stt == kFlagIncl) {
+                        const float *in = incl + j * (16 * 32);
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)
+                            mu[k] = fmaf(accQ, ld_agent(in + (8 * hh + k) * 32 + col), accR[k]);
+                        break;
+                    }
+                    const float *pa = agg + j * (17 * 32);
+                    const float qj = ld_agent(pa + col);
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        accR[k] = fmaf(accQ, ld_agent(pa + (1 + 8 * hh + k) * 32 + col), accR[k]);
+                    accQ *= qj;
+                    ++j;
                 }
+            }
+            float *ic = incl + me * (16 * 32);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float mo = fmaf(Qt, mu[k], Rt[k]);
+                st_agent(ic + (8 * hh + k) * 32 + col, mo);
+                if (chunk == 0 && dx0 && valid) dx0[(bi * Di + c) * N + 8 * hh + k] = mo;
+            }
+            wait_mem();
+            if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagIncl));
+#pragma unroll
+            for (int k = 0; k < 8; ++k) sMu[8 * hh + k][col] = mu[k];
+        }
+        __syncthreads();
+
+        // ------------------------------------------------------- phase B
+        // this wave's entering adjoint (the later waves pass it first), Mu,
+        // x_in and Phi_0 = mu_out . x_in
+        // mu_in of this wave: the workgroup's entering adjoint passed through the
+        // later waves (states 8h..8h+7 of channel col)
+        auto entering = [&](float (&mu)[8]) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) mu[k] = sMu[8 * hh + k][col];
+            for (int w = kTW - 1; w > tw; --w) {
+                const float qw = sQ[w][col];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) mu[k] = fmaf(qw, mu[k], sR[w][8 * hh + k][col]);
+            }
+        };
+        float xin[8], Mu[8];
+        float phi0;
+        {
+            float mu[8];
+            entering(mu);
+            const float pl = sQ[tw][col];
+            const float *ck = ckpt + (((int64_t)bi * n_waves + wrow) * N + 8 * hh) * Di + c;
+            float t = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                xin[k] = (active && valid) ? ck[(int64_t)k * Di] : 0.f;
+                Mu[k] = pl * mu[k];
+                t = fmaf(Mu[k] + sR[tw][8 * hh + k][col], xin[k], t);
+                sXT[tw][8 * hh + k][col] = from_f<bf16>(xin[k]);
+                sMT[tw][8 * hh + k][col] = from_f<bf16>(Mu[k]);
+            }
+            phi0 = t + xhalf(t, upper);
+        }
+
+        // inputs of w = sigma(b) h
+        float cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f, Dc = 0.f;
+        if (valid) {
+            Dc = D[c];
+            if (BLOCK) {
+                cw0 = conv_w[c * 4 + 0];
+                cw1 = conv_w[c * 4 + 1];
+                cw2 = conv_w[c * 4 + 2];
+                cw3 = conv_w[c * 4 + 3];
             }
         }
-        // block: conv transpose du_m = sum_k w_k dpre_{m+3-k} (next group's
-        // first three dpre come from the partner half; wave edges via the workspace)
-        if (BLOCK) {
-            float nx[4][3];
+        // u window of the lane's tokens as bf16 pairs (exact): w[0..15] its own
+        // tokens, w[16..27] the partner half's tokens r = 1..3 of each group,
+        // w[28..30] the three tokens before the wave
+        uint32_t wk[16];
+        auto wget = [&](int j) -> float {
+            const uint32_t v = wk[j >> 1];
+            return __uint_as_float((j & 1) ? (v & 0xFFFF0000u) : (v << 16));
+        };
+        // window u_{n-3..n} of slot 4q+r: entries k = 0..6 are tokens n-r-3 .. n-r+3
+        auto win = [&](int q, int k) -> float {
+            if (k >= 3) return wget(4 * q + (k - 3));
+            if (upper) return wget(16 + 3 * q + k);
+            return q == 0 ? wget(28 + k) : wget(16 + 3 * (q - 1) + k);
+        };
+        // fills wk (block only); loaded again after the matrix products rather
+        // than kept live across them
+        auto fill_window = [&]() {
+            uint32_t vo[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                for (int k = 0; k < 3; ++k) {
-                    const float mine = dpre[4 * q + k];
-                    const float nxt = (q < 3) ? dpre[4 * (q + 1) + k] : 0.f;
-                    const float send = hh ? mine : nxt;
-                    nx[q][k] = __shfl_xor(send, 32);
-                }
+            for (int r = 0; r < 4; ++r) {
+                vo[r] = vr[r];
+                asm volatile("" : "+v"(vo[r]));
             }
-            float *eg = edge + (((int64_t)bi * n_waves + wrow) * 6) * Di + c;
+            float uv[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) uv[i] = ldb(grs(hu, i >> 2), vo[i & 3]);
+            {
+                // u at the three tokens before the wave: the previous rows of u,
+                // or the carried conv state before the sequence start
+                const bool first = n0 == 0;
+                const bf16 *pbase = first ? conv_state : hu;
+                const int64_t poff = first ? (int64_t)bi * 3 * Di : (tokbase + n0 - 3) * Di;
+                const uint32_t pbytes =
+                    ((first && !conv_state) || !active) ? 0u : 3u * (uint32_t)Di * 2;
+                const rsrc_t rp = make_rsrc(pbytes ? (const void *)(pbase + poff + tile * 32)
+                                                   : (const void *)a,
+                                            pbytes);
+                const uint32_t po = valid ? (uint32_t)col * 2 : kOOB;
+                float ext[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int r = 1; r < 4; ++r) ext[3 * q + r - 1] = xhalf(uv[4 * q + r], upper);
+#pragma unroll
+                for (int k = 0; k < 3; ++k) ext[12 + k] = ldb(rp, po + (uint32_t)(k * Di) * 2);
+                ext[15] = 0.f;
+                auto pack = [](float lo, float hi) -> uint32_t {
+                    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+                };
+#pragma unroll
+                for (int k = 0; k < 8; ++k) wk[k] = pack(uv[2 * k], uv[2 * k + 1]);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) wk[8 + k] = pack(ext[2 * k], ext[2 * k + 1]);
+            }
+        };
+        float h[16], hd[16], ib[16];
+        bf16x8 WB[2];
+        {
+            float uv[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (!BLOCK) uv[i] = LD(hu, i);
+                const float bv = LD(bg, i);
+                ib[i] = rcp(1.f + ex2(-bv * kLog2e));
+            }
+            if (BLOCK) fill_window();
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float d0 = dpre[4 * q], d1 = dpre[4 * q + 1], d2 = dpre[4 * q + 2],
-                            d3 = dpre[4 * q + 3];
-                const float e0 = nx[q][0], e1 = nx[q][1], e2 = nx[q][2];
-                const bool last = (q == 3 && hh == 1);  // next group is in the next wave
-                const float du0 = cw3 * d0 + cw2 * d1 + cw1 * d2 + cw0 * d3;
-                const float du1 = cw3 * d1 + cw2 * d2 + cw1 * d3 + (last ? 0.f : cw0 * e0);
-                const float du2 = cw3 * d2 + cw2 * d3 + (last ? 0.f : cw1 * e0 + cw0 * e1);
-                const float du3 = cw3 * d3 + (last ? 0.f : cw2 * e0 + cw1 * e1 + cw0 * e2);
-                const float dus[4] = {du0, du1, du2, du3};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 4 * q + r;
-                    if (valid && tval(i)) {
-                        const int64_t t = (tokbase + n0 + tok(i)) * Di + c;
-                        if (last && r >= 1)
-                            eg[(3 + (r - 1)) * Di] = dus[r];
-                        else
-                            dhu[t] = from_f<bf16>(dus[r]);
+                    float hv;
+                    if (BLOCK) {
+                        const float pre = cw0 * win(q, r) + cw1 * win(q, r + 1) +
+                                          cw2 * win(q, r + 2) + cw3 * win(q, r + 3);
+                        const float ep_ = ex2(-pre * kLog2e);
+                        const float sp = rcp(1.f + ep_);
+                        const float sm = ep_ < __builtin_huge_valf() ? ep_ * sp : 1.f;
+                        hv = pre * sp;
+                        hd[i] = sp * fmaf(pre, sm, 1.f);  // SiLU'(pre)
+                    } else {
+                        hv = uv[i];
+                        hd[i] = 0.f;
                     }
+                    h[i] = hv;
+                    const float wp = ib[i] * hv * invP[i];
+                    ok = ok && (__builtin_fabsf(wp) < 1e30f);
+                    WB[i >> 3][i & 7] = (__bf16)wp;
                 }
             }
-            if (hh == 0 && valid) {
 #pragma unroll
-                for (int k = 0; k < 3; ++k) eg[k * Di] = (n0 + k < L) ? dpre[k] : 0.f;
-            }
+            for (int i = 0; i < 16; ++i) sWT[tw][tok(i)][col] = bits_of(WB[i >> 3], i & 7);
         }
-        // token sums of this wave (dD, dconv_w)
-        {
-            dDp += __shfl_xor(dDp, 32);
-            if (hh == 0 && valid) dd_part[((int64_t)bi * n_waves + wrow) * Di + c] = dDp;
-            if (BLOCK) {
-                dwa0 += __shfl_xor(dwa0, 32);
-                dwa1 += __shfl_xor(dwa1, 32);
-                dwa2 += __shfl_xor(dwa2, 32);
-                dwa3 += __shfl_xor(dwa3, 32);
-                if (hh == 0 && valid) {
-                    float *pw = dw_part + (((int64_t)bi * n_waves + wrow) * Di + c) * 4;
-                    pw[0] = dwa0;
-                    pw[1] = dwa1;
-                    pw[2] = dwa2;
-                    pw[3] = dwa3;
+        const bool wave_ok = __all(ok);
+
+        if (!wave_ok) {
+            // leave this (wave, tile) to the fix-up kernel: it needs the entering adjoint
+            if (active && valid) {
+                float mu[8];
+                entering(mu);
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    fix_mu[(((int64_t)bi * n_waves + wrow) * N + 8 * hh + k) * Di + c] = mu[k];
+            }
+            if (lane == 0 && active) {
+                const uint32_t key = (uint32_t)(((int64_t)bi * n_super + sup) * n_waves + wrow);
+                const uint32_t old = __hip_atomic_fetch_or(&fix_mask[key], 1u << st,
+                                                           __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+                if (old == 0) {
+                    const uint32_t idx = add_agent(&hdr->pad[0], 1u);
+                    fix_list[idx] = key;
                 }
             }
-        }
-        // channel contractions: H = Gp W'^T, dC = (Gp X_in + tril(H) B)/sqrt N,
-        // dB = tril(H)^T C / sqrt N + W' Mu
-        {
-            bf16x8 GpT[2], WpT[2], XK[2][2], MK[2][2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                GpT[kb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&sGpT[wv][col][16 * kb + 8 * hh]);
-                WpT[kb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&sWpT[wv][col][16 * kb + 8 * hh]);
+        } else if (active) {
+            const f32x16 zero = {};
+            f32x16 Z, PU;  // PU = G^T_{m>=n} Gp + B.Mu, so dw = PU / P
+            {
+                bf16x8 XH, XL, MH, ML;
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     __bf16 h1, l1, h2, l2;
-                    const int chn = 16 * kb + 8 * hh + k;
-                    split2(col < N ? sXin[wv][chn][col] : 0.f, h1, l1);
-                    split2(col < N ? sMuw[wv][chn][col] : 0.f, h2, l2);
-                    XK[kb][0][k] = h1;
-                    XK[kb][1][k] = l1;
-                    MK[kb][0][k] = h2;
-                    MK[kb][1][k] = l2;
+                    split2(xin[k], h1, l1);
+                    split2(Mu[k], h2, l2);
+                    XH[k] = h1;
+                    XL[k] = l1;
+                    MH[k] = h2;
+                    ML[k] = l2;
+                }
+                // tril(G) and its transpose as A operands (C pre-scaled, so G = Csc.B)
+                bf16x8 GA[2], GTA[2];
+                {
+                    const f32x16 g1 = mma(Bop, Csc, zero);  // g1[i] = G[col][tok(i)]
+                    const f32x16 g2 = mma(Csc, Bop, zero);  // g2[i] = G[tok(i)][col]
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        GA[i >> 3][i & 7] = (__bf16)((tok(i) <= col) ? g1[i] : 0.f);
+                        GTA[i >> 3][i & 7] = (__bf16)((tok(i) >= col) ? g2[i] : 0.f);
+                    }
+                }
+                PU = mma(Bop, MH, zero);
+                PU = mma(Bop, ML, PU);
+                Z = mma(Csc, XH, zero);
+                Z = mma(Csc, XL, Z);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    Z = mma(GA[kb], WB[kb], Z);
+                    PU = mma(GTA[kb], GpH[kb], PU);
+                    PU = mma(GTA[kb], GpL[kb], PU);
                 }
             }
-            f32x16 HA = zero, HTA = zero;
+
+            // per 4-token group q: outputs, the exclusive prefix for da, the conv
+            // transpose (the upper half finishes its previous group once the
+            // partner's first three dpre of this group arrive) and dconv_w partials
+            if (BLOCK) fill_window();  // the u window again, for dconv_w
+            float dDp = 0.f, dwa0 = 0.f, dwa1 = 0.f, dwa2 = 0.f, dwa3 = 0.f;
+            float base = 0.f;              // prefix of ph over the groups before
+            float dprev[4] = {0.f, 0.f, 0.f, 0.f};  // upper half: previous group's dpre
+            float *eg = edge + (((int64_t)bi * n_waves + wrow) * 6) * Di + c;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                HA = mma(WpT[kb], GpT[kb], HA);   // lane m=col: H[col][tok(i)]
-                HTA = mma(GpT[kb], WpT[kb], HTA); // lane k=col: H[tok(i)][col]
+            for (int q = 0; q < 4; ++q) {
+                float ph[4], dp[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * q + r;
+                    const float dw = invP[i] * PU[i];
+                    const float ysd = rcp(invP[i]) * Z[i];
+                    ph[r] = fmaf(g[i], ysd, -ib[i] * h[i] * dw);
+                    ST(db, i, dw * h[i] * ib[i] * (1.f - ib[i]));
+                    const float dh = fmaf(dw, ib[i], Dc * g[i]);
+                    dDp = fmaf(g[i], h[i], dDp);
+                    if (BLOCK) {
+                        ST(dz, i, sGZ[tw][i][lane] * fmaf(Dc, h[i], ysd));
+                        dp[r] = dh * hd[i];
+                    } else {
+                        ST(dhu, i, dh);
+                    }
+                }
+                {
+                    const float sq = (ph[0] + ph[1]) + (ph[2] + ph[3]);
+                    const float ps = xhalf(sq, upper);
+                    float run = upper ? base + ps : base;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 4 * q + r;
+                        ST(da, i, sSA[tw][i][lane] * (phi0 - run));
+                        run += ph[r];
+                    }
+                    base += sq + ps;
+                }
+                if (BLOCK) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        dwa0 = fmaf(dp[r], win(q, r), dwa0);
+                        dwa1 = fmaf(dp[r], win(q, r + 1), dwa1);
+                        dwa2 = fmaf(dp[r], win(q, r + 2), dwa2);
+                        dwa3 = fmaf(dp[r], win(q, r + 3), dwa3);
+                    }
+                    // du_m = sum_k w_k dpre_{m+3-k}.  Lower half: group q followed by the
+                    // partner's group q.  Upper half: group q-1 followed by the partner's
+                    // group q (its first three dpre are what arrives here).
+                    float e[3];
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) e[k] = xhalf(dp[k], upper);
+                    const float *d = upper ? dprev : dp;
+                    const float du[4] = {cw3 * d[0] + cw2 * d[1] + cw1 * d[2] + cw0 * d[3],
+                                         cw3 * d[1] + cw2 * d[2] + cw1 * d[3] + cw0 * e[0],
+                                         cw3 * d[2] + cw2 * d[3] + cw1 * e[0] + cw0 * e[1],
+                                         cw3 * d[3] + cw2 * e[0] + cw1 * e[1] + cw0 * e[2]};
+                    const int qo = upper ? q - 1 : q;  // the group finished here
+                    if (qo >= 0) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) ST(dhu, 4 * qo + r, du[r]);
+                    }
+                    if (q == 0 && !upper && valid) {
+                        // the wave's first three dpre, for the previous wave's last tokens
+#pragma unroll
+                        for (int k = 0; k < 3; ++k) eg[k * Di] = (k < Lw) ? dp[k] : 0.f;
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dprev[r] = dp[r];
+                }
             }
-            bf16x8 HAb[2], HTAb[2];
+            if (BLOCK && upper) {
+                // the upper half's last group: token 28 is complete, tokens 29..31 wait
+                // for the next wave's first dpre (finished from the workspace)
+                const float *d = dprev;
+                const float du[4] = {cw3 * d[0] + cw2 * d[1] + cw1 * d[2] + cw0 * d[3],
+                                     cw3 * d[1] + cw2 * d[2] + cw1 * d[3],
+                                     cw3 * d[2] + cw2 * d[3],
+                                     cw3 * d[3]};
+                ST(dhu, 12, du[0]);
+                if (valid) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                HAb[i >> 3][i & 7] = (__bf16)(tok(i) <= col ? HA[i] : 0.f);
-                HTAb[i >> 3][i & 7] = (__bf16)(tok(i) >= col ? HTA[i] : 0.f);
+                    for (int r = 1; r < 4; ++r)
+                        if (tval(12 + r)) eg[(3 + (r - 1)) * Di] = du[r];
+                }
             }
-            f32x16 c1 = zero, c2 = zero, b1 = zero, b2 = zero;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                c1 = mma(GpT[kb], XK[kb][0], c1);
-                c1 = mma(GpT[kb], XK[kb][1], c1);
-                c2 = mma(HAb[kb], Bsv[kb], c2);
-                b1 = mma(HTAb[kb], Csv[kb], b1);
-                b2 = mma(WpT[kb], MK[kb][0], b2);
-                b2 = mma(WpT[kb], MK[kb][1], b2);
+            // token sums of this wave (dD, dconv_w)
+            dDp += xhalf(dDp, upper);
+            if (BLOCK) {
+                dwa0 += xhalf(dwa0, upper);
+                dwa1 += xhalf(dwa1, upper);
+                dwa2 += xhalf(dwa2, upper);
+                dwa3 += xhalf(dwa3, upper);
             }
+            if (!upper && valid) {
+                dd_part[((int64_t)bi * n_waves + wrow) * Di + c] = dDp;
+                if (BLOCK)
+                    *(float4 *)(dw_part + (((int64_t)bi * n_waves + wrow) * Di + c) * 4) =
+                        make_float4(dwa0, dwa1, dwa2, dwa3);
+            }
+
+            // channel contractions: H = Gp W'^T; columns 0..15 of dBC gather
+            // tril(H)^T C + W' Mu (C pre-scaled), columns 16..31 Gp X_in + tril(H) B
+            __builtin_amdgcn_wave_barrier();
+            {
+                bf16x8 GpT[2], WpT[2], XM[2];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                dCr[i] = scale * (c1[i] + c2[i]);
-                dBr[i] = b1[i] + b2[i];
+                for (int kb = 0; kb < 2; ++kb) {
+                    GpT[kb] = __builtin_bit_cast(bf16x8,
+                                                 *(const uint4 *)&sGT[tw][col][16 * kb + 8 * hh]);
+                    WpT[kb] = __builtin_bit_cast(bf16x8,
+                                                 *(const uint4 *)&sWT[tw][col][16 * kb + 8 * hh]);
+                    // state col & 15 over channels: Mu for dB (columns < 16), x_in for dC
+                    const uint4 mq = *(const uint4 *)&sMT[tw][col & 15][16 * kb + 8 * hh];
+                    const uint4 xq = *(const uint4 *)&sXT[tw][col & 15][16 * kb + 8 * hh];
+                    XM[kb] = __builtin_bit_cast(bf16x8, col < N ? mq : xq);
+                }
+                f32x16 HA = zero, HTA = zero;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    HA = mma(WpT[kb], GpT[kb], HA);    // HA[i]  = H[col][tok(i)]
+                    HTA = mma(GpT[kb], WpT[kb], HTA);  // HTA[i] = H[tok(i)][col]
+                }
+                bf16x8 HAb[2], HTAb[2];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    HAb[i >> 3][i & 7] = (__bf16)(tok(i) <= col ? HA[i] : 0.f);
+                    HTAb[i >> 3][i & 7] = (__bf16)(tok(i) >= col ? HTA[i] : 0.f);
+                }
+                // the A operand of the Mu / x_in term: W' for dB, Gp for dC -- one
+                // product per column half, selected by zeroing the other half of XM
+                bf16x8 XMb[2], XMc[2];
+                const uint4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    XMb[kb] = col < N ? XM[kb] : __builtin_bit_cast(bf16x8, z4);
+                    XMc[kb] = col < N ? __builtin_bit_cast(bf16x8, z4) : XM[kb];
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    dBC = mma(HTAb[kb], Csv[kb], dBC);  // columns 0..15
+                    dBC = mma(WpT[kb], XMb[kb], dBC);   // columns 0..15
+                    dBC = mma(HAb[kb], Bsv[kb], dBC);   // columns 16..31
+                    dBC = mma(GpT[kb], XMc[kb], dBC);   // columns 16..31
+                }
             }
         }
+        __syncthreads();  // sQ, sR, sMu are rewritten by the next tile
     }
 
-    // ---------------- combine the two channel groups, write per-tile partials
-    if (grp == 1 && col < N) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            sDBC[tw][tok(i)][col] = dBr[i];
-            sDBC[tw][tok(i)][16 + col] = dCr[i];
-        }
-    }
-    __syncthreads();
-    if (grp == 0 && col < N && active) {
+    // ------------------------- dB/dC partial of this super-tile, per token
+    if (active) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             if (tval(i)) {
-                float *pp = bc_part + ((tokbase + n0 + tok(i)) * n_tiles + tile) * (2 * N);
-                pp[col] = dBr[i] + sDBC[tw][tok(i)][col];
-                pp[N + col] = dCr[i] + sDBC[tw][tok(i)][16 + col];
+                float *pp = bc_part + ((tokbase + n0 + tok(i)) * n_super + sup) * (2 * N);
+                pp[col] = col < N ? dBC[i] : dBC[i] * scale;
             }
         }
     }
@@ -650,14 +713,15 @@ __global__ __launch_bounds__(512, 1) void bwd_mfma_kernel(
 
 // ---------------------------------------------------------------- fix-up
 // Recomputes, with the plain reverse recurrence, the gradients of the waves the
-// matrix-core kernel listed.  One 64-lane workgroup per list entry (a 32-token
-// chunk of one 64-channel tile); lanes are channels, 16 fp32 states each; the
-// chunk's states are kept in LDS.  Channel groups that were not listed only
-// contribute zeros (their results are already written).
+// matrix-core kernel listed.  A list entry is one 32-token chunk of one
+// super-tile; a 64-lane workgroup walks its listed 32-channel tiles two at a
+// time (lane = channel, 16 fp32 states each, the chunk's states kept in LDS).
+// Tiles that were not listed only contribute zeros (their results are already
+// written).
 template <bool BLOCK>
 __global__ __launch_bounds__(64) void bwd_fix_kernel(
-    const int64_t Bt, const int64_t L, const int64_t Di, const int n_tiles,
-    const int64_t n_waves, const float scale, const bf16 *__restrict__ hu,
+    const int64_t Bt, const int64_t L, const int64_t Di, const int n_tiles, const int n_sub,
+    const int n_super, const int64_t n_waves, const float scale, const bf16 *__restrict__ hu,
     const bf16 *__restrict__ a, const bf16 *__restrict__ bg, const bf16 *__restrict__ Bm,
     const bf16 *__restrict__ Cm, const float *__restrict__ D, const bf16 *__restrict__ z,
     const float *__restrict__ conv_w, const bf16 *__restrict__ conv_state,
@@ -673,176 +737,175 @@ __global__ __launch_bounds__(64) void bwd_fix_kernel(
     const uint32_t cnt = ld_agent(&hdr->pad[0]);
     for (uint32_t e = blockIdx.x; e < cnt; e += gridDim.x) {
         const uint32_t key = fix_list[e];
-        const uint32_t gmask = fix_mask[key];
+        const uint32_t tmask = fix_mask[key];
         const int64_t wrow = key % n_waves;
-        const int64_t bt = key / n_waves;
-        const int tile = (int)(bt % n_tiles);
-        const int bi = (int)(bt / n_tiles);
-        const int64_t c = (int64_t)tile * 64 + lane;
-        const bool mine = ((gmask >> (lane >> 5)) & 1u) != 0;
-        const bool valid = c < Di && mine;
+        const int64_t bs = key / n_waves;
+        const int sup = (int)(bs % n_super);
+        const int bi = (int)(bs / n_super);
         const int64_t n0 = wrow * T;
         const int64_t tokbase = (int64_t)bi * L;
-        const float Dc = valid ? D[c] : 0.f;
-        float cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f;
-        if (BLOCK && valid) {
-            cw0 = conv_w[c * 4 + 0];
-            cw1 = conv_w[c * 4 + 1];
-            cw2 = conv_w[c * 4 + 2];
-            cw3 = conv_w[c * 4 + 3];
-        }
-        auto u_at = [&](int64_t m) -> float {
-            if (!valid || m >= L) return 0.f;
-            if (m >= 0) return to_f(hu[(tokbase + m) * Di + c]);
-            if (m >= -3 && conv_state) return to_f(conv_state[((int64_t)bi * 3 + (m + 3)) * Di + c]);
-            return 0.f;
-        };
-        // per-token values (recomputed as needed)
-        auto gate = [&](int64_t n, float &f, float &fm, float &ib, float &ibm, float &h,
-                        float &gs, float &dyv, float &zd, float &pre_d, float &zs) {
-            f = 1.f; fm = 0.f; ib = 0.f; ibm = 0.f; h = 0.f; gs = 0.f; dyv = 0.f; zd = 0.f;
-            pre_d = 0.f; zs = 0.f;
-            if (!valid || n >= L) return;
-            const int64_t t = (tokbase + n) * Di + c;
-            sigm2(to_f(a[t]), f, fm);
-            sigm2(to_f(bg[t]), ib, ibm);
-            gs = to_f(dy[t]);
-            if (BLOCK) {
-                const float pre = cw0 * u_at(n - 3) + cw1 * u_at(n - 2) + cw2 * u_at(n - 1) +
-                                  cw3 * u_at(n);
-                float sp, sm;
-                sigm2(pre, sp, sm);
-                h = pre * sp;
-                pre_d = sp * fmaf(pre, sm, 1.f);
-                const float zv = to_f(z[t]);
-                float zp, zm;
-                sigm2(zv, zp, zm);
-                zs = zv * zp;
-                zd = zp * fmaf(zv, zm, 1.f);
-                dyv = gs;
-                gs *= zs;
-            } else {
-                h = to_f(hu[t]);
+        for (int pr = 0; 2 * pr < n_sub; ++pr) {
+            const int st = 2 * pr + (lane >> 5);
+            const int tile = sup * n_sub + st;
+            const int64_t c = (int64_t)tile * 32 + (lane & 31);
+            const bool mine = st < n_sub && tile < n_tiles && ((tmask >> st) & 1u) != 0;
+            const bool valid = c < Di && mine;
+            const float Dc = valid ? D[c] : 0.f;
+            float cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f;
+            if (BLOCK && valid) {
+                cw0 = conv_w[c * 4 + 0];
+                cw1 = conv_w[c * 4 + 1];
+                cw2 = conv_w[c * 4 + 2];
+                cw3 = conv_w[c * 4 + 3];
             }
-        };
-        float x[16];
-        const float *ck = ckpt + ((int64_t)bi * n_waves + wrow) * N * Di + c;
-#pragma unroll
-        for (int s = 0; s < 16; ++s) x[s] = valid ? ck[(int64_t)s * Di] : 0.f;
-        float xin[16];
-#pragma unroll
-        for (int s = 0; s < 16; ++s) xin[s] = x[s];
-        for (int j = 0; j < T; ++j) {
-            const int64_t n = n0 + j;
-            float f, fm, ib, ibm, h, gs, dyv, zd, pd, zs;
-            gate(n, f, fm, ib, ibm, h, gs, dyv, zd, pd, zs);
-            if (n < L) {
-                const bf16 *Bn = Bm + (tokbase + n) * N;
-#pragma unroll
-                for (int s = 0; s < 16; ++s) x[s] = fmaf(f, x[s], ib * h * to_f(Bn[s]));
-            }
-#pragma unroll
-            for (int s = 0; s < 16; ++s) sx[j][s][lane] = x[s];
-        }
-        float mu[16];
-#pragma unroll
-        for (int s = 0; s < 16; ++s)
-            mu[s] = valid ? fix_mu[(((int64_t)bi * n_waves + wrow) * N + s) * Di + c] : 0.f;
-        float dDp = 0.f, dwa[4] = {0.f, 0.f, 0.f, 0.f};
-        float dp1 = 0.f, dp2 = 0.f, dp3 = 0.f;
-        for (int j = T - 1; j >= 0; --j) {
-            const int64_t n = n0 + j;
-            if (n >= L) continue;
-            float f, fm, ib, ibm, h, gs, dyv, zd, pd, zs;
-            gate(n, f, fm, ib, ibm, h, gs, dyv, zd, pd, zs);
-            const bf16 *Bn = Bm + (tokbase + n) * N;
-            const bf16 *Cn = Cm + (tokbase + n) * N;
-            const float gsc = gs * scale;
-            float lam[16], cb[16], cc[16], df = 0.f, dwv = 0.f, yc = 0.f;
-#pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                const float cv = to_f(Cn[s]);
-                lam[s] = fmaf(gsc, cv, mu[s]);
-                const float xp = j > 0 ? sx[j - 1][s][lane] : xin[s];
-                const float xn = sx[j][s][lane];
-                df = fmaf(lam[s], xp, df);
-                dwv = fmaf(lam[s], to_f(Bn[s]), dwv);
-                cb[s] = valid ? lam[s] * ib * h : 0.f;
-                cc[s] = valid ? gsc * xn : 0.f;
-                yc = fmaf(xn, cv, yc);
-            }
-            // dB, dC contributions of the listed channels, added to the partials
-            float vb[16], vc[16];
-#pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                vb[s] = cb[s];
-                vc[s] = cc[s];
-            }
-#pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) {
-#pragma unroll
-                for (int s = 0; s < 16; ++s) {
-                    vb[s] += __shfl_xor(vb[s], m);
-                    vc[s] += __shfl_xor(vc[s], m);
-                }
-            }
-            if (lane < 16) {
-                float *pp = bc_part + ((tokbase + n) * n_tiles + tile) * (2 * N);
-                float tb = 0.f, tc = 0.f;
-#pragma unroll
-                for (int s = 0; s < 16; ++s) {
-                    tb = (s == lane) ? vb[s] : tb;
-                    tc = (s == lane) ? vc[s] : tc;
-                }
-                pp[lane] += tb;
-                pp[N + lane] += tc;
-            }
-            const float dav = df * f * fm;
-            const float dbv = dwv * h * ib * ibm;
-            const float dh = fmaf(dwv, ib, Dc * gs);
-            dDp = fmaf(gs, h, dDp);
-            if (valid) {
+            auto u_at = [&](int64_t m) -> float {
+                if (!valid || m >= L) return 0.f;
+                if (m >= 0) return to_f(hu[(tokbase + m) * Di + c]);
+                if (m >= -3 && conv_state)
+                    return to_f(conv_state[((int64_t)bi * 3 + (m + 3)) * Di + c]);
+                return 0.f;
+            };
+            // per-token values (recomputed as needed)
+            auto gate = [&](int64_t n, float &f, float &fm, float &ib, float &ibm, float &h,
+                            float &gs, float &dyv, float &zd, float &pre_d, float &zs) {
+                f = 1.f; fm = 0.f; ib = 0.f; ibm = 0.f; h = 0.f; gs = 0.f; dyv = 0.f; zd = 0.f;
+                pre_d = 0.f; zs = 0.f;
+                if (!valid || n >= L) return;
                 const int64_t t = (tokbase + n) * Di + c;
-                da[t] = from_f<bf16>(dav);
-                db[t] = from_f<bf16>(dbv);
+                sigm2(to_f(a[t]), f, fm);
+                sigm2(to_f(bg[t]), ib, ibm);
+                gs = to_f(dy[t]);
                 if (BLOCK) {
-                    const float ys = fmaf(scale, yc, Dc * h);
-                    dz[t] = from_f<bf16>(dyv * ys * zd);
-                    const float dpre = dh * pd;
-                    const float du = cw3 * dpre + cw2 * dp1 + cw1 * dp2 + cw0 * dp3;
-                    dp3 = dp2;
-                    dp2 = dp1;
-                    dp1 = dpre;
-                    dwa[0] = fmaf(dpre, u_at(n - 3), dwa[0]);
-                    dwa[1] = fmaf(dpre, u_at(n - 2), dwa[1]);
-                    dwa[2] = fmaf(dpre, u_at(n - 1), dwa[2]);
-                    dwa[3] = fmaf(dpre, u_at(n), dwa[3]);
-                    float *eg = edge + (((int64_t)bi * n_waves + wrow) * 6) * Di + c;
-                    if (j >= T - 3)
-                        eg[(3 + (j - (T - 3))) * Di] = du;
-                    else
-                        dhu[t] = from_f<bf16>(du);
-                    if (j < 3) eg[j * Di] = dpre;
+                    const float pre = cw0 * u_at(n - 3) + cw1 * u_at(n - 2) + cw2 * u_at(n - 1) +
+                                      cw3 * u_at(n);
+                    float sp, sm;
+                    sigm2(pre, sp, sm);
+                    h = pre * sp;
+                    pre_d = sp * fmaf(pre, sm, 1.f);
+                    const float zv = to_f(z[t]);
+                    float zp, zm;
+                    sigm2(zv, zp, zm);
+                    zs = zv * zp;
+                    zd = zp * fmaf(zv, zm, 1.f);
+                    dyv = gs;
+                    gs *= zs;
                 } else {
-                    dhu[t] = from_f<bf16>(dh);
+                    h = to_f(hu[t]);
+                }
+            };
+            float x[16];
+            const float *ck = ckpt + ((int64_t)bi * n_waves + wrow) * N * Di + c;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) x[s] = valid ? ck[(int64_t)s * Di] : 0.f;
+            float xin[16];
+#pragma unroll
+            for (int s = 0; s < 16; ++s) xin[s] = x[s];
+            for (int j = 0; j < T; ++j) {
+                const int64_t n = n0 + j;
+                float f, fm, ib, ibm, h, gs, dyv, zd, pd, zs;
+                gate(n, f, fm, ib, ibm, h, gs, dyv, zd, pd, zs);
+                if (n < L) {
+                    const bf16 *Bn = Bm + (tokbase + n) * N;
+#pragma unroll
+                    for (int s = 0; s < 16; ++s) x[s] = fmaf(f, x[s], ib * h * to_f(Bn[s]));
+                }
+#pragma unroll
+                for (int s = 0; s < 16; ++s) sx[j][s][lane] = x[s];
+            }
+            float mu[16];
+#pragma unroll
+            for (int s = 0; s < 16; ++s)
+                mu[s] = valid ? fix_mu[(((int64_t)bi * n_waves + wrow) * N + s) * Di + c] : 0.f;
+            float dDp = 0.f, dwa[4] = {0.f, 0.f, 0.f, 0.f};
+            float dp1 = 0.f, dp2 = 0.f, dp3 = 0.f;
+            for (int j = T - 1; j >= 0; --j) {
+                const int64_t n = n0 + j;
+                if (n >= L) continue;
+                float f, fm, ib, ibm, h, gs, dyv, zd, pd, zs;
+                gate(n, f, fm, ib, ibm, h, gs, dyv, zd, pd, zs);
+                const bf16 *Bn = Bm + (tokbase + n) * N;
+                const bf16 *Cn = Cm + (tokbase + n) * N;
+                const float gsc = gs * scale;
+                float lam[16], cb[16], cc[16], df = 0.f, dwv = 0.f, yc = 0.f;
+#pragma unroll
+                for (int s = 0; s < 16; ++s) {
+                    const float cv = to_f(Cn[s]);
+                    lam[s] = fmaf(gsc, cv, mu[s]);
+                    const float xp = j > 0 ? sx[j - 1][s][lane] : xin[s];
+                    const float xn = sx[j][s][lane];
+                    df = fmaf(lam[s], xp, df);
+                    dwv = fmaf(lam[s], to_f(Bn[s]), dwv);
+                    cb[s] = valid ? lam[s] * ib * h : 0.f;
+                    cc[s] = valid ? gsc * xn : 0.f;
+                    yc = fmaf(xn, cv, yc);
+                }
+                // dB, dC contributions of the listed channels, added to the partials
+#pragma unroll
+                for (int m = 32; m >= 1; m >>= 1) {
+#pragma unroll
+                    for (int s = 0; s < 16; ++s) {
+                        cb[s] += __shfl_xor(cb[s], m);
+                        cc[s] += __shfl_xor(cc[s], m);
+                    }
+                }
+                if (lane < 16) {
+                    float *pp = bc_part + ((tokbase + n) * n_super + sup) * (2 * N);
+                    float tb = 0.f, tc = 0.f;
+#pragma unroll
+                    for (int s = 0; s < 16; ++s) {
+                        tb = (s == lane) ? cb[s] : tb;
+                        tc = (s == lane) ? cc[s] : tc;
+                    }
+                    pp[lane] += tb;
+                    pp[N + lane] += tc;
+                }
+                const float dav = df * f * fm;
+                const float dbv = dwv * h * ib * ibm;
+                const float dh = fmaf(dwv, ib, Dc * gs);
+                dDp = fmaf(gs, h, dDp);
+                if (valid) {
+                    const int64_t t = (tokbase + n) * Di + c;
+                    da[t] = from_f<bf16>(dav);
+                    db[t] = from_f<bf16>(dbv);
+                    if (BLOCK) {
+                        const float ys = fmaf(scale, yc, Dc * h);
+                        dz[t] = from_f<bf16>(dyv * ys * zd);
+                        const float dpre = dh * pd;
+                        const float du = cw3 * dpre + cw2 * dp1 + cw1 * dp2 + cw0 * dp3;
+                        dp3 = dp2;
+                        dp2 = dp1;
+                        dp1 = dpre;
+                        dwa[0] = fmaf(dpre, u_at(n - 3), dwa[0]);
+                        dwa[1] = fmaf(dpre, u_at(n - 2), dwa[1]);
+                        dwa[2] = fmaf(dpre, u_at(n - 1), dwa[2]);
+                        dwa[3] = fmaf(dpre, u_at(n), dwa[3]);
+                        float *eg = edge + (((int64_t)bi * n_waves + wrow) * 6) * Di + c;
+                        if (j >= T - 3)
+                            eg[(3 + (j - (T - 3))) * Di] = du;
+                        else
+                            dhu[t] = from_f<bf16>(du);
+                        if (j < 3) eg[j * Di] = dpre;
+                    } else {
+                        dhu[t] = from_f<bf16>(dh);
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < 16; ++s) mu[s] = f * lam[s];
+            }
+            if (valid) {
+                dd_part[((int64_t)bi * n_waves + wrow) * Di + c] = dDp;
+                if (BLOCK) {
+                    float *pw = dw_part + (((int64_t)bi * n_waves + wrow) * Di + c) * 4;
+                    pw[0] = dwa[0];
+                    pw[1] = dwa[1];
+                    pw[2] = dwa[2];
+                    pw[3] = dwa[3];
+                    float *eg = edge + (((int64_t)bi * n_waves + wrow) * 6) * Di + c;
+                    for (int r = (int)(L - n0); r < 3; ++r) eg[r * Di] = 0.f;
                 }
             }
-#pragma unroll
-            for (int s = 0; s < 16; ++s) mu[s] = f * lam[s];
+            __syncthreads();  // sx is rewritten by the next tile pair
         }
-        if (valid) {
-            dd_part[((int64_t)bi * n_waves + wrow) * Di + c] = dDp;
-            if (BLOCK) {
-                float *pw = dw_part + (((int64_t)bi * n_waves + wrow) * Di + c) * 4;
-                pw[0] = dwa[0];
-                pw[1] = dwa[1];
-                pw[2] = dwa[2];
-                pw[3] = dwa[3];
-                float *eg = edge + (((int64_t)bi * n_waves + wrow) * 6) * Di + c;
-                for (int r = (int)(L - n0); r < 3; ++r) eg[r * Di] = 0.f;
-            }
-        }
-        __syncthreads();
         if (lane == 0) fix_mask[key] = 0u;  // leave the workspace clean
         __syncthreads();
     }
@@ -860,15 +923,13 @@ template <bool BLOCK>
 static hipError_t launch_bwd_mfma_t(const BwdArgs &g, hipStream_t stream)
 {
     const BwdPlan pl = bwd_plan(g.Bt, g.L, g.Di, g.N, g.block);
+    const MfmaBwdShape m = mfma_bwd_shape(g.Bt, g.L, g.Di);
     char *ws = (char *)g.ws;
     WsHeader *hdr = (WsHeader *)ws;
-    const int n_tiles = (int)((g.Di + 63) / 64);
-    const int n_chunks = (int)((g.L + 127) / 128);
-    const int64_t n_wg = g.Bt * n_tiles * n_chunks;
     const int64_t n_waves = (g.L + 31) / 32;
-    uint32_t *flags = (uint32_t *)(ws + pl.off_flags);
-    float *agg = (float *)(ws + pl.off_agg);
-    float *incl = (float *)(ws + pl.off_incl);
+    uint32_t *flags = (uint32_t *)(ws + pl.off_mflags);
+    float *agg = (float *)(ws + pl.off_magg);
+    float *incl = (float *)(ws + pl.off_mincl);
     float *bc = (float *)(ws + pl.off_bc);
     float *dd = (float *)(ws + pl.off_dd);
     float *dw = (float *)(ws + pl.off_dw);
@@ -876,19 +937,19 @@ static hipError_t launch_bwd_mfma_t(const BwdArgs &g, hipStream_t stream)
     uint32_t *fmask = (uint32_t *)(ws + pl.off_fixmask);
     uint32_t *flist = (uint32_t *)(ws + pl.off_fixlist);
     float *fmu = (float *)(ws + pl.off_fixmu);
-    hipLaunchKernelGGL((bwd_mfma_kernel<BLOCK>), dim3(n_wg), dim3(512), 0, stream, g.Bt, g.L, g.Di,
-                       n_tiles, n_chunks, n_waves, g.scale, (const bf16 *)g.hu,
-                       (const bf16 *)g.a, (const bf16 *)g.b, (const bf16 *)g.B,
-                       (const bf16 *)g.C, g.D, (const bf16 *)g.z, g.conv_w,
+    hipLaunchKernelGGL((bwd_mfma_kernel<BLOCK>), dim3((unsigned)m.n_wg), dim3(64 * kTW), 0, stream,
+                       g.Bt, g.L, g.Di, m.n_tiles, m.n_sub, m.n_super, m.n_chunks, n_waves,
+                       g.scale, (const bf16 *)g.hu, (const bf16 *)g.a, (const bf16 *)g.b,
+                       (const bf16 *)g.B, (const bf16 *)g.C, g.D, (const bf16 *)g.z, g.conv_w,
                        (const bf16 *)g.conv_state, g.ckpt, (const bf16 *)g.dy, g.dx_final,
                        (bf16 *)g.dhu, (bf16 *)g.da, (bf16 *)g.db, (bf16 *)g.dz, g.dx0, hdr, flags,
                        agg, incl, bc, dd, dw, edge, fmask, flist, fmu);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_fix_kernel<BLOCK>), dim3(256), dim3(64), 0, stream, g.Bt, g.L, g.Di,
-                       n_tiles, n_waves, g.scale, (const bf16 *)g.hu, (const bf16 *)g.a,
-                       (const bf16 *)g.b, (const bf16 *)g.B, (const bf16 *)g.C, g.D,
-                       (const bf16 *)g.z, g.conv_w, (const bf16 *)g.conv_state, g.ckpt,
+                       m.n_tiles, m.n_sub, m.n_super, n_waves, g.scale, (const bf16 *)g.hu,
+                       (const bf16 *)g.a, (const bf16 *)g.b, (const bf16 *)g.B, (const bf16 *)g.C,
+                       g.D, (const bf16 *)g.z, g.conv_w, (const bf16 *)g.conv_state, g.ckpt,
                        (const bf16 *)g.dy, (bf16 *)g.dhu, (bf16 *)g.da, (bf16 *)g.db,
                        (bf16 *)g.dz, hdr, bc, dd, dw, edge, fmask, (const uint32_t *)flist,
                        (const float *)fmu);

@@ -59,11 +59,34 @@ inline size_t ckpt_bytes(int64_t Bt, int64_t L, int64_t Di, int64_t N)
     return (size_t)Bt * (size_t)((L + kFwdT - 1) / kFwdT) * (size_t)N * (size_t)Di * 4;
 }
 
+// Matrix-core backward decomposition: a workgroup owns 128 tokens (four
+// 32-token waves) of a super-tile of n_sub consecutive 32-channel tiles, which
+// it visits in turn; its reverse look-back runs per (tile, 128-token chunk).
+struct MfmaBwdShape {
+    int n_tiles;   // 32-channel tiles
+    int n_sub;     // tiles per super-tile
+    int n_super;   // super-tiles (dB/dC partials per token)
+    int n_chunks;  // 128-token chunks
+    int64_t n_wg;  // workgroups = tickets
+};
+
+inline MfmaBwdShape mfma_bwd_shape(int64_t Bt, int64_t L, int64_t Di)
+{
+    MfmaBwdShape m{};
+    m.n_tiles = (int)((Di + 31) / 32);
+    m.n_sub = m.n_tiles < 4 ? (m.n_tiles > 0 ? m.n_tiles : 1) : 4;
+    m.n_super = (m.n_tiles + m.n_sub - 1) / m.n_sub;
+    m.n_chunks = (int)((L + 127) / 128);
+    m.n_wg = Bt * m.n_super * m.n_chunks;
+    return m;
+}
+
 struct BwdPlan {
     int n_tiles, n_chunks;
     int64_t n_wg, n_waves;
     size_t off_flags, off_agg, off_incl;  // reverse look-back (same shapes as forward)
-    size_t off_bc;    // dB/dC partials   [Bt][L][n_tiles][2N] fp32
+    size_t off_mflags, off_magg, off_mincl;  // matrix-core look-back, per (tile, chunk)
+    size_t off_bc;    // dB/dC partials   [Bt][L][n_parts][2N] fp32 (tiles or super-tiles)
     size_t off_dd;    // dD partials      [Bt][n_waves][Di] fp32
     size_t off_dw;    // dconv_w partials [Bt][n_waves][Di][4] fp32
     size_t off_edge;  // block: per wave boundary  [Bt][n_waves][6][Di] fp32
@@ -72,8 +95,8 @@ struct BwdPlan {
     size_t off_ckpt;  // recomputed checkpoints when the caller passes none
     size_t off_fwd;   // workspace of the checkpoint-only forward
     // matrix-core backward: chunks its rescaled form cannot take
-    size_t off_fixmask;  // [Bt][n_tiles][n_waves] u32 channel-group bits
-    size_t off_fixlist;  // [Bt][n_tiles][n_waves] u32 keys
+    size_t off_fixmask;  // [Bt][n_super][n_waves] u32 tile bits
+    size_t off_fixlist;  // [Bt][n_super][n_waves] u32 keys
     size_t off_fixmu;    // [Bt][n_waves][N][Di] fp32 entering adjoints
     size_t bytes;
 };
@@ -91,13 +114,19 @@ inline BwdPlan bwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N, bool block
     p.off_flags = f4.off_flags;
     p.off_agg = f4.off_agg;
     p.off_incl = f4.off_incl;
-    p.off_bc = f4.bytes;
-    p.off_dd = align256(p.off_bc + (size_t)Bt * L * p.n_tiles * 2 * N * 4);
+    const MfmaBwdShape m = mfma_bwd_shape(Bt, L, Di);
+    const size_t m_ent = N == 16 ? (size_t)Bt * m.n_tiles * m.n_chunks : 0;
+    p.off_mflags = f4.bytes;
+    p.off_magg = align256(p.off_mflags + 4 * m_ent);
+    p.off_mincl = align256(p.off_magg + 17 * 32 * 4 * m_ent);
+    p.off_bc = align256(p.off_mincl + 16 * 32 * 4 * m_ent);
+    const int64_t n_parts = (N == 16 && m.n_super > p.n_tiles) ? m.n_super : p.n_tiles;
+    p.off_dd = align256(p.off_bc + (size_t)Bt * L * n_parts * 2 * N * 4);
     p.off_dw = align256(p.off_dd + (size_t)Bt * p.n_waves * Di * 4);
     p.off_edge = align256(p.off_dw + (block ? (size_t)Bt * p.n_waves * Di * 4 * 4 : 0));
     p.off_ckpt = align256(p.off_edge + (block ? (size_t)Bt * p.n_waves * 6 * Di * 4 : 0));
     p.off_fwd = align256(p.off_ckpt + ckpt_bytes(Bt, L, Di, N));
-    const size_t n_keys = (size_t)Bt * (size_t)((Di + 63) / 64) * (size_t)p.n_waves;
+    const size_t n_keys = (size_t)Bt * (size_t)m.n_super * (size_t)p.n_waves;
     p.off_fixmask = align256(p.off_fwd + fwd_ws_bytes(Bt, L, Di, N));
     p.off_fixlist = align256(p.off_fixmask + 4 * n_keys);
     p.off_fixmu = align256(p.off_fixlist + 4 * n_keys);
