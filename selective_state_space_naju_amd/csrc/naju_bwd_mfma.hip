@@ -74,13 +74,15 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
                                              0x00020000);
 }
-__device__ __forceinline__ float ldb(rsrc_t r, uint32_t off)
+// bf16 element at byte offset off + soff (soff wave-uniform; the range check
+// covers the sum)
+__device__ __forceinline__ float ldb(rsrc_t r, uint32_t off, uint32_t soff = 0)
 {
-    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0) << 16);
+    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0) << 16);
 }
-__device__ __forceinline__ void stb(rsrc_t r, uint32_t off, float v)
+__device__ __forceinline__ void stb(rsrc_t r, uint32_t off, uint32_t soff, float v)
 {
-    __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(v), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(v), r, off, soff, 0);
 }
 
 // Value held by lane l ^ 32.  v_permlane32_swap exchanges the upper half of
@@ -103,11 +105,10 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
     const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, const float *__restrict__ D,
     const bf16 *__restrict__ z, const float *__restrict__ conv_w,
     const bf16 *__restrict__ conv_state, const float *__restrict__ ckpt,
-    const bf16 *__restrict__ dy, const float *__restrict__ dx_final, bf16 *__restrict__ dhu,
-    bf16 *__restrict__ da, bf16 *__restrict__ db, bf16 *__restrict__ dz, float *dx0,
-    WsHeader *hdr, uint32_t *flags, float *agg, float *incl, float *__restrict__ bc_part,
-    float *__restrict__ dd_part, float *__restrict__ dw_part, float *__restrict__ edge,
-    uint32_t *fix_mask, uint32_t *fix_list, float *fix_mu)
+    const bf16 *__restrict__ dy, const float *__restrict__ muin, bf16 *__restrict__ dhu,
+    bf16 *__restrict__ da, bf16 *__restrict__ db, bf16 *__restrict__ dz, WsHeader *hdr,
+    float *__restrict__ bc_part, float *__restrict__ dd_part, float *__restrict__ dw_part,
+    float *__restrict__ edge, uint32_t *fix_mask, uint32_t *fix_list, float *fix_mu)
 {
     constexpr int N = 16, T = 32;
     const int lane = threadIdx.x & 63;
@@ -118,12 +119,9 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
     const int hh = lane >> 5;
     const bool upper = hh != 0;
 
-    __shared__ uint32_t s_ticket, s_epoch;
-    // reverse carries of the four waves and the adjoint entering the workgroup's
-    // last token
+    // reverse carries of the four waves
     __shared__ float sQ[kTW][32];
     __shared__ float sR[kTW][16][32];
-    __shared__ float sMu[16][32];
     // per-token factors consumed once, after the matrix products: sigma(-a) and
     // dy SiLU'(z)  [wave][slot][lane]
     __shared__ float sSA[kTW][16][64];
@@ -134,18 +132,9 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
     __shared__ __attribute__((aligned(16))) bf16 sXT[kTW][16][40];  // x_in [state][channel]
     __shared__ __attribute__((aligned(16))) bf16 sMT[kTW][16][40];  // Mu   [state][channel]
 
-    if (threadIdx.x == 0) {
-        s_ticket = add_agent(&hdr->ticket, 1u);
-        s_epoch = (ld_agent(&hdr->epoch) + 1u) & 0x3FFFFFFFu;
-    }
-    __syncthreads();
-    const uint32_t ticket = s_ticket;
-    const uint32_t ep = s_epoch;
-    const uint32_t per_chunk = (uint32_t)(Bt * n_super);
-    const int chunk = n_chunks - 1 - (int)(ticket / per_chunk);
-    const int rem = (int)(ticket % per_chunk);
-    const int bi = rem / n_super;
-    const int sup = rem % n_super;
+    const int sup = (int)(blockIdx.x % (uint32_t)n_super);
+    const int bi = (int)((blockIdx.x / (uint32_t)n_super) % (uint32_t)Bt);
+    const int chunk = (int)(blockIdx.x / (uint32_t)n_super / (uint32_t)Bt);
     const int64_t n0 = (int64_t)chunk * (kTW * T) + (int64_t)tw * T;
     const int64_t wrow = (int64_t)chunk * kTW + tw;
     const bool active = n0 < L;
@@ -196,18 +185,20 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
         const bool valid = c < Di;
         const int64_t ebase = (tokbase + (active ? n0 : 0)) * Di + (int64_t)tile * 32;
         // Element access of every [Bt][L][Di] tensor: slot i = 4q + r is token
-        // 8q + 4h + r.  One buffer per 8-token group q (built on the scalar unit,
-        // ending at the last valid token) and the lane offsets of rows 4h + r.
+        // 8q + 4h + r.  One buffer per tensor, ending at the wave's last valid
+        // token; the lane offset of row 4h + r plus the wave-uniform offset of
+        // group q's first row.
         const uint32_t row2 = (uint32_t)Di * 2;
         uint32_t vr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) vr[r] = valid ? (uint32_t)((4 * hh + r) * Di + col) * 2 : kOOB;
-        auto grs = [&](const bf16 *t, int q) -> rsrc_t {
-            const int rows = Lw - 8 * q;
-            return make_rsrc(t + ebase + (int64_t)(8 * q) * Di, rows > 0 ? (uint32_t)rows * row2 : 0u);
+        auto trs = [&](const bf16 *t) -> rsrc_t { return make_rsrc(t + ebase, (uint32_t)Lw * row2); };
+        auto LD = [&](const bf16 *t, int i) -> float {
+            return ldb(trs(t), vr[i & 3], (uint32_t)(8 * (i >> 2)) * row2);
         };
-        auto LD = [&](const bf16 *t, int i) -> float { return ldb(grs(t, i >> 2), vr[i & 3]); };
-        auto ST = [&](bf16 *t, int i, float v) { stb(grs(t, i >> 2), vr[i & 3], v); };
+        auto ST = [&](bf16 *t, int i, float v) {
+            stb(trs(t), vr[i & 3], (uint32_t)(8 * (i >> 2)) * row2, v);
+        };
 
         // ------------------------------------------------------- phase A
         // gates and readout gradients; the wave's reverse carry (P_last, R)
@@ -265,115 +256,6 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                 GpL[i >> 3][i & 7] = lo;
             }
         }
-        {
-            f32x16 r = {};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                r = mma(Csv[kb], GpH[kb], r);  // rows: state, columns: channel
-                r = mma(Csv[kb], GpL[kb], r);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sR[tw][tok(i)][col] = r[i];
-            if (upper) sQ[tw][col] = rcp(invP[15]);  // P at the wave's last token
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sGT[tw][tok(i)][col] = bits_of(GpH[i >> 3], i & 7);
-        }
-        __syncthreads();
-
-        // ------------------------- reverse look-back (wave 0, 32 channels)
-        // lane (col, h) carries states 8h..8h+7 of channel col
-        if (tw == 0) {
-            float Qt = 1.f, Rt[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) Rt[k] = 0.f;
-            for (int w = kTW - 1; w >= 0; --w) {
-                const float qw = sQ[w][col];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) Rt[k] = fmaf(qw, Rt[k], sR[w][8 * hh + k][col]);
-                Qt *= qw;
-            }
-            const size_t me = ((size_t)bi * n_tiles + tile) * n_chunks + chunk;
-            float mu[8];
-            if (chunk == n_chunks - 1) {
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    mu[k] = (dx_final && valid) ? dx_final[(bi * Di + c) * N + 8 * hh + k] : 0.f;
-            } else {
-                float *ag = agg + me * (17 * 32);
-                if (!upper) st_agent(ag + col, Qt);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) st_agent(ag + (1 + 8 * hh + k) * 32 + col, Rt[k]);
-                wait_mem();
-                if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagAgg));
-                float accQ = 1.f, accR[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) accR[k] = 0.f;
-                size_t j = me + 1;
-                for (;;) {
-                    const uint32_t stt = wait_flag(&flags[j], ep, hdr);
-                    if (stt == kFlagIncl) {
-                        const float *in = incl + j * (16 * 32);
-#pragma unroll
-                        for (int k = 0; k < 8; ++k)
-                            mu[k] = fmaf(accQ, ld_agent(in + (8 * hh + k) * 32 + col), accR[k]);
-                        break;
-                    }
-                    const float *pa = agg + j * (17 * 32);
-                    const float qj = ld_agent(pa + col);
-#pragma unroll
-                    for (int k = 0; k < 8; ++k)
-                        accR[k] = fmaf(accQ, ld_agent(pa + (1 + 8 * hh + k) * 32 + col), accR[k]);
-                    accQ *= qj;
-                    ++j;
-                }
-            }
-            float *ic = incl + me * (16 * 32);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float mo = fmaf(Qt, mu[k], Rt[k]);
-                st_agent(ic + (8 * hh + k) * 32 + col, mo);
-                if (chunk == 0 && dx0 && valid) dx0[(bi * Di + c) * N + 8 * hh + k] = mo;
-            }
-            wait_mem();
-            if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagIncl));
-#pragma unroll
-            for (int k = 0; k < 8; ++k) sMu[8 * hh + k][col] = mu[k];
-        }
-        __syncthreads();
-
-        // ------------------------------------------------------- phase B
-        // this wave's entering adjoint (the later waves pass it first), Mu,
-        // x_in and Phi_0 = mu_out . x_in
-        // mu_in of this wave: the workgroup's entering adjoint passed through the
-        // later waves (states 8h..8h+7 of channel col)
-        auto entering = [&](float (&mu)[8]) {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) mu[k] = sMu[8 * hh + k][col];
-            for (int w = kTW - 1; w > tw; --w) {
-                const float qw = sQ[w][col];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) mu[k] = fmaf(qw, mu[k], sR[w][8 * hh + k][col]);
-            }
-        };
-        float xin[8], Mu[8];
-        float phi0;
-        {
-            float mu[8];
-            entering(mu);
-            const float pl = sQ[tw][col];
-            const float *ck = ckpt + (((int64_t)bi * n_waves + wrow) * N + 8 * hh) * Di + c;
-            float t = 0.f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                xin[k] = (active && valid) ? ck[(int64_t)k * Di] : 0.f;
-                Mu[k] = pl * mu[k];
-                t = fmaf(Mu[k] + sR[tw][8 * hh + k][col], xin[k], t);
-                sXT[tw][8 * hh + k][col] = from_f<bf16>(xin[k]);
-                sMT[tw][8 * hh + k][col] = from_f<bf16>(Mu[k]);
-            }
-            phi0 = t + xhalf(t, upper);
-        }
-
         // inputs of w = sigma(b) h
         float cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f, Dc = 0.f;
         if (valid) {
@@ -410,7 +292,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
             }
             float uv[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) uv[i] = ldb(grs(hu, i >> 2), vo[i & 3]);
+            for (int i = 0; i < 16; ++i) uv[i] = ldb(trs(hu), vo[i & 3], (uint32_t)(8 * (i >> 2)) * row2);
             {
                 // u at the three tokens before the wave: the previous rows of u,
                 // or the carried conv state before the sequence start
@@ -479,6 +361,61 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
             for (int i = 0; i < 16; ++i) sWT[tw][tok(i)][col] = bits_of(WB[i >> 3], i & 7);
         }
         const bool wave_ok = __all(ok);
+        // x_in (forward checkpoint): states 8h..8h+7 of channel col
+        float xin[8];
+        {
+            const float *ck = ckpt + (((int64_t)bi * n_waves + wrow) * N + 8 * hh) * Di + c;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) xin[k] = (active && valid) ? ck[(int64_t)k * Di] : 0.f;
+        }
+        {
+            f32x16 r = {};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                r = mma(Csv[kb], GpH[kb], r);  // rows: state, columns: channel
+                r = mma(Csv[kb], GpL[kb], r);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sR[tw][tok(i)][col] = r[i];
+            if (upper) sQ[tw][col] = rcp(invP[15]);  // P at the wave's last token
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sGT[tw][tok(i)][col] = bits_of(GpH[i >> 3], i & 7);
+        }
+        __syncthreads();
+
+        const size_t me = ((size_t)bi * n_tiles + tile) * n_chunks + chunk;
+
+        // ------------------------------------------------------- phase B
+        // this wave's entering adjoint (the later waves pass it first), Mu,
+        // x_in and Phi_0 = mu_out . x_in
+        // mu_in of this wave: the workgroup's entering adjoint passed through the
+        // later waves (states 8h..8h+7 of channel col)
+        auto entering = [&](float (&mu)[8]) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) mu[k] = muin[me * (16 * 32) + (8 * hh + k) * 32 + col];
+            for (int w = kTW - 1; w > tw; --w) {
+                const float qw = sQ[w][col];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) mu[k] = fmaf(qw, mu[k], sR[w][8 * hh + k][col]);
+            }
+        };
+        float Mu[8];
+        float phi0;
+        {
+            float mu[8];
+            entering(mu);
+            const float pl = sQ[tw][col];
+            float t = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                Mu[k] = pl * mu[k];
+                t = fmaf(Mu[k] + sR[tw][8 * hh + k][col], xin[k], t);
+                sXT[tw][8 * hh + k][col] = from_f<bf16>(xin[k]);
+                sMT[tw][8 * hh + k][col] = from_f<bf16>(Mu[k]);
+            }
+            phi0 = t + xhalf(t, upper);
+        }
+
 
         if (!wave_ok) {
             // leave this (wave, tile) to the fix-up kernel: it needs the entering adjoint
@@ -699,16 +636,145 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
         }
     }
 
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t total = per_chunk * (uint32_t)n_chunks;
-        const uint32_t old = add_agent(&hdr->done, 1u);
-        if (old == total - 1) {
-            st_agent(&hdr->ticket, 0u);
-            st_agent(&hdr->done, 0u);
-            st_agent(&hdr->epoch, ep);
+}
+
+// ----------------------------------------------------- reverse carry pass
+// The adjoint crossing a chunk boundary only needs, per 128-token chunk of a
+// 32-channel tile, the chunk's reverse carry  mu_out = Q mu_in + R  with
+// Q = P_last (per channel) and R = Gp^T C / sqrt(N) (per channel and state).
+// Four waves compute their 32-token carries with the same products as the
+// gradient kernel and compose them (the adjoint passes the later waves first).
+template <bool BLOCK>
+__global__ __launch_bounds__(64 * kTW) void bwd_carry_kernel(
+    const int64_t Bt, const int64_t L, const int64_t Di, const int n_tiles, const int n_chunks,
+    const float scale, const bf16 *__restrict__ a, const bf16 *__restrict__ Cm,
+    const bf16 *__restrict__ z, const bf16 *__restrict__ dy, float *__restrict__ agg)
+{
+    constexpr int N = 16, T = 32;
+    const int lane = threadIdx.x & 63;
+    const int tw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 31;
+    const int hh = lane >> 5;
+    const bool upper = hh != 0;
+    __shared__ float sQ[kTW][32];
+    __shared__ float sR[kTW][16][32];
+
+    const int tile = (int)(blockIdx.x % (uint32_t)n_tiles);
+    const int chunk = (int)((blockIdx.x / (uint32_t)n_tiles) % (uint32_t)n_chunks);
+    const int bi = (int)(blockIdx.x / (uint32_t)n_tiles / (uint32_t)n_chunks);
+    const int64_t n0 = (int64_t)chunk * (kTW * T) + (int64_t)tw * T;
+    const bool active = n0 < L;
+    const int Lw = active ? (int)(L - n0 < T ? L - n0 : T) : 0;
+    const int64_t tokbase = (int64_t)bi * L;
+    const int64_t c = (int64_t)tile * 32 + col;
+    const bool valid = c < Di;
+    auto tok = [&](int i) -> int { return 8 * (i >> 2) + 4 * hh + (i & 3); };
+
+    bf16x8 Csv[2];
+    {
+        const rsrc_t rC = make_rsrc(Cm + (tokbase + (active ? n0 : 0)) * N, (uint32_t)Lw * N * 2);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t o = col < N ? (uint32_t)(tok(i) * N + col) * 2 : kOOB;
+            Csv[i >> 3][i & 7] = (__bf16)(ldb(rC, o) * scale);
         }
     }
+    const int64_t ebase = (tokbase + (active ? n0 : 0)) * Di + (int64_t)tile * 32;
+    const uint32_t row2 = (uint32_t)Di * 2;
+    uint32_t vr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) vr[r] = valid ? (uint32_t)((4 * hh + r) * Di + col) * 2 : kOOB;
+    auto LD = [&](const bf16 *t, int i) -> float {
+        return ldb(make_rsrc(t + ebase, (uint32_t)Lw * row2), vr[i & 3], (uint32_t)(8 * (i >> 2)) * row2);
+    };
+    float invf[16], g[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float av = LD(a, i);
+        float dv = LD(dy, i);
+        // tokens past the end keep the state (f = 1)
+        invf[i] = 1.f + (tok(i) < Lw ? ex2(-av * kLog2e) : 0.f);
+        if (BLOCK) {
+            const float zv = LD(z, i);
+            dv *= zv * rcp(1.f + ex2(-zv * kLog2e));  // dy SiLU(z)
+        }
+        g[i] = dv;
+    }
+    float tot[4], cum[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float run = 1.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            run *= invf[4 * q + r];
+            cum[4 * q + r] = run;
+        }
+        tot[q] = run;
+    }
+    float E[4], acc = 1.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float pt = xhalf(tot[q], upper);
+        E[q] = upper ? acc * pt : acc;
+        acc *= tot[q] * pt;
+    }
+    bf16x8 GpH[2], GpL[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        __bf16 hi, lo;
+        split2(g[i] * rcp(E[i >> 2] * cum[i]), hi, lo);
+        GpH[i >> 3][i & 7] = hi;
+        GpL[i >> 3][i & 7] = lo;
+    }
+    f32x16 r = {};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        r = mma(Csv[kb], GpH[kb], r);  // rows: state, columns: channel
+        r = mma(Csv[kb], GpL[kb], r);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sR[tw][tok(i)][col] = r[i];
+    if (upper) sQ[tw][col] = rcp(E[3] * cum[15]);
+    __syncthreads();
+    if (tw == 0) {
+        float Qt = 1.f, Rt[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) Rt[k] = 0.f;
+        for (int w = kTW - 1; w >= 0; --w) {
+            const float qw = sQ[w][col];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) Rt[k] = fmaf(qw, Rt[k], sR[w][8 * hh + k][col]);
+            Qt *= qw;
+        }
+        float *ag = agg + (((size_t)bi * n_tiles + tile) * n_chunks + chunk) * (17 * 32);
+        if (!upper) ag[col] = Qt;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) ag[(1 + 8 * hh + k) * 32 + col] = Rt[k];
+    }
+}
+
+// Reverse scan of the chunk carries: the adjoint arriving after each chunk's
+// last token (dx_final after the sequence), and dx0 before the first token.
+// One thread per (channel, state); a workgroup per (batch row, tile).
+__global__ __launch_bounds__(512) void bwd_carry_scan_kernel(
+    const int64_t Di, const int n_tiles, const int n_chunks, const float *__restrict__ agg,
+    const float *__restrict__ dx_final, float *__restrict__ muin, float *__restrict__ dx0)
+{
+    constexpr int N = 16;
+    const int s = threadIdx.x >> 5, col = threadIdx.x & 31;
+    const int tile = (int)(blockIdx.x % (uint32_t)n_tiles);
+    const int64_t bi = blockIdx.x / (uint32_t)n_tiles;
+    const int64_t c = (int64_t)tile * 32 + col;
+    const bool valid = c < Di;
+    float mu = (dx_final && valid) ? dx_final[(bi * Di + c) * N + s] : 0.f;
+    const size_t e0 = (size_t)blockIdx.x * n_chunks;
+#pragma unroll 4
+    for (int ch = n_chunks - 1; ch >= 0; --ch) {
+        muin[(e0 + ch) * (16 * 32) + s * 32 + col] = mu;
+        const float *ag = agg + (e0 + ch) * (17 * 32);
+        mu = fmaf(ag[col], mu, ag[(1 + s) * 32 + col]);
+    }
+    if (dx0 && valid) dx0[(bi * Di + c) * N + s] = mu;
 }
 
 // ---------------------------------------------------------------- fix-up
@@ -927,9 +993,8 @@ static hipError_t launch_bwd_mfma_t(const BwdArgs &g, hipStream_t stream)
     char *ws = (char *)g.ws;
     WsHeader *hdr = (WsHeader *)ws;
     const int64_t n_waves = (g.L + 31) / 32;
-    uint32_t *flags = (uint32_t *)(ws + pl.off_mflags);
     float *agg = (float *)(ws + pl.off_magg);
-    float *incl = (float *)(ws + pl.off_mincl);
+    float *muin = (float *)(ws + pl.off_mincl);
     float *bc = (float *)(ws + pl.off_bc);
     float *dd = (float *)(ws + pl.off_dd);
     float *dw = (float *)(ws + pl.off_dw);
@@ -937,15 +1002,24 @@ static hipError_t launch_bwd_mfma_t(const BwdArgs &g, hipStream_t stream)
     uint32_t *fmask = (uint32_t *)(ws + pl.off_fixmask);
     uint32_t *flist = (uint32_t *)(ws + pl.off_fixlist);
     float *fmu = (float *)(ws + pl.off_fixmu);
+    hipError_t e;
+    hipLaunchKernelGGL((bwd_carry_kernel<BLOCK>), dim3((unsigned)(g.Bt * m.n_chunks * m.n_tiles)),
+                       dim3(64 * kTW), 0, stream, g.Bt, g.L, g.Di, m.n_tiles, m.n_chunks, g.scale,
+                       (const bf16 *)g.a, (const bf16 *)g.C, (const bf16 *)g.z, (const bf16 *)g.dy,
+                       agg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_carry_scan_kernel, dim3((unsigned)(g.Bt * m.n_tiles)), dim3(512), 0,
+                       stream, g.Di, m.n_tiles, m.n_chunks, (const float *)agg, g.dx_final, muin,
+                       g.dx0);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_mfma_kernel<BLOCK>), dim3((unsigned)m.n_wg), dim3(64 * kTW), 0, stream,
                        g.Bt, g.L, g.Di, m.n_tiles, m.n_sub, m.n_super, m.n_chunks, n_waves,
                        g.scale, (const bf16 *)g.hu, (const bf16 *)g.a, (const bf16 *)g.b,
                        (const bf16 *)g.B, (const bf16 *)g.C, g.D, (const bf16 *)g.z, g.conv_w,
-                       (const bf16 *)g.conv_state, g.ckpt, (const bf16 *)g.dy, g.dx_final,
-                       (bf16 *)g.dhu, (bf16 *)g.da, (bf16 *)g.db, (bf16 *)g.dz, g.dx0, hdr, flags,
-                       agg, incl, bc, dd, dw, edge, fmask, flist, fmu);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+                       (const bf16 *)g.conv_state, g.ckpt, (const bf16 *)g.dy, (const float *)muin,
+                       (bf16 *)g.dhu, (bf16 *)g.da, (bf16 *)g.db, (bf16 *)g.dz, hdr, bc, dd, dw,
+                       edge, fmask, flist, fmu);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_fix_kernel<BLOCK>), dim3(256), dim3(64), 0, stream, g.Bt, g.L, g.Di,
                        m.n_tiles, m.n_sub, m.n_super, n_waves, g.scale, (const bf16 *)g.hu,
                        (const bf16 *)g.a, (const bf16 *)g.b, (const bf16 *)g.B, (const bf16 *)g.C,
