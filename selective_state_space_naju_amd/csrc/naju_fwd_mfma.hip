@@ -179,11 +179,14 @@ __device__ __forceinline__ void rr_output(int64_t L, int64_t Di, int bi, int64_t
 }
 
 // ------------------------------------------------------------------- kernel
-// Persistent: one workgroup per CU takes tickets (workgroup chunks of 64
-// channels x 256 tokens, chunk-major so look-back predecessors always hold
-// smaller tickets) until none are left.  The h/a/b tile of the next ticket is
-// copied HBM -> LDS with global_load_lds_dwordx4 (no VGPRs involved) while the
-// current one runs its matrix products, look-back and epilogue.
+// Persistent: workgroup w of G takes tickets w, w + G, w + 2G, ... (workgroup
+// chunks of 64 channels x 128 tokens, chunk-major, so a look-back predecessor
+// always holds a smaller ticket, taken by a workgroup that is resident and in
+// an earlier or the same round).  The static schedule needs no shared ticket
+// counter; one count per workgroup at exit lets the last one advance the epoch.
+// The h/a/b tile of the next ticket is copied HBM -> LDS with
+// global_load_lds_dwordx4 (no VGPRs involved) while the current one runs its
+// matrix products, look-back and epilogue.
 constexpr int kRows = kFwdT * kMfmaW;  // tokens per workgroup chunk
 
 template <bool BLOCK>
@@ -202,7 +205,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
 
     __shared__ __attribute__((aligned(1024))) bf16 sIn[3][kRows][64];  // h|u, a, b
     __shared__ __attribute__((aligned(1024))) bf16 sBC[2][kRows][16];  // B, C rows
-    __shared__ uint32_t s_next, s_epoch;
+    __shared__ uint32_t s_epoch;
     __shared__ float sP[W][64];
     __shared__ float sS[W][16][64];
     __shared__ float sX[16][64];
@@ -243,20 +246,15 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                                          16, 0, 0);
     };
 
-    if (threadIdx.x == 0) {
-        s_next = add_agent(&hdr->ticket, 1u);
-        s_epoch = (ld_agent(&hdr->epoch) + 1u) & 0x3FFFFFFFu;
-    }
+    if (threadIdx.x == 0) s_epoch = (ld_agent(&hdr->epoch) + 1u) & 0x3FFFFFFFu;
+    uint32_t cur = blockIdx.x;
+    if (cur < total) prefetch(cur, threadIdx.x & 63);
     __syncthreads();
-    uint32_t cur = s_next;
     const uint32_t ep = s_epoch;
-    if (cur >= total) return;
-    prefetch(cur, threadIdx.x & 63);
 
-    for (;;) {
+    while (cur < total) {
         wait_mem();
-        __syncthreads();  // the tile of `cur` is in LDS; s_next consumed
-        if (threadIdx.x == 0) s_next = add_agent(&hdr->ticket, 1u);
+        __syncthreads();  // the tile of `cur` is in LDS
         // lane-dependent values are re-derived every ticket (kept out of
         // loop-invariant code motion, which would otherwise pin dozens of
         // per-lane addresses in registers across the whole loop)
@@ -397,8 +395,8 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
             }
         }
         const bool wave_ok = __all(ok);
-        __syncthreads();  // every wave is done with sIn; s_next is visible
-        const uint32_t nxt = s_next;
+        __syncthreads();  // every wave is done with sIn
+        const uint32_t nxt = cur + gridDim.x;
         if (nxt < total) prefetch(nxt, lane);
 
         // ------------------------------------- chunk aggregates (P_T, S) -> LDS
@@ -604,16 +602,15 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         }
 
         __syncthreads();  // sP/sS/sX are reused by the next ticket
-        if (threadIdx.x == 0) {
-            const uint32_t old = add_agent(&hdr->done, 1u);
-            if (old == total - 1) {
-                st_agent(&hdr->ticket, 0u);
-                st_agent(&hdr->done, 0u);
-                st_agent(&hdr->epoch, ep);
-            }
-        }
         cur = nxt;
-        if (cur >= total) break;
+    }
+    // the last workgroup out advances the epoch (every workgroup has read it)
+    if (threadIdx.x == 0) {
+        const uint32_t old = add_agent(&hdr->done, 1u);
+        if (old == gridDim.x - 1) {
+            st_agent(&hdr->done, 0u);
+            st_agent(&hdr->epoch, ep);
+        }
     }
 }
 
