@@ -317,8 +317,9 @@ static bool use_mfma(const FwdArgs &g)
         return v && v[0] == 'r' && v[1] == 'r';
     }();
     const auto al16 = [](const void *p) { return ((uintptr_t)p % 16) == 0; };
-    return !forced_rr && g.io == 1 && g.N == 16 && g.Di % 8 == 0 && al16(g.B) && al16(g.C) &&
-           al16(g.hu) && al16(g.a) && al16(g.b);
+    // (buffer ranges of 32 token rows / 16 checkpoint rows stay below 2^31 bytes)
+    return !forced_rr && g.io == 1 && g.N == 16 && g.Di % 8 == 0 && g.Di < ((int64_t)1 << 24) &&
+           al16(g.B) && al16(g.C) && al16(g.hu) && al16(g.a) && al16(g.b);
 }
 
 hipError_t launch_fwd(const FwdArgs &g, hipStream_t stream)

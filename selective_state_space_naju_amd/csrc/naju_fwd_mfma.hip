@@ -24,6 +24,8 @@
 // Safety: the factorisation needs 1/P over the chunk to stay in range.  A wave
 // whose chunk has prod(1/f) > 2^64 or a non-finite input falls back to the
 // plain register recurrence for that chunk (exact for any input).
+#include <type_traits>
+
 #include "naju_device.h"
 #include "naju_launch.h"
 
@@ -184,10 +186,25 @@ __device__ __forceinline__ void rr_output(int64_t L, int64_t Di, int bi, int64_t
 // always holds a smaller ticket, taken by a workgroup that is resident and in
 // an earlier or the same round).  The static schedule needs no shared ticket
 // counter; one count per workgroup at exit lets the last one advance the epoch.
-// The h/a/b tile of the next ticket is copied HBM -> LDS with
+// The h|u, a, b tile of the next ticket (and, for the block, the eight rows of
+// u before it, for the conv window) is copied HBM -> LDS with
 // global_load_lds_dwordx4 (no VGPRs involved) while the current one runs its
 // matrix products, look-back and epilogue.
 constexpr int kRows = kFwdT * kMfmaW;  // tokens per workgroup chunk
+constexpr int kHalo = 8;               // rows of u kept before the chunk (block)
+
+namespace {
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every range used here
+
+// Raw buffer over [p, p + bytes): loads past the end read 0, stores past the end
+// are dropped; the range check covers the lane offset plus the uniform soffset.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+}  // namespace
 
 template <bool BLOCK>
 __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
@@ -199,12 +216,14 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
     float *__restrict__ x_final, bf16 *__restrict__ conv_state_out, float *__restrict__ ckpt,
     WsHeader *hdr, uint32_t *flags, float *agg, float *incl)
 {
-    constexpr int N = 16, T = kFwdT, W = kMfmaW;
+    constexpr int N = 16, T = kFwdT, W = kMfmaW, H = BLOCK ? kHalo : 0;
     static_assert(T == 32, "one 32x32 MFMA tile of tokens per wave");
-    const int wv = threadIdx.x >> 6;
+    // wave-uniform (readfirstlane keeps what derives from it in scalar registers)
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-    __shared__ __attribute__((aligned(1024))) bf16 sIn[3][kRows][64];  // h|u, a, b
-    __shared__ __attribute__((aligned(1024))) bf16 sBC[2][kRows][16];  // B, C rows
+    __shared__ __attribute__((aligned(16))) bf16 sU[H + kRows][64];  // h (scan) or u (block)
+    __shared__ __attribute__((aligned(16))) bf16 sAB[2][kRows][64];  // a, b
+    __shared__ __attribute__((aligned(16))) bf16 sBC[2][kRows][16];  // B, C rows
     __shared__ uint32_t s_epoch;
     __shared__ float sP[W][64];
     __shared__ float sS[W][16][64];
@@ -213,10 +232,9 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
     const uint32_t per_chunk = (uint32_t)(Bt * n_tiles);
     const uint32_t total = per_chunk * (uint32_t)n_chunks;
     const int64_t n_waves = (L + T - 1) / T;
-    const bf16 *srcs[3] = {hu, a, bg};
 
     // copy the h|u, a, b tile and the B, C rows of ticket tk into LDS (this
-    // wave's 32 rows)
+    // wave's 32 rows; wave 0 also the rows of u before the chunk)
     auto prefetch = [&](uint32_t tk, int lane) {
         const int ch = (int)(tk / per_chunk);
         const int rm = (int)(tk % per_chunk);
@@ -228,12 +246,24 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
             int64_t n = (int64_t)ch * kRows + 32 * wv + 8 * k + (lane >> 3);
             if (n >= L) n = L - 1;  // rows past the end are never used
             const int64_t off = ((int64_t)b_ * L + n) * Di + cg;
-#pragma unroll
-            for (int t = 0; t < 3; ++t)
-                __builtin_amdgcn_global_load_lds(
-                    (const void *)(srcs[t] + off),
-                    (__attribute__((address_space(3))) void *)&sIn[t][32 * wv + 8 * k][0], 16, 0,
-                    0);
+            __builtin_amdgcn_global_load_lds((const void *)(hu + off),
+                                             (__attribute__((address_space(3))) void *)&sU[H + 32 * wv + 8 * k][0],
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(a + off),
+                                             (__attribute__((address_space(3))) void *)&sAB[0][32 * wv + 8 * k][0],
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(bg + off),
+                                             (__attribute__((address_space(3))) void *)&sAB[1][32 * wv + 8 * k][0],
+                                             16, 0, 0);
+        }
+        if (BLOCK && wv == 0) {
+            // rows n0-8 .. n0-1 of u (the first chunk's are replaced after the copy)
+            int64_t n = (int64_t)ch * kRows - 8 + (lane >> 3);
+            if (n < 0) n = 0;
+            if (n >= L) n = L - 1;
+            __builtin_amdgcn_global_load_lds((const void *)(hu + ((int64_t)b_ * L + n) * Di + cg),
+                                             (__attribute__((address_space(3))) void *)&sU[0][0],
+                                             16, 0, 0);
         }
         int64_t n = (int64_t)ch * kRows + 32 * wv + (lane >> 1);
         if (n >= L) n = L - 1;
@@ -262,6 +292,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         asm volatile("" : "+v"(lane));
         const int col = lane & 31;
         const int hh = lane >> 5;
+        const bool upper = hh != 0;
 
         const int chunk = (int)(cur / per_chunk);
         const int rem = (int)(cur % per_chunk);
@@ -270,136 +301,140 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         const int64_t cbase = (int64_t)tile * 64;
         const int64_t n0 = (int64_t)chunk * kRows + (int64_t)wv * T;
         const int64_t tokbase = (int64_t)bi * L;
+        const bool active = n0 < L;
+        const int Lw = active ? (int)(L - n0 < T ? L - n0 : T) : 0;  // valid tokens of the wave
         auto tok = [&](int i) -> int { return 8 * (i >> 2) + 4 * hh + (i & 3); };
 
-        // ------------------------------------------------ token-shared operands
-        bf16x8 Bop, Cop, Csc;
-        {
-            if (n0 + col < L) {
-                const uint4 qb = *(const uint4 *)&sBC[0][32 * wv + col][8 * hh];
-                const uint4 qc = *(const uint4 *)&sBC[1][32 * wv + col][8 * hh];
-                Bop = __builtin_bit_cast(bf16x8, qb);
-                Cop = __builtin_bit_cast(bf16x8, qc);
-            } else {
-#pragma unroll
-                for (int s = 0; s < 8; ++s) Bop[s] = Cop[s] = (__bf16)0.f;
+        if (BLOCK && chunk == 0) {
+            // the conv window before the sequence start: the carried conv state or zeros
+            if (threadIdx.x < 3 * 64) {
+                const int r = threadIdx.x >> 6, chn = threadIdx.x & 63;
+                const int64_t c = cbase + chn;
+                sU[H - 3 + r][chn] = (conv_state && c < Di)
+                                         ? conv_state[((int64_t)bi * 3 + r) * Di + c]
+                                         : (bf16)0;
             }
+            __syncthreads();
+        }
+
+        // ------------------------------------------------ token-shared operands
+        bf16x8 Bop, Cop, Csc, Bsv[2];
+        {
+            const uint4 qb = *(const uint4 *)&sBC[0][32 * wv + col][8 * hh];
+            const uint4 qc = *(const uint4 *)&sBC[1][32 * wv + col][8 * hh];
+            const uint4 z4 = {0u, 0u, 0u, 0u};
+            Bop = __builtin_bit_cast(bf16x8, col < Lw ? qb : z4);
+            Cop = __builtin_bit_cast(bf16x8, col < Lw ? qc : z4);
 #pragma unroll
             for (int s = 0; s < 8; ++s) Csc[s] = (__bf16)((float)Cop[s] * scale);
-        }
-        bf16x8 Bsv[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            bf16 v = 0;
-            if (col < N && n0 + tok(i) < L) v = sBC[0][32 * wv + tok(i)][col];
-            Bsv[i >> 3][i & 7] = as_bf(v);
+            for (int i = 0; i < 16; ++i) {
+                const bf16 v = sBC[0][32 * wv + tok(i)][col & 15];
+                Bsv[i >> 3][i & 7] = as_bf((col < N && tok(i) < Lw) ? v : (bf16)0);
+            }
         }
 
         // ------------------------------------------------------ gates, W', P
+        // Tokens past the end of the sequence (only in the last wave of a row)
+        // get f = 1 and w = 0, so they leave the state and the aggregate alone.
         float Pv[2][16], FT[2][16];
         bf16x8 Whi[2][2], Wlo[2][2];
         float Ptot[2];
         bool ok = true;
+        auto gates = [&](auto tail_c) {
+            constexpr bool TL = decltype(tail_c)::value;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t c = cbase + col + 32 * j;
-            const bool valid = c < Di;
-            const float Dc = valid ? D[c] : 0.f;
-            float cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f;
-            if (BLOCK && valid) {
-                cw0 = conv_w[c * 4 + 0];
-                cw1 = conv_w[c * 4 + 1];
-                cw2 = conv_w[c * 4 + 2];
-                cw3 = conv_w[c * 4 + 3];
-            }
-            float invf[16], wr[16], hv[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int rg = 32 * wv + 8 * q + 4 * hh;  // tile row of the group's first token
-                const int64_t g0 = n0 + 8 * q + 4 * hh;
-                float uw[7];
+            for (int j = 0; j < 2; ++j) {
+                const int chn = 32 * j + col;
+                const int64_t c = cbase + chn;
+                const int64_t cc = c < Di ? c : 0;
+                const float Dc = D[cc];
+                float cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f;
                 if (BLOCK) {
-#pragma unroll
-                    for (int k = 0; k < 7; ++k) {
-                        const int r = rg - 3 + k;
-                        const int64_t m = g0 - 3 + k;
-                        float v = 0.f;
-                        if (r >= 0) {
-                            v = to_f(sIn[0][r][32 * j + col]);
-                        } else if (valid) {
-                            if (m >= 0)
-                                v = to_f(hu[(tokbase + m) * Di + c]);
-                            else if (m >= -3 && conv_state)
-                                v = to_f(conv_state[((int64_t)bi * 3 + (m + 3)) * Di + c]);
-                        }
-                        uw[k] = (m < L) ? v : 0.f;
-                    }
+                    cw0 = conv_w[cc * 4 + 0];
+                    cw1 = conv_w[cc * 4 + 1];
+                    cw2 = conv_w[cc * 4 + 2];
+                    cw3 = conv_w[cc * 4 + 3];
                 }
+                float invf[16], wr[16], hv[16];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 4 * q + r;
-                    const int64_t n = g0 + r;
-                    float e = 0.f, ib = 0.f, h = 0.f;
-                    if (valid && n < L) {
-                        e = ex2(-to_f(sIn[1][rg + r][32 * j + col]) * kLog2e);
-                        ib = sigm(to_f(sIn[2][rg + r][32 * j + col]));
+                for (int q = 0; q < 4; ++q) {
+                    const int rg = 32 * wv + 8 * q + 4 * hh;  // tile row of the group's first token
+                    float uw[7];
+                    if (BLOCK) {
+#pragma unroll
+                        for (int k = 0; k < 7; ++k) uw[k] = to_f(sU[H + rg - 3 + k][chn]);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 4 * q + r;
+                        float h;
                         if (BLOCK) {
-                            const float pre = cw0 * uw[r] + cw1 * uw[r + 1] + cw2 * uw[r + 2] +
-                                              cw3 * uw[r + 3];
+                            const float pre =
+                                cw0 * uw[r] + cw1 * uw[r + 1] + cw2 * uw[r + 2] + cw3 * uw[r + 3];
                             h = pre * sigm(pre);
                         } else {
-                            h = to_f(sIn[0][rg + r][32 * j + col]);
+                            h = to_f(sU[rg + r][chn]);
                         }
+                        float e = ex2(-to_f(sAB[0][rg + r][chn]) * kLog2e);
+                        float w = sigm(to_f(sAB[1][rg + r][chn])) * h;
+                        if (TL) {
+                            const bool tv = tok(i) < Lw;
+                            e = tv ? e : 0.f;
+                            w = tv ? w : 0.f;
+                        }
+                        invf[i] = 1.f + e;
+                        wr[i] = w;
+                        hv[i] = h;
+                        FT[j][i] = Dc * h;
                     }
-                    invf[i] = 1.f + e;
-                    wr[i] = ib * h;
-                    hv[i] = h;
-                    FT[j][i] = Dc * h;
+                }
+                float tot[4], cum[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float run = 1.f;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        run *= invf[4 * q + r];
+                        cum[4 * q + r] = run;
+                    }
+                    tot[q] = run;
+                }
+                float E[4], acc = 1.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float pt = __shfl_xor(tot[q], 32);  // partner group (q, 1-h)
+                    // token order of the groups: (0,0) (0,1) (1,0) (1,1) ...
+                    E[q] = upper ? acc * pt : acc;
+                    acc *= tot[q] * pt;
+                }
+                ok = ok && (acc <= 18446744073709551616.f);  // 2^64; false for NaN
+                Ptot[j] = rcp(acc);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float invP = E[i >> 2] * cum[i];
+                    const float wp = wr[i] * invP;
+                    ok = ok && (__builtin_fabsf(wp) < 1e30f) && (__builtin_fabsf(hv[i]) < 1e30f);
+                    Pv[j][i] = rcp(invP);
+                    FT[j][i] *= invP;  // y = P (G W' + C x_in + D h / P)
+                    __bf16 hi, lo;
+                    split(wp, hi, lo);
+                    Whi[j][i >> 3][i & 7] = hi;
+                    Wlo[j][i >> 3][i & 7] = lo;
                 }
             }
-            float tot[4], cum[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float run = 1.f;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    run *= invf[4 * q + r];
-                    cum[4 * q + r] = run;
-                }
-                tot[q] = run;
-            }
-            float ptot[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) ptot[q] = __shfl_xor(tot[q], 32);
-            float E[4], acc = 1.f;
-#pragma unroll
-            for (int g = 0; g < 8; ++g) {
-                const bool mine = (g & 1) == hh;
-                const float Tg = mine ? tot[g >> 1] : ptot[g >> 1];
-                if (mine) E[g >> 1] = acc;
-                acc *= Tg;
-            }
-            ok = ok && (acc <= 18446744073709551616.f);  // 2^64; false for NaN
-            Ptot[j] = rcp(acc);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float invP = E[i >> 2] * cum[i];
-                const float wp = wr[i] * invP;
-                ok = ok && (__builtin_fabsf(wp) < 1e30f) && (__builtin_fabsf(hv[i]) < 1e30f);
-                Pv[j][i] = rcp(invP);
-                FT[j][i] *= invP;  // y = P (G W' + C x_in + D h / P)
-                __bf16 hi, lo;
-                split(wp, hi, lo);
-                Whi[j][i >> 3][i & 7] = hi;
-                Wlo[j][i >> 3][i & 7] = lo;
-            }
-        }
+        };
+        if (Lw < T)
+            gates(std::true_type{});
+        else
+            gates(std::false_type{});
         const bool wave_ok = __all(ok);
-        __syncthreads();  // every wave is done with sIn
+        __syncthreads();  // every wave is done with the tile
         const uint32_t nxt = cur + gridDim.x;
         if (nxt < total) prefetch(nxt, lane);
 
         // ------------------------------------- chunk aggregates (P_T, S) -> LDS
+        // S = P_T (W'^T B), formed as B^T W' so each lane holds its own channel
         f32x16 Y[2];
         if (wave_ok) {
 #pragma unroll
@@ -407,14 +442,12 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                 f32x16 sacc = {};
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    sacc = mfma(Whi[j][kb], Bsv[kb], sacc);
-                    sacc = mfma(Wlo[j][kb], Bsv[kb], sacc);
+                    sacc = mfma(Bsv[kb], Whi[j][kb], sacc);  // rows: state, columns: channel
+                    sacc = mfma(Bsv[kb], Wlo[j][kb], sacc);
                 }
-                if (col < N) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) sS[wv][col][32 * j + tok(i)] = sacc[i];
-                }
-                if (hh == 0) sP[wv][32 * j + col] = Ptot[j];
+                for (int i = 0; i < 8; ++i) sS[wv][tok(i)][32 * j + col] = sacc[i] * Ptot[j];
+                if (!upper) sP[wv][32 * j + col] = Ptot[j];
             }
         } else {
             float P, S[16];
@@ -423,12 +456,6 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
             sP[wv][lane] = P;
 #pragma unroll
             for (int s = 0; s < 16; ++s) sS[wv][s][lane] = S[s];
-        }
-        __syncthreads();
-        if (wave_ok) {
-            const float pt = sP[wv][lane];
-#pragma unroll
-            for (int s = 0; s < 16; ++s) sS[wv][s][lane] *= pt;
         }
         __syncthreads();
 
@@ -516,8 +543,6 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                 xo[s] = fmaf(Pt, xin[s], St[s]);
                 st_agent(ic + s * 64 + lane, xo[s]);
             }
-            wait_mem();
-            if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagIncl));
 #pragma unroll
             for (int s = 0; s < 16; ++s) sX[s][lane] = xin[s];
             if (valid_lane) {
@@ -538,70 +563,91 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                     }
                 }
             }
+            wait_mem();
+            if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagIncl));
         }
         __syncthreads();
 
-        // --------------------- this wave's entering state (lane = channel):
-        // the workgroup's entering state carried through the waves before it
-        float xin[16];
+        // --------------------- this wave's entering state, in the B-operand
+        // layout (channel 32j + col, states 8h..8h+7): the workgroup's entering
+        // state carried through the waves before it
+        float xs[2][8];
 #pragma unroll
-        for (int s = 0; s < 16; ++s) xin[s] = sX[s][lane];
-        for (int w = 0; w < wv; ++w) {
-            const float pw = sP[w][lane];
+        for (int j = 0; j < 2; ++j) {
+            const int chn = 32 * j + col;
 #pragma unroll
-            for (int s = 0; s < 16; ++s) xin[s] = fmaf(pw, xin[s], sS[w][s][lane]);
+            for (int k = 0; k < 8; ++k) xs[j][k] = sX[8 * hh + k][chn];
+            for (int w = 0; w < wv; ++w) {
+                const float pw = sP[w][chn];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) xs[j][k] = fmaf(pw, xs[j][k], sS[w][8 * hh + k][chn]);
+            }
         }
-        __syncthreads();  // every wave has read sS before it is reused below
-        if (ckpt && valid_lane && n0 < L) {
-            const int64_t wrow = (int64_t)chunk * W + wv;
+        if (ckpt && active) {
+            float *cp = ckpt + (((int64_t)bi * n_waves + (int64_t)chunk * W + wv) * N) * Di + cbase;
+            const rsrc_t rc = make_rsrc(cp, (uint32_t)(N * Di * 4));
 #pragma unroll
-            for (int s = 0; s < 16; ++s)
-                ckpt[(((int64_t)bi * n_waves + wrow) * N + s) * Di + c_lane] = xin[s];
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t vo =
+                    cbase + 32 * j + col < Di ? (uint32_t)((8 * hh) * Di + 32 * j + col) * 4 : kOOB;
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xs[j][k]), rc, vo,
+                                                          (uint32_t)(k * Di) * 4, 0);
+            }
         }
 
         if (!wave_ok) {
-            if (y)
+            if (y) {
+                // the fallback works in lane = channel layout
+                float xin[16];
+#pragma unroll
+                for (int s = 0; s < 16; ++s) xin[s] = sX[s][lane];
+                for (int w = 0; w < wv; ++w) {
+                    const float pw = sP[w][lane];
+#pragma unroll
+                    for (int s = 0; s < 16; ++s) xin[s] = fmaf(pw, xin[s], sS[w][s][lane]);
+                }
                 rr_output<BLOCK>(L, Di, bi, c_lane, valid_lane, n0, scale, hu, a, bg, Bm, Cm, D,
                                  z, conv_w, conv_state, xin, y);
+            }
         } else if (y) {
-#pragma unroll
-            for (int s = 0; s < 16; ++s) sS[wv][s][lane] = xin[s];
-            __builtin_amdgcn_wave_barrier();
+            const int64_t ebase = (tokbase + (active ? n0 : 0)) * Di + cbase;
+            const uint32_t row2 = (uint32_t)Di * 2;
+            const rsrc_t ry = make_rsrc(y + ebase, (uint32_t)Lw * row2);
+            const rsrc_t rz = make_rsrc(BLOCK ? (const void *)(z + ebase) : (const void *)y,
+                                        BLOCK ? (uint32_t)Lw * row2 : 0u);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 bf16x8 xh, xl;
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     __bf16 hi, lo;
-                    split(sS[wv][8 * hh + k][32 * j + col], hi, lo);
+                    split(xs[j][k], hi, lo);
                     xh[k] = hi;
                     xl[k] = lo;
                 }
                 Y[j] = mfma(Csc, xh, Y[j]);
                 Y[j] = mfma(Csc, xl, Y[j]);
-            }
+                const bool vc = cbase + 32 * j + col < Di;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int64_t c = cbase + col + 32 * j;
-                if (c < Di) {
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t vo = vc ? (uint32_t)((4 * hh + r) * Di + 32 * j + col) * 2 : kOOB;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int64_t n = n0 + tok(i);
-                        if (n < L) {
-                            const int64_t t = (tokbase + n) * Di + c;
-                            float yv = Pv[j][i] * Y[j][i];
-                            if (BLOCK) {
-                                const float zv = to_f(z[t]);
-                                yv *= zv * sigm(zv);
-                            }
-                            y[t] = from_f<bf16>(yv);
+                    for (int q = 0; q < 4; ++q) {
+                        const int i = 4 * q + r;
+                        const uint32_t so = (uint32_t)(8 * q) * row2;
+                        float yv = Pv[j][i] * Y[j][i];
+                        if (BLOCK) {
+                            const float zv = __uint_as_float(
+                                (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rz, vo, so, 0) << 16);
+                            yv *= zv * sigm(zv);
                         }
+                        __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(yv), ry, vo, so, 0);
                     }
                 }
             }
         }
-
-        __syncthreads();  // sP/sS/sX are reused by the next ticket
         cur = nxt;
     }
     // the last workgroup out advances the epoch (every workgroup has read it)
