@@ -491,66 +491,107 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         const bool valid_lane = c_lane < Di;
 
         // -------------------------------- look-back for the entering state
-        if (wv == 0) {
-            float Pt = 1.f, St[16];
-#pragma unroll
-            for (int s = 0; s < 16; ++s) St[s] = 0.f;
+        // Split by state group: wave w carries states 4w..4w+3 of the 64 channels
+        // (lane = channel) and publishes / reads its own flags, so the four
+        // waves look back in parallel.  Up to kLB predecessors' flags are read
+        // at once; when every one up to the nearest inclusive state is
+        // published, their payloads are loaded together and folded in order.
+        {
+            constexpr int kLB = 4;
+            const int s0 = 4 * wv;
+            float Pt = 1.f, St[4] = {0.f, 0.f, 0.f, 0.f};
             for (int w = 0; w < W; ++w) {
                 const float pw = sP[w][lane];
 #pragma unroll
-                for (int s = 0; s < 16; ++s) St[s] = fmaf(pw, St[s], sS[w][s][lane]);
+                for (int k = 0; k < 4; ++k) St[k] = fmaf(pw, St[k], sS[w][s0 + k][lane]);
                 Pt *= pw;
             }
             const size_t me = ((size_t)bi * n_tiles + tile) * n_chunks + chunk;
-            float xin[16];
+            const size_t mg = me * W + wv;  // this wave's flag / payload slot
+            float xin[4];
             if (chunk == 0) {
 #pragma unroll
-                for (int s = 0; s < 16; ++s)
-                    xin[s] = (x0 && valid_lane) ? x0[(bi * Di + c_lane) * N + s] : 0.f;
+                for (int k = 0; k < 4; ++k)
+                    xin[k] = (x0 && valid_lane) ? x0[(bi * Di + c_lane) * N + s0 + k] : 0.f;
             } else {
-                float *ag = agg + me * (17 * 64);
+                float *ag = agg + mg * (5 * 64);
                 st_agent(ag + lane, Pt);
 #pragma unroll
-                for (int s = 0; s < 16; ++s) st_agent(ag + (1 + s) * 64 + lane, St[s]);
+                for (int k = 0; k < 4; ++k) st_agent(ag + (1 + k) * 64 + lane, St[k]);
                 wait_mem();
-                if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagAgg));
-                float accP = 1.f, accS[16];
-#pragma unroll
-                for (int s = 0; s < 16; ++s) accS[s] = 0.f;
-                size_t jx = me - 1;
+                if (lane == 0) st_agent(&flags[mg], make_flag(ep, kFlagAgg));
+                float accP = 1.f, accS[4] = {0.f, 0.f, 0.f, 0.f};
+                size_t jx = me - 1;  // nearest predecessor not folded in yet
+                int left = chunk;    // predecessors not folded in yet
+                uint32_t spins = 0;
                 for (;;) {
-                    const uint32_t st = wait_flag(&flags[jx], ep, hdr);
-                    if (st == kFlagIncl) {
-                        const float *in = incl + jx * (16 * 64);
+                    const int K = left < kLB ? left : kLB;
+                    uint32_t st = 0;
+                    if (lane < K) {
+                        const uint32_t f = ld_agent(&flags[(jx - lane) * W + wv]);
+                        st = (f >> 2) == ep ? (f & 3u) : 0u;
+                    }
+                    const uint64_t im = __ballot(lane < K && st == kFlagIncl);
+                    const uint64_t rm = __ballot(lane < K && st != 0u);
+                    const int d = im ? (int)__builtin_ctzll(im) : K;  // aggregates before it
+                    const uint64_t need = im ? ((2ull << d) - 1) : ((1ull << K) - 1);
+                    if ((rm & need) != need) {
+                        if (++spins > kSpinLimit) {
+                            __hip_atomic_fetch_or(&hdr->error, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-                        for (int s = 0; s < 16; ++s)
-                            xin[s] = fmaf(accP, ld_agent(in + s * 64 + lane), accS[s]);
+                            for (int k = 0; k < 4; ++k) xin[k] = 0.f;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
+                        continue;
+                    }
+                    float pj[kLB], sj[kLB][4], in[4];
+#pragma unroll
+                    for (int o = 0; o < kLB; ++o) {
+                        if (o < d) {
+                            const float *pa = agg + ((jx - o) * W + wv) * (5 * 64);
+                            pj[o] = ld_agent(pa + lane);
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) sj[o][k] = ld_agent(pa + (1 + k) * 64 + lane);
+                        }
+                    }
+                    if (im) {
+                        const float *pi = incl + ((jx - d) * W + wv) * (4 * 64);
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) in[k] = ld_agent(pi + k * 64 + lane);
+                    }
+#pragma unroll
+                    for (int o = 0; o < kLB; ++o) {
+                        if (o < d) {
+#pragma unroll
+                            for (int k = 0; k < 4; ++k) accS[k] = fmaf(accP, sj[o][k], accS[k]);
+                            accP *= pj[o];
+                        }
+                    }
+                    if (im) {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) xin[k] = fmaf(accP, in[k], accS[k]);
                         break;
                     }
-                    const float *pa = agg + jx * (17 * 64);
-                    const float pj = ld_agent(pa + lane);
-#pragma unroll
-                    for (int s = 0; s < 16; ++s)
-                        accS[s] = fmaf(accP, ld_agent(pa + (1 + s) * 64 + lane), accS[s]);
-                    accP *= pj;
-                    --jx;
+                    jx -= K;
+                    left -= K;
                 }
             }
-            float *ic = incl + me * (16 * 64);
-            float xo[16];
+            float *ic = incl + mg * (4 * 64);
+            float xo[4];
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                xo[s] = fmaf(Pt, xin[s], St[s]);
-                st_agent(ic + s * 64 + lane, xo[s]);
+            for (int k = 0; k < 4; ++k) {
+                xo[k] = fmaf(Pt, xin[k], St[k]);
+                st_agent(ic + k * 64 + lane, xo[k]);
+                sX[s0 + k][lane] = xin[k];
             }
+            if (valid_lane && chunk == n_chunks - 1) {
+                if (x_final) {
 #pragma unroll
-            for (int s = 0; s < 16; ++s) sX[s][lane] = xin[s];
-            if (valid_lane) {
-                if (chunk == n_chunks - 1 && x_final) {
-#pragma unroll
-                    for (int s = 0; s < 16; ++s) x_final[(bi * Di + c_lane) * N + s] = xo[s];
+                    for (int k = 0; k < 4; ++k) x_final[(bi * Di + c_lane) * N + s0 + k] = xo[k];
                 }
-                if (BLOCK && chunk == n_chunks - 1 && conv_state_out) {
+                if (BLOCK && wv == 0 && conv_state_out) {
 #pragma unroll
                     for (int k = 0; k < 3; ++k) {
                         const int64_t m = L - 3 + k;
@@ -564,7 +605,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                 }
             }
             wait_mem();
-            if (lane == 0) st_agent(&flags[me], make_flag(ep, kFlagIncl));
+            if (lane == 0) st_agent(&flags[mg], make_flag(ep, kFlagIncl));
         }
         __syncthreads();
 
