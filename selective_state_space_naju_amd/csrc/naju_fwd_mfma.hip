@@ -233,30 +233,34 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
     const uint32_t total = per_chunk * (uint32_t)n_chunks;
     const int64_t n_waves = (L + T - 1) / T;
 
-    // copy the h|u, a, b tile and the B, C rows of ticket tk into LDS (this
-    // wave's 32 rows; wave 0 also the rows of u before the chunk)
+    // Copy the h|u, a, b tile and the B, C rows of ticket tk into LDS.  Only
+    // waves 2 and 3 copy (64 rows each; wave 2 also the rows of u before the
+    // chunk and the B rows, wave 3 the C rows): a wave's wait for its own
+    // memory operations covers every one it issued, and waves 0 and 1, which
+    // run the look-back, must not wait for a tile copy on every flag read.
     auto prefetch = [&](uint32_t tk, int lane) {
         const int ch = (int)(tk / per_chunk);
         const int rm = (int)(tk % per_chunk);
         const int b_ = rm / n_tiles;
         const int64_t cb = (int64_t)(rm % n_tiles) * 64 + 8 * (lane & 7);
         const int64_t cg = cb < Di ? cb : 0;  // whole 8-channel groups: Di % 8 == 0
+        const int r0 = 64 * (wv - 2);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            int64_t n = (int64_t)ch * kRows + 32 * wv + 8 * k + (lane >> 3);
+        for (int k = 0; k < 8; ++k) {
+            int64_t n = (int64_t)ch * kRows + r0 + 8 * k + (lane >> 3);
             if (n >= L) n = L - 1;  // rows past the end are never used
             const int64_t off = ((int64_t)b_ * L + n) * Di + cg;
             __builtin_amdgcn_global_load_lds((const void *)(hu + off),
-                                             (__attribute__((address_space(3))) void *)&sU[H + 32 * wv + 8 * k][0],
+                                             (__attribute__((address_space(3))) void *)&sU[H + r0 + 8 * k][0],
                                              16, 0, 0);
             __builtin_amdgcn_global_load_lds((const void *)(a + off),
-                                             (__attribute__((address_space(3))) void *)&sAB[0][32 * wv + 8 * k][0],
+                                             (__attribute__((address_space(3))) void *)&sAB[0][r0 + 8 * k][0],
                                              16, 0, 0);
             __builtin_amdgcn_global_load_lds((const void *)(bg + off),
-                                             (__attribute__((address_space(3))) void *)&sAB[1][32 * wv + 8 * k][0],
+                                             (__attribute__((address_space(3))) void *)&sAB[1][r0 + 8 * k][0],
                                              16, 0, 0);
         }
-        if (BLOCK && wv == 0) {
+        if (BLOCK && wv == 2) {
             // rows n0-8 .. n0-1 of u (the first chunk's are replaced after the copy)
             int64_t n = (int64_t)ch * kRows - 8 + (lane >> 3);
             if (n < 0) n = 0;
@@ -265,20 +269,21 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                                              (__attribute__((address_space(3))) void *)&sU[0][0],
                                              16, 0, 0);
         }
-        int64_t n = (int64_t)ch * kRows + 32 * wv + (lane >> 1);
-        if (n >= L) n = L - 1;
-        const int64_t boff = ((int64_t)b_ * L + n) * N + 8 * (lane & 1);
-        __builtin_amdgcn_global_load_lds((const void *)(Bm + boff),
-                                         (__attribute__((address_space(3))) void *)&sBC[0][32 * wv][0],
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)(Cm + boff),
-                                         (__attribute__((address_space(3))) void *)&sBC[1][32 * wv][0],
-                                         16, 0, 0);
+        const bf16 *bcs = wv == 2 ? Bm : Cm;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            int64_t n = (int64_t)ch * kRows + 32 * k + (lane >> 1);
+            if (n >= L) n = L - 1;
+            const int64_t boff = ((int64_t)b_ * L + n) * N + 8 * (lane & 1);
+            __builtin_amdgcn_global_load_lds((const void *)(bcs + boff),
+                                             (__attribute__((address_space(3))) void *)&sBC[wv - 2][32 * k][0],
+                                             16, 0, 0);
+        }
     };
 
     if (threadIdx.x == 0) s_epoch = (ld_agent(&hdr->epoch) + 1u) & 0x3FFFFFFFu;
     uint32_t cur = blockIdx.x;
-    if (cur < total) prefetch(cur, threadIdx.x & 63);
+    if (cur < total && wv >= 2) prefetch(cur, threadIdx.x & 63);
     __syncthreads();
     const uint32_t ep = s_epoch;
 
@@ -431,7 +436,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         const bool wave_ok = __all(ok);
         __syncthreads();  // every wave is done with the tile
         const uint32_t nxt = cur + gridDim.x;
-        if (nxt < total) prefetch(nxt, lane);
+        if (nxt < total && wv >= 2) prefetch(nxt, lane);
 
         // ------------------------------------- chunk aggregates (P_T, S) -> LDS
         // S = P_T (W'^T B), formed as B^T W' so each lane holds its own channel
@@ -491,36 +496,40 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         const bool valid_lane = c_lane < Di;
 
         // -------------------------------- look-back for the entering state
-        // Split by state group: wave w carries states 4w..4w+3 of the 64 channels
-        // (lane = channel) and publishes / reads its own flags, so the four
-        // waves look back in parallel.  Up to kLB predecessors' flags are read
-        // at once; when every one up to the nearest inclusive state is
+        // Waves 0 and 1 (which issue no tile copies) carry states 8w..8w+7 of
+        // the 64 channels (lane = channel); each publishes / reads its own flags,
+        // so the two look back in parallel.  Up to kLB predecessors' flags are
+        // read at once; when every one up to the nearest inclusive state is
         // published, their payloads are loaded together and folded in order.
-        {
-            constexpr int kLB = 4;
-            const int s0 = 4 * wv;
-            float Pt = 1.f, St[4] = {0.f, 0.f, 0.f, 0.f};
+        if (wv < 2) {
+            constexpr int kLB = 2, SG = 8;
+            const int s0 = SG * wv;
+            float Pt = 1.f, St[SG];
+#pragma unroll
+            for (int k = 0; k < SG; ++k) St[k] = 0.f;
             for (int w = 0; w < W; ++w) {
                 const float pw = sP[w][lane];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) St[k] = fmaf(pw, St[k], sS[w][s0 + k][lane]);
+                for (int k = 0; k < SG; ++k) St[k] = fmaf(pw, St[k], sS[w][s0 + k][lane]);
                 Pt *= pw;
             }
             const size_t me = ((size_t)bi * n_tiles + tile) * n_chunks + chunk;
-            const size_t mg = me * W + wv;  // this wave's flag / payload slot
-            float xin[4];
+            const size_t mg = me * 2 + wv;  // this wave's flag / payload slot
+            float xin[SG];
             if (chunk == 0) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
+                for (int k = 0; k < SG; ++k)
                     xin[k] = (x0 && valid_lane) ? x0[(bi * Di + c_lane) * N + s0 + k] : 0.f;
             } else {
-                float *ag = agg + mg * (5 * 64);
+                float *ag = agg + mg * ((SG + 1) * 64);
                 st_agent(ag + lane, Pt);
 #pragma unroll
-                for (int k = 0; k < 4; ++k) st_agent(ag + (1 + k) * 64 + lane, St[k]);
+                for (int k = 0; k < SG; ++k) st_agent(ag + (1 + k) * 64 + lane, St[k]);
                 wait_mem();
                 if (lane == 0) st_agent(&flags[mg], make_flag(ep, kFlagAgg));
-                float accP = 1.f, accS[4] = {0.f, 0.f, 0.f, 0.f};
+                float accP = 1.f, accS[SG];
+#pragma unroll
+                for (int k = 0; k < SG; ++k) accS[k] = 0.f;
                 size_t jx = me - 1;  // nearest predecessor not folded in yet
                 int left = chunk;    // predecessors not folded in yet
                 uint32_t spins = 0;
@@ -528,7 +537,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                     const int K = left < kLB ? left : kLB;
                     uint32_t st = 0;
                     if (lane < K) {
-                        const uint32_t f = ld_agent(&flags[(jx - lane) * W + wv]);
+                        const uint32_t f = ld_agent(&flags[(jx - lane) * 2 + wv]);
                         st = (f >> 2) == ep ? (f & 3u) : 0u;
                     }
                     const uint64_t im = __ballot(lane < K && st == kFlagIncl);
@@ -540,48 +549,48 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                             __hip_atomic_fetch_or(&hdr->error, 1u, __ATOMIC_RELAXED,
                                                   __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-                            for (int k = 0; k < 4; ++k) xin[k] = 0.f;
+                            for (int k = 0; k < SG; ++k) xin[k] = 0.f;
                             break;
                         }
                         __builtin_amdgcn_s_sleep(1);
                         continue;
                     }
-                    float pj[kLB], sj[kLB][4], in[4];
+                    float pj[kLB], sj[kLB][SG], in[SG];
 #pragma unroll
                     for (int o = 0; o < kLB; ++o) {
                         if (o < d) {
-                            const float *pa = agg + ((jx - o) * W + wv) * (5 * 64);
+                            const float *pa = agg + ((jx - o) * 2 + wv) * ((SG + 1) * 64);
                             pj[o] = ld_agent(pa + lane);
 #pragma unroll
-                            for (int k = 0; k < 4; ++k) sj[o][k] = ld_agent(pa + (1 + k) * 64 + lane);
+                            for (int k = 0; k < SG; ++k) sj[o][k] = ld_agent(pa + (1 + k) * 64 + lane);
                         }
                     }
                     if (im) {
-                        const float *pi = incl + ((jx - d) * W + wv) * (4 * 64);
+                        const float *pi = incl + ((jx - d) * 2 + wv) * (SG * 64);
 #pragma unroll
-                        for (int k = 0; k < 4; ++k) in[k] = ld_agent(pi + k * 64 + lane);
+                        for (int k = 0; k < SG; ++k) in[k] = ld_agent(pi + k * 64 + lane);
                     }
 #pragma unroll
                     for (int o = 0; o < kLB; ++o) {
                         if (o < d) {
 #pragma unroll
-                            for (int k = 0; k < 4; ++k) accS[k] = fmaf(accP, sj[o][k], accS[k]);
+                            for (int k = 0; k < SG; ++k) accS[k] = fmaf(accP, sj[o][k], accS[k]);
                             accP *= pj[o];
                         }
                     }
                     if (im) {
 #pragma unroll
-                        for (int k = 0; k < 4; ++k) xin[k] = fmaf(accP, in[k], accS[k]);
+                        for (int k = 0; k < SG; ++k) xin[k] = fmaf(accP, in[k], accS[k]);
                         break;
                     }
                     jx -= K;
                     left -= K;
                 }
             }
-            float *ic = incl + mg * (4 * 64);
-            float xo[4];
+            float *ic = incl + mg * (SG * 64);
+            float xo[SG];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < SG; ++k) {
                 xo[k] = fmaf(Pt, xin[k], St[k]);
                 st_agent(ic + k * 64 + lane, xo[k]);
                 sX[s0 + k][lane] = xin[k];
@@ -589,7 +598,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
             if (valid_lane && chunk == n_chunks - 1) {
                 if (x_final) {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) x_final[(bi * Di + c_lane) * N + s0 + k] = xo[k];
+                    for (int k = 0; k < SG; ++k) x_final[(bi * Di + c_lane) * N + s0 + k] = xo[k];
                 }
                 if (BLOCK && wv == 0 && conv_state_out) {
 #pragma unroll

@@ -38,9 +38,9 @@ inline FwdPlan fwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N, int W = kF
     p.n_chunks = (int)((L + kFwdT * W - 1) / (kFwdT * W));
     p.n_wg = Bt * p.n_tiles * p.n_chunks;
     p.n_waves = (L + kFwdT - 1) / kFwdT;
-    // the matrix-core forward looks back per wave and state group of four:
-    // four flags and four (P, S[4]) aggregates per workgroup chunk
-    const size_t fl = W == kMfmaW ? 4 : 1, ar = W == kMfmaW ? 20 : 17;
+    // the matrix-core forward looks back in two state groups of eight: two
+    // flags and two (P, S[8]) aggregates per workgroup chunk
+    const size_t fl = W == kMfmaW ? 2 : 1, ar = W == kMfmaW ? 18 : 17;
     p.off_flags = 256;
     p.off_agg = align256(p.off_flags + 4 * fl * (size_t)p.n_wg);
     p.off_incl = align256(p.off_agg + ar * 64 * 4 * (size_t)p.n_wg);
