@@ -57,6 +57,8 @@ __device__ __forceinline__ void split2(float v, __bf16 &hi, __bf16 &lo)
     lo = (__bf16)(v - (float)hi);
 }
 
+__device__ __forceinline__ __bf16 asbf(bf16 v) { return __builtin_bit_cast(__bf16, v); }
+
 // Bit pattern of element s of a bf16x8.  Goes through the whole vector: a
 // bit_cast of a single __bf16 vector element to an integer is mis-lowered by
 // this compiler (every element reads as element 0).
@@ -124,13 +126,16 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
     __shared__ float sR[kTW][16][32];
     // per-token factors consumed once, after the matrix products: sigma(-a) and
     // dy SiLU'(z)  [wave][slot][lane]
-    __shared__ float sSA[kTW][16][64];
+    __shared__ _Float16 sSA[kTW][16][64];  // in (0, 1): fp16 is ample
     __shared__ float sGZ[BLOCK ? kTW : 1][16][64];
+    __shared__ bf16 sUw[BLOCK ? kTW : 1][35][32];  // u: three tokens before the wave, then its 32
     // per-wave transposes for the channel contractions (bf16, padded rows)
     __shared__ __attribute__((aligned(16))) bf16 sGT[kTW][32][40];  // Gp  [token][channel]
     __shared__ __attribute__((aligned(16))) bf16 sWT[kTW][32][40];  // W'  [token][channel]
     __shared__ __attribute__((aligned(16))) bf16 sXT[kTW][16][40];  // x_in [state][channel]
     __shared__ __attribute__((aligned(16))) bf16 sMT[kTW][16][40];  // Mu   [state][channel]
+    __shared__ __attribute__((aligned(16))) bf16 sBr[kTW * 32][16];  // B rows of the 128 tokens
+    __shared__ __attribute__((aligned(16))) bf16 sCr[kTW * 32][16];  // C rows / sqrt(N)
 
     const int sup = (int)(blockIdx.x % (uint32_t)n_super);
     const int bi = (int)((blockIdx.x / (uint32_t)n_super) % (uint32_t)Bt);
@@ -144,27 +149,20 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
     auto tval = [&](int i) -> bool { return tok(i) < Lw; };
 
     // ------------------------------------------------ token-shared operands
-    // Bop/Cop: A/B-operand rows (token col, states 8h..8h+7); Bsv/Csv: the
-    // transposed operands (tokens tok(i)) -- Csv holds state col in columns
-    // 0..15, Bsv state col-16 in columns 16..31, so dB and dC accumulate into the
-    // two halves of one matrix.  C is used pre-scaled (scale = 1/4 is exact in
-    // bf16).
-    bf16x8 Bop, Csc, Bsv[2], Csv[2];
+    // The wave's B and C rows (C pre-scaled: scale = 1/4 is exact in bf16),
+    // zero past the last token, staged once in LDS; the token-shared operands
+    // are read from there where they are used rather than held in registers.
     {
         const rsrc_t rB = make_rsrc(Bm + (tokbase + (active ? n0 : 0)) * N, (uint32_t)Lw * N * 2);
         const rsrc_t rC = make_rsrc(Cm + (tokbase + (active ? n0 : 0)) * N, (uint32_t)Lw * N * 2);
         const uint32_t ro = (uint32_t)(col * N + 8 * hh) * 2;
-        Bop = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rB, ro, 0, 0));
-        const bf16x8 Cop =
-            __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rC, ro, 0, 0));
+        const bf16x8 Bq = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rB, ro, 0, 0));
+        const bf16x8 Cq = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rC, ro, 0, 0));
+        bf16x8 Cs;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) Csc[s] = (__bf16)((float)Cop[s] * scale);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t o = (uint32_t)(tok(i) * N + (col & 15)) * 2;
-            Bsv[i >> 3][i & 7] = (__bf16)ldb(rB, col >= N ? o : kOOB);
-            Csv[i >> 3][i & 7] = (__bf16)(ldb(rC, col < N ? o : kOOB) * scale);
-        }
+        for (int s = 0; s < 8; ++s) Cs[s] = (__bf16)((float)Cq[s] * scale);
+        *(uint4 *)&sBr[32 * tw + col][8 * hh] = __builtin_bit_cast(uint4, Bq);
+        *(uint4 *)&sCr[32 * tw + col][8 * hh] = __builtin_bit_cast(uint4, Cs);
     }
 
     f32x16 dBC = {};  // dB (columns 0..15) | dC / scale (columns 16..31) of this wave's tokens
@@ -180,6 +178,22 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
         const bool upper = hh != 0;
         auto tok = [&](int i) -> int { return 8 * (i >> 2) + 4 * hh + (i & 3); };
         auto tval = [&](int i) -> bool { return tok(i) < Lw; };
+        // token-shared operands: Bop / Csc are A/B-operand rows (token col, states
+        // 8h..8h+7); Bsv / Csv the transposed operands over tokens tok(i), Csv
+        // holding state col in columns 0..15 and Bsv state col-16 in columns
+        // 16..31, so dB and dC accumulate into the two halves of one matrix
+        auto rows = [&](const bf16 (*r)[16]) -> bf16x8 {
+            return __builtin_bit_cast(bf16x8, *(const uint4 *)&r[32 * tw + col][8 * hh]);
+        };
+        auto trans = [&](const bf16 (*r)[16], int kb, bool on) -> bf16x8 {
+            bf16x8 v;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const bf16 e = r[32 * tw + tok(8 * kb + s)][col & 15];
+                v[s] = asbf(on ? e : (bf16)0);
+            }
+            return v;
+        };
         const int tile = sup * n_sub + st;
         const int64_t c = (int64_t)tile * 32 + col;
         const bool valid = c < Di;
@@ -213,7 +227,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                 float dv = LD(dy, i);
                 const float e = tval(i) ? ex2(-av * kLog2e) : 0.f;
                 invf[i] = 1.f + e;
-                sSA[tw][i][lane] = e * rcp(invf[i]);  // sigma(-a)
+                sSA[tw][i][lane] = (_Float16)(e * rcp(invf[i]));  // sigma(-a)
                 if (BLOCK) {
                     const float zv = LD(z, i);
                     const float ez = ex2(-zv * kLog2e);
@@ -267,62 +281,37 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                 cw3 = conv_w[c * 4 + 3];
             }
         }
-        // u window of the lane's tokens as bf16 pairs (exact): w[0..15] its own
-        // tokens, w[16..27] the partner half's tokens r = 1..3 of each group,
-        // w[28..30] the three tokens before the wave
-        uint32_t wk[16];
-        auto wget = [&](int j) -> float {
-            const uint32_t v = wk[j >> 1];
-            return __uint_as_float((j & 1) ? (v & 0xFFFF0000u) : (v << 16));
-        };
-        // window u_{n-3..n} of slot 4q+r: entries k = 0..6 are tokens n-r-3 .. n-r+3
-        auto win = [&](int q, int k) -> float {
-            if (k >= 3) return wget(4 * q + (k - 3));
-            if (upper) return wget(16 + 3 * q + k);
-            return q == 0 ? wget(28 + k) : wget(16 + 3 * (q - 1) + k);
-        };
-        // fills wk (block only); loaded again after the matrix products rather
-        // than kept live across them
+        // the u window: the wave's 32 tokens and the three before, staged in LDS
+        // (row 3 + t is token n0 + t); window u_{n-3..n} of slot 4q+r is rows
+        // 8q + 4h + r .. 8q + 4h + r + 3
+        auto win = [&](int q, int k) -> float { return to_f(sUw[tw][8 * q + 4 * hh + k][col]); };
         auto fill_window = [&]() {
-            uint32_t vo[4];
+            // u at the three tokens before the wave: the previous rows of u, or the
+            // carried conv state before the sequence start
+            const bool first = n0 == 0;
+            const bf16 *pbase = first ? conv_state : hu;
+            const int64_t poff = first ? (int64_t)bi * 3 * Di : (tokbase + n0 - 3) * Di;
+            const uint32_t pbytes = ((first && !conv_state) || !active) ? 0u : 3u * (uint32_t)Di * 2;
+            const rsrc_t rp = make_rsrc(pbytes ? (const void *)(pbase + poff + tile * 32)
+                                               : (const void *)a,
+                                        pbytes);
+            const uint32_t po = valid ? (uint32_t)col * 2 : kOOB;
+            const rsrc_t ru = trs(hu);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                vo[r] = vr[r];
-                asm volatile("" : "+v"(vo[r]));
-            }
-            float uv[16];
+            for (int i = 0; i < 16; ++i)
+                sUw[tw][3 + tok(i)][col] = (bf16)__builtin_amdgcn_raw_buffer_load_b16(
+                    ru, vr[i & 3], (uint32_t)(8 * (i >> 2)) * row2, 0);
+            if (!upper) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) uv[i] = ldb(trs(hu), vo[i & 3], (uint32_t)(8 * (i >> 2)) * row2);
-            {
-                // u at the three tokens before the wave: the previous rows of u,
-                // or the carried conv state before the sequence start
-                const bool first = n0 == 0;
-                const bf16 *pbase = first ? conv_state : hu;
-                const int64_t poff = first ? (int64_t)bi * 3 * Di : (tokbase + n0 - 3) * Di;
-                const uint32_t pbytes =
-                    ((first && !conv_state) || !active) ? 0u : 3u * (uint32_t)Di * 2;
-                const rsrc_t rp = make_rsrc(pbytes ? (const void *)(pbase + poff + tile * 32)
-                                                   : (const void *)a,
-                                            pbytes);
-                const uint32_t po = valid ? (uint32_t)col * 2 : kOOB;
-                float ext[16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-#pragma unroll
-                    for (int r = 1; r < 4; ++r) ext[3 * q + r - 1] = xhalf(uv[4 * q + r], upper);
-#pragma unroll
-                for (int k = 0; k < 3; ++k) ext[12 + k] = ldb(rp, po + (uint32_t)(k * Di) * 2);
-                ext[15] = 0.f;
-                auto pack = [](float lo, float hi) -> uint32_t {
-                    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
-                };
-#pragma unroll
-                for (int k = 0; k < 8; ++k) wk[k] = pack(uv[2 * k], uv[2 * k + 1]);
-#pragma unroll
-                for (int k = 0; k < 8; ++k) wk[8 + k] = pack(ext[2 * k], ext[2 * k + 1]);
+                for (int k = 0; k < 3; ++k)
+                    sUw[tw][k][col] = (bf16)__builtin_amdgcn_raw_buffer_load_b16(
+                        rp, po + (uint32_t)(k * Di) * 2, 0, 0);
             }
         };
-        float h[16], hd[16], ib[16];
+        float h[16], ib[16];
+        // SiLU'(pre) in [-0.1, 1.1], kept as fp16 pairs (2^-11 relative) to save registers
+        typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+        half2_t hd2[8];
         bf16x8 WB[2];
         {
             float uv[16];
@@ -346,10 +335,10 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                         const float sp = rcp(1.f + ep_);
                         const float sm = ep_ < __builtin_huge_valf() ? ep_ * sp : 1.f;
                         hv = pre * sp;
-                        hd[i] = sp * fmaf(pre, sm, 1.f);  // SiLU'(pre)
+                        hd2[i >> 1][i & 1] = (_Float16)(sp * fmaf(pre, sm, 1.f));  // SiLU'(pre)
                     } else {
                         hv = uv[i];
-                        hd[i] = 0.f;
+                        hd2[i >> 1][i & 1] = (_Float16)0.f;
                     }
                     h[i] = hv;
                     const float wp = ib[i] * hv * invP[i];
@@ -372,8 +361,9 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
             f32x16 r = {};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
-                r = mma(Csv[kb], GpH[kb], r);  // rows: state, columns: channel
-                r = mma(Csv[kb], GpL[kb], r);
+                const bf16x8 Cv = trans(sCr, kb, col < N);
+                r = mma(Cv, GpH[kb], r);  // rows: state, columns: channel
+                r = mma(Cv, GpL[kb], r);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) sR[tw][tok(i)][col] = r[i];
@@ -451,6 +441,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                     MH[k] = h2;
                     ML[k] = l2;
                 }
+                const bf16x8 Bop = rows(sBr), Csc = rows(sCr);
                 // tril(G) and its transpose as A operands (C pre-scaled, so G = Csc.B)
                 bf16x8 GA[2], GTA[2];
                 {
@@ -477,7 +468,6 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
             // per 4-token group q: outputs, the exclusive prefix for da, the conv
             // transpose (the upper half finishes its previous group once the
             // partner's first three dpre of this group arrive) and dconv_w partials
-            if (BLOCK) fill_window();  // the u window again, for dconv_w
             float dDp = 0.f, dwa0 = 0.f, dwa1 = 0.f, dwa2 = 0.f, dwa3 = 0.f;
             float base = 0.f;              // prefix of ph over the groups before
             float dprev[4] = {0.f, 0.f, 0.f, 0.f};  // upper half: previous group's dpre
@@ -496,7 +486,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                     dDp = fmaf(g[i], h[i], dDp);
                     if (BLOCK) {
                         ST(dz, i, sGZ[tw][i][lane] * fmaf(Dc, h[i], ysd));
-                        dp[r] = dh * hd[i];
+                        dp[r] = dh * (float)hd2[i >> 1][i & 1];
                     } else {
                         ST(dhu, i, dh);
                     }
@@ -508,7 +498,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int i = 4 * q + r;
-                        ST(da, i, sSA[tw][i][lane] * (phi0 - run));
+                        ST(da, i, (float)sSA[tw][i][lane] * (phi0 - run));
                         run += ph[r];
                     }
                     base += sq + ps;
@@ -615,9 +605,9 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                 }
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    dBC = mma(HTAb[kb], Csv[kb], dBC);  // columns 0..15
-                    dBC = mma(WpT[kb], XMb[kb], dBC);   // columns 0..15
-                    dBC = mma(HAb[kb], Bsv[kb], dBC);   // columns 16..31
+                    dBC = mma(HTAb[kb], trans(sCr, kb, col < N), dBC);   // columns 0..15
+                    dBC = mma(WpT[kb], XMb[kb], dBC);                   // columns 0..15
+                    dBC = mma(HAb[kb], trans(sBr, kb, col >= N), dBC);  // columns 16..31
                     dBC = mma(GpT[kb], XMc[kb], dBC);   // columns 16..31
                 }
             }
