@@ -472,24 +472,26 @@ __global__ void bc_reduce_kernel(const int64_t rows, const int n_tiles, const in
         dC[row * N + (s - N)] = from_f<IO>(acc);
 }
 
-// dD[c] = sum over (batch, wave) rows, dconv_w likewise.  A workgroup of 16
-// waves owns 64 channels; wave w sums rows w, w+16, w+32, ... and the 16 wave
-// partials are added in wave order (fixed order: deterministic).
-__global__ __launch_bounds__(1024) void dd_reduce_kernel(const int64_t rows, const int64_t Di,
+// dD[c] = sum over (batch, wave) rows, dconv_w likewise, in two passes with a
+// fixed order (deterministic).  Pass 1: row group g of RG (consecutive rows)
+// for 64 channels, its four waves taking every fourth row, summed in wave order.
+
+__global__ __launch_bounds__(256) void dd_reduce1_kernel(const int64_t rows, const int64_t Di,
+                                                         const int RG,
                                                          const float *__restrict__ dd_part,
                                                          const float *__restrict__ dw_part,
-                                                         float *__restrict__ dD,
-                                                         float *__restrict__ dconv_w)
+                                                         float *__restrict__ part2)
 {
-    __shared__ float red[16][5][64];
+    __shared__ float red[4][5][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int64_t c = (int64_t)blockIdx.x * 64 + lane;
+    const int g = blockIdx.y;
+    const int64_t r0 = rows * g / RG, r1 = rows * (g + 1) / RG;
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, s4 = 0.f;
     if (c < Di) {
-#pragma unroll 4
-        for (int64_t r = wv; r < rows; r += 16) {
+        for (int64_t r = r0 + wv; r < r1; r += 4) {
             s0 += dd_part[r * Di + c];
-            if (dconv_w) {
+            if (dw_part) {
                 const float4 q = *(const float4 *)(dw_part + (r * Di + c) * 4);
                 s1 += q.x;
                 s2 += q.y;
@@ -505,16 +507,28 @@ __global__ __launch_bounds__(1024) void dd_reduce_kernel(const int64_t rows, con
     red[wv][4][lane] = s4;
     __syncthreads();
     if (wv == 0 && c < Di) {
-        float t[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int w = 0; w < 16; ++w)
-            for (int k = 0; k < 5; ++k) t[k] += red[w][k][lane];
-        dD[c] = t[0];
-        if (dconv_w) {
-            dconv_w[c * 4 + 0] = t[1];
-            dconv_w[c * 4 + 1] = t[2];
-            dconv_w[c * 4 + 2] = t[3];
-            dconv_w[c * 4 + 3] = t[4];
-        }
+#pragma unroll
+        for (int k = 0; k < 5; ++k)
+            part2[((int64_t)g * Di + c) * 5 + k] =
+                ((red[0][k][lane] + red[1][k][lane]) + red[2][k][lane]) + red[3][k][lane];
+    }
+}
+
+// Pass 2: the RG row-group partials of each channel, in group order.
+__global__ void dd_reduce2_kernel(const int64_t Di, const int RG, const float *__restrict__ part2,
+                                  float *__restrict__ dD, float *__restrict__ dconv_w)
+{
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= Di) return;
+    float t[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < RG; ++g)
+        for (int k = 0; k < 5; ++k) t[k] += part2[((int64_t)g * Di + c) * 5 + k];
+    dD[c] = t[0];
+    if (dconv_w) {
+        dconv_w[c * 4 + 0] = t[1];
+        dconv_w[c * 4 + 1] = t[2];
+        dconv_w[c * 4 + 2] = t[3];
+        dconv_w[c * 4 + 3] = t[4];
     }
 }
 
@@ -610,10 +624,19 @@ static hipError_t launch_bwd_finish(const BwdArgs &g, int n_parts, hipStream_t s
                            (IO *)g.dC);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(dd_reduce_kernel, dim3((unsigned)((g.Di + 63) / 64)), dim3(1024), 0, stream,
-                       g.Bt * pl.n_waves, g.Di, (const float *)dd, (const float *)dw, g.dD,
-                       g.block ? g.dconv_w : (float *)nullptr);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    {
+        const int64_t rows = g.Bt * pl.n_waves;
+        const int RG = (int)(rows / 8 < 1 ? 1 : rows / 8 > kDdGroups ? kDdGroups : rows / 8);
+        float *part2 = (float *)(ws + pl.off_dd2);
+        hipLaunchKernelGGL(dd_reduce1_kernel, dim3((unsigned)((g.Di + 63) / 64), (unsigned)RG),
+                           dim3(256), 0, stream, rows, g.Di, RG, (const float *)dd,
+                           g.block ? (const float *)dw : (const float *)nullptr, part2);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(dd_reduce2_kernel, dim3((unsigned)((g.Di + 255) / 256)), dim3(256), 0,
+                           stream, g.Di, RG, (const float *)part2, g.dD,
+                           g.block ? g.dconv_w : (float *)nullptr);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (g.block) {
         const int64_t tot = g.Bt * pl.n_waves * g.Di;
         hipLaunchKernelGGL((edge_fix_kernel<IO>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0,

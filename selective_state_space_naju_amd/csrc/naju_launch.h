@@ -86,6 +86,8 @@ inline MfmaBwdShape mfma_bwd_shape(int64_t Bt, int64_t L, int64_t Di)
     return m;
 }
 
+constexpr int kDdGroups = 32;  // most row groups of the first dD / dconv_w reduction pass
+
 struct BwdPlan {
     int n_tiles, n_chunks;
     int64_t n_wg, n_waves;
@@ -103,6 +105,7 @@ struct BwdPlan {
     size_t off_fixmask;  // [Bt][n_super][n_waves] u32 tile bits
     size_t off_fixlist;  // [Bt][n_super][n_waves] u32 keys
     size_t off_fixmu;    // [Bt][n_waves][N][Di] fp32 entering adjoints
+    size_t off_dd2;      // dD / dconv_w row-group partials [kDdGroups][Di][5] fp32
     size_t bytes;
 };
 
@@ -135,7 +138,8 @@ inline BwdPlan bwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N, bool block
     p.off_fixmask = align256(p.off_fwd + fwd_ws_bytes(Bt, L, Di, N));
     p.off_fixlist = align256(p.off_fixmask + 4 * n_keys);
     p.off_fixmu = align256(p.off_fixlist + 4 * n_keys);
-    p.bytes = align256(p.off_fixmu + (N == 16 ? ckpt_bytes(Bt, L, Di, N) : 0));
+    p.off_dd2 = align256(p.off_fixmu + (N == 16 ? ckpt_bytes(Bt, L, Di, N) : 0));
+    p.bytes = align256(p.off_dd2 + (size_t)kDdGroups * Di * 5 * 4);
     return p;
 }
 
