@@ -97,6 +97,16 @@ __device__ __forceinline__ float xhalf(float v, bool upper)
     return __uint_as_float(upper ? r[0] : r[1]);
 }
 
+// Workgroups b and b + 8 run on the same XCD (round-robin dispatch) and start
+// together; they are paired on the two halves of 128-byte rows (two adjacent
+// 32-channel tiles), so each line is fetched once into that XCD's L2 and used
+// by both.  Groups of 16 workgroups hold 8 pairs: pair index p, half h.
+__device__ __forceinline__ void pair_of(uint32_t b, uint32_t &p, int &h)
+{
+    p = (b >> 4) * 8 + (b & 7);
+    h = (int)((b >> 3) & 1);
+}
+
 }  // namespace
 
 template <bool BLOCK>
@@ -137,9 +147,18 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
     __shared__ __attribute__((aligned(16))) bf16 sBr[kTW * 32][16];  // B rows of the 128 tokens
     __shared__ __attribute__((aligned(16))) bf16 sCr[kTW * 32][16];  // C rows / sqrt(N)
 
-    const int sup = (int)(blockIdx.x % (uint32_t)n_super);
-    const int bi = (int)((blockIdx.x / (uint32_t)n_super) % (uint32_t)Bt);
-    const int chunk = (int)(blockIdx.x / (uint32_t)n_super / (uint32_t)Bt);
+    // a pair of workgroups covers 2 n_sub consecutive tiles, half h taking
+    // tiles 2 st + h; sup = 2 (pair's tile group) + h indexes the dB/dC partials
+    uint32_t pr;
+    int hf;
+    pair_of(blockIdx.x, pr, hf);
+    const uint32_t n_ps = (uint32_t)(n_super / 2);
+    if (pr >= (uint32_t)n_chunks * (uint32_t)Bt * n_ps) return;
+    const int ps = (int)(pr % n_ps);
+    const int bi = (int)((pr / n_ps) % (uint32_t)Bt);
+    const int chunk = (int)(pr / n_ps / (uint32_t)Bt);
+    const int sup = 2 * ps + hf;
+    auto tile_of = [&](int st) -> int { return ps * 2 * n_sub + 2 * st + hf; };
     const int64_t n0 = (int64_t)chunk * (kTW * T) + (int64_t)tw * T;
     const int64_t wrow = (int64_t)chunk * kTW + tw;
     const bool active = n0 < L;
@@ -166,9 +185,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
     }
 
     f32x16 dBC = {};  // dB (columns 0..15) | dC / scale (columns 16..31) of this wave's tokens
-    const int n_sub_here = (n_tiles - sup * n_sub) < n_sub ? (n_tiles - sup * n_sub) : n_sub;
-
-    for (int st = 0; st < n_sub_here; ++st) {
+    for (int st = 0; st < n_sub && tile_of(st) < n_tiles; ++st) {
         // lane-derived values are re-derived every tile: kept out of loop-invariant
         // code motion, which would pin dozens of them (masks, offsets) in registers
         // across the whole loop
@@ -194,7 +211,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
             }
             return v;
         };
-        const int tile = sup * n_sub + st;
+        const int tile = tile_of(st);
         const int64_t c = (int64_t)tile * 32 + col;
         const bool valid = c < Di;
         const int64_t ebase = (tokbase + (active ? n0 : 0)) * Di + (int64_t)tile * 32;
@@ -649,9 +666,15 @@ __global__ __launch_bounds__(64 * kTW) void bwd_carry_kernel(
     __shared__ float sQ[kTW][32];
     __shared__ float sR[kTW][16][32];
 
-    const int tile = (int)(blockIdx.x % (uint32_t)n_tiles);
-    const int chunk = (int)((blockIdx.x / (uint32_t)n_tiles) % (uint32_t)n_chunks);
-    const int bi = (int)(blockIdx.x / (uint32_t)n_tiles / (uint32_t)n_chunks);
+    uint32_t pr;
+    int hf;
+    pair_of(blockIdx.x, pr, hf);
+    const uint32_t n_tp = (uint32_t)(n_tiles + 1) / 2;  // tile pairs
+    if (pr >= (uint32_t)Bt * (uint32_t)n_chunks * n_tp) return;
+    const int tile = (int)(pr % n_tp) * 2 + hf;
+    if (tile >= n_tiles) return;
+    const int chunk = (int)((pr / n_tp) % (uint32_t)n_chunks);
+    const int bi = (int)(pr / n_tp / (uint32_t)n_chunks);
     const int64_t n0 = (int64_t)chunk * (kTW * T) + (int64_t)tw * T;
     const bool active = n0 < L;
     const int Lw = active ? (int)(L - n0 < T ? L - n0 : T) : 0;
@@ -802,7 +825,7 @@ __global__ __launch_bounds__(64) void bwd_fix_kernel(
         const int64_t tokbase = (int64_t)bi * L;
         for (int pr = 0; 2 * pr < n_sub; ++pr) {
             const int st = 2 * pr + (lane >> 5);
-            const int tile = sup * n_sub + st;
+            const int tile = (sup >> 1) * 2 * n_sub + 2 * st + (sup & 1);
             const int64_t c = (int64_t)tile * 32 + (lane & 31);
             const bool mine = st < n_sub && tile < n_tiles && ((tmask >> st) & 1u) != 0;
             const bool valid = c < Di && mine;
@@ -993,7 +1016,8 @@ static hipError_t launch_bwd_mfma_t(const BwdArgs &g, hipStream_t stream)
     uint32_t *flist = (uint32_t *)(ws + pl.off_fixlist);
     float *fmu = (float *)(ws + pl.off_fixmu);
     hipError_t e;
-    hipLaunchKernelGGL((bwd_carry_kernel<BLOCK>), dim3((unsigned)(g.Bt * m.n_chunks * m.n_tiles)),
+    const int64_t k1_pairs = g.Bt * m.n_chunks * ((m.n_tiles + 1) / 2);
+    hipLaunchKernelGGL((bwd_carry_kernel<BLOCK>), dim3((unsigned)(16 * ((k1_pairs + 7) / 8))),
                        dim3(64 * kTW), 0, stream, g.Bt, g.L, g.Di, m.n_tiles, m.n_chunks, g.scale,
                        (const bf16 *)g.a, (const bf16 *)g.C, (const bf16 *)g.z, (const bf16 *)g.dy,
                        agg);
@@ -1002,7 +1026,8 @@ static hipError_t launch_bwd_mfma_t(const BwdArgs &g, hipStream_t stream)
                        stream, g.Di, m.n_tiles, m.n_chunks, (const float *)agg, g.dx_final, muin,
                        g.dx0);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_mfma_kernel<BLOCK>), dim3((unsigned)m.n_wg), dim3(64 * kTW), 0, stream,
+    const int64_t k3_pairs = m.n_wg / 2;
+    hipLaunchKernelGGL((bwd_mfma_kernel<BLOCK>), dim3((unsigned)(16 * ((k3_pairs + 7) / 8))), dim3(64 * kTW), 0, stream,
                        g.Bt, g.L, g.Di, m.n_tiles, m.n_sub, m.n_super, m.n_chunks, n_waves,
                        g.scale, (const bf16 *)g.hu, (const bf16 *)g.a, (const bf16 *)g.b,
                        (const bf16 *)g.B, (const bf16 *)g.C, g.D, (const bf16 *)g.z, g.conv_w,

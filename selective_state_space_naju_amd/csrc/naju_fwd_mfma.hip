@@ -497,13 +497,12 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
 
         // -------------------------------- look-back for the entering state
         // Waves 0 and 1 (which issue no tile copies) carry states 8w..8w+7 of
-        // the 64 channels (lane = channel) and look back in parallel.  Every
-        // published value travels with its tag -- the epoch and whether it is
-        // the chunk's aggregate (P, S) or its inclusive state x_out -- in one
-        // 64-bit store, so publishing needs no wait and a reader accepts a
-        // payload only if all of its tags are current: one round trip per step.
+        // the 64 channels (lane = channel); each publishes / reads its own flags,
+        // so the two look back in parallel.  Up to kLB predecessors' flags are
+        // read at once; when every one up to the nearest inclusive state is
+        // published, their payloads are loaded together and folded in order.
         if (wv < 2) {
-            constexpr int SG = 8;
+            constexpr int kLB = 2, SG = 8;
             const int s0 = SG * wv;
             float Pt = 1.f, St[SG];
 #pragma unroll
@@ -515,77 +514,85 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                 Pt *= pw;
             }
             const size_t me = ((size_t)bi * n_tiles + tile) * n_chunks + chunk;
-            const uint64_t tagA = (uint64_t)make_flag(ep, kFlagAgg) << 32;
-            const uint64_t tagI = (uint64_t)make_flag(ep, kFlagIncl) << 32;
-            // slot of (ticket j, this wave): aggregate [SG + 1][64], inclusive [SG][64] pairs
-            auto aslot = [&](size_t j) { return (uint64_t *)agg + (j * 2 + wv) * ((SG + 1) * 64); };
-            auto islot = [&](size_t j) { return (uint64_t *)incl + (j * 2 + wv) * (SG * 64); };
-            auto put = [&](uint64_t *p, float v, uint64_t tag) {
-                __hip_atomic_store(p, tag | __float_as_uint(v), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            };
-            auto get = [&](const uint64_t *p) -> uint64_t {
-                return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-            };
+            const size_t mg = me * 2 + wv;  // this wave's flag / payload slot
             float xin[SG];
             if (chunk == 0) {
 #pragma unroll
                 for (int k = 0; k < SG; ++k)
                     xin[k] = (x0 && valid_lane) ? x0[(bi * Di + c_lane) * N + s0 + k] : 0.f;
             } else {
-                uint64_t *ag = aslot(me);
-                put(ag + lane, Pt, tagA);
+                float *ag = agg + mg * ((SG + 1) * 64);
+                st_agent(ag + lane, Pt);
 #pragma unroll
-                for (int k = 0; k < SG; ++k) put(ag + (1 + k) * 64 + lane, St[k], tagA);
+                for (int k = 0; k < SG; ++k) st_agent(ag + (1 + k) * 64 + lane, St[k]);
+                wait_mem();
+                if (lane == 0) st_agent(&flags[mg], make_flag(ep, kFlagAgg));
                 float accP = 1.f, accS[SG];
 #pragma unroll
                 for (int k = 0; k < SG; ++k) accS[k] = 0.f;
                 size_t jx = me - 1;  // nearest predecessor not folded in yet
+                int left = chunk;    // predecessors not folded in yet
                 uint32_t spins = 0;
                 for (;;) {
-                    // the predecessor's inclusive state and aggregate, read together
-                    const uint64_t *pi = islot(jx), *pa = aslot(jx);
-                    uint64_t vi[SG], va[SG + 1];
-#pragma unroll
-                    for (int k = 0; k < SG; ++k) vi[k] = get(pi + k * 64 + lane);
-#pragma unroll
-                    for (int k = 0; k <= SG; ++k) va[k] = get(pa + k * 64 + lane);
-                    bool iok = true, aok = true;
-#pragma unroll
-                    for (int k = 0; k < SG; ++k) iok = iok && (vi[k] & 0xFFFFFFFF00000000ull) == tagI;
-#pragma unroll
-                    for (int k = 0; k <= SG; ++k) aok = aok && (va[k] & 0xFFFFFFFF00000000ull) == tagA;
-                    if (__all(iok)) {
-#pragma unroll
-                        for (int k = 0; k < SG; ++k)
-                            xin[k] = fmaf(accP, __uint_as_float((uint32_t)vi[k]), accS[k]);
-                        break;
+                    const int K = left < kLB ? left : kLB;
+                    uint32_t st = 0;
+                    if (lane < K) {
+                        const uint32_t f = ld_agent(&flags[(jx - lane) * 2 + wv]);
+                        st = (f >> 2) == ep ? (f & 3u) : 0u;
                     }
-                    if (__all(aok)) {
+                    const uint64_t im = __ballot(lane < K && st == kFlagIncl);
+                    const uint64_t rm = __ballot(lane < K && st != 0u);
+                    const int d = im ? (int)__builtin_ctzll(im) : K;  // aggregates before it
+                    const uint64_t need = im ? ((2ull << d) - 1) : ((1ull << K) - 1);
+                    if ((rm & need) != need) {
+                        if (++spins > kSpinLimit) {
+                            __hip_atomic_fetch_or(&hdr->error, 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-                        for (int k = 0; k < SG; ++k)
-                            accS[k] = fmaf(accP, __uint_as_float((uint32_t)va[1 + k]), accS[k]);
-                        accP *= __uint_as_float((uint32_t)va[0]);
-                        --jx;  // chunk 0 always publishes its inclusive state
+                            for (int k = 0; k < SG; ++k) xin[k] = 0.f;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(1);
                         continue;
                     }
-                    if (++spins > kSpinLimit) {
-                        __hip_atomic_fetch_or(&hdr->error, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
+                    float pj[kLB], sj[kLB][SG], in[SG];
 #pragma unroll
-                        for (int k = 0; k < SG; ++k) xin[k] = 0.f;
+                    for (int o = 0; o < kLB; ++o) {
+                        if (o < d) {
+                            const float *pa = agg + ((jx - o) * 2 + wv) * ((SG + 1) * 64);
+                            pj[o] = ld_agent(pa + lane);
+#pragma unroll
+                            for (int k = 0; k < SG; ++k) sj[o][k] = ld_agent(pa + (1 + k) * 64 + lane);
+                        }
+                    }
+                    if (im) {
+                        const float *pi = incl + ((jx - d) * 2 + wv) * (SG * 64);
+#pragma unroll
+                        for (int k = 0; k < SG; ++k) in[k] = ld_agent(pi + k * 64 + lane);
+                    }
+#pragma unroll
+                    for (int o = 0; o < kLB; ++o) {
+                        if (o < d) {
+#pragma unroll
+                            for (int k = 0; k < SG; ++k) accS[k] = fmaf(accP, sj[o][k], accS[k]);
+                            accP *= pj[o];
+                        }
+                    }
+                    if (im) {
+#pragma unroll
+                        for (int k = 0; k < SG; ++k) xin[k] = fmaf(accP, in[k], accS[k]);
                         break;
                     }
-                    __builtin_amdgcn_s_sleep(1);
+                    jx -= K;
+                    left -= K;
                 }
             }
-            uint64_t *ic = islot(me);
+            float *ic = incl + mg * (SG * 64);
             float xo[SG];
 #pragma unroll
             for (int k = 0; k < SG; ++k) {
                 xo[k] = fmaf(Pt, xin[k], St[k]);
-                put(ic + k * 64 + lane, xo[k], tagI);
+                st_agent(ic + k * 64 + lane, xo[k]);
                 sX[s0 + k][lane] = xin[k];
             }
             if (valid_lane && chunk == n_chunks - 1) {
@@ -606,6 +613,8 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                     }
                 }
             }
+            wait_mem();
+            if (lane == 0) st_agent(&flags[mg], make_flag(ep, kFlagIncl));
         }
         __syncthreads();
 

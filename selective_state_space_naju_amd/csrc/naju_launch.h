@@ -38,15 +38,13 @@ inline FwdPlan fwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N, int W = kF
     p.n_chunks = (int)((L + kFwdT * W - 1) / (kFwdT * W));
     p.n_wg = Bt * p.n_tiles * p.n_chunks;
     p.n_waves = (L + kFwdT - 1) / kFwdT;
-    // the matrix-core forward looks back in two state groups of eight, with
-    // 8-byte (value, tag) pairs: two (P, S[8]) aggregates and two x_out[8]
-    // per workgroup chunk
-    const size_t ab = W == kMfmaW ? 2 * 9 * 64 * 8 : 17 * 64 * 4;
-    const size_t ib = W == kMfmaW ? 2 * 8 * 64 * 8 : 16 * 64 * 4;
+    // the matrix-core forward looks back in two state groups of eight: two
+    // flags and two (P, S[8]) aggregates per workgroup chunk
+    const size_t fl = W == kMfmaW ? 2 : 1, ar = W == kMfmaW ? 18 : 17;
     p.off_flags = 256;
-    p.off_agg = align256(p.off_flags + 4 * (size_t)p.n_wg);
-    p.off_incl = align256(p.off_agg + ab * (size_t)p.n_wg);
-    p.bytes = align256(p.off_incl + ib * (size_t)p.n_wg);
+    p.off_agg = align256(p.off_flags + 4 * fl * (size_t)p.n_wg);
+    p.off_incl = align256(p.off_agg + ar * 64 * 4 * (size_t)p.n_wg);
+    p.bytes = align256(p.off_incl + 16 * 64 * 4 * (size_t)p.n_wg);
     return p;
 }
 
@@ -77,10 +75,13 @@ struct MfmaBwdShape {
 
 inline MfmaBwdShape mfma_bwd_shape(int64_t Bt, int64_t L, int64_t Di)
 {
+    // workgroups come in pairs sharing 2 n_sub consecutive tiles (alternate
+    // tiles each), so n_super is even
     MfmaBwdShape m{};
     m.n_tiles = (int)((Di + 31) / 32);
-    m.n_sub = m.n_tiles < 4 ? (m.n_tiles > 0 ? m.n_tiles : 1) : 4;
-    m.n_super = (m.n_tiles + m.n_sub - 1) / m.n_sub;
+    const int half = (m.n_tiles + 1) / 2;
+    m.n_sub = half < 4 ? (half > 0 ? half : 1) : 4;
+    m.n_super = 2 * ((m.n_tiles + 2 * m.n_sub - 1) / (2 * m.n_sub));
     m.n_chunks = (int)((L + 127) / 128);
     m.n_wg = Bt * m.n_super * m.n_chunks;
     return m;
