@@ -226,8 +226,13 @@ def main():
     rf = rf_scan
     if "block_bwd" in parts and "block_fwd" in parts:
         if parts["block_bwd"]["ms_mean"] >= parts["block_fwd"]["ms_mean"]:
-            rf = roofline("block_bwd", "naju_block_bwd call: naju::bwd_mfma_kernel<true> + fix-up "
-                          "+ 3 reduction kernels")
+            bwd_src = ("selective_state_space_naju_amd/csrc/naju_bwd_mfma.hip",
+                       "selective_state_space_naju_amd/csrc/naju_bwd.hip",
+                       "selective_state_space_naju_amd/csrc/naju_device.h",
+                       "selective_state_space_naju_amd/csrc/naju_launch.h")
+            rf = roofline("block_bwd", "naju_block_bwd call: bwd_carry + bwd_carry_scan + "
+                          "bwd_mfma<true> (gradients) + bwd_fix + 4 reduction kernels",
+                          "hbm_traffic_block_bwd_train_bf16_b8_l2048_d1536_n16.md", bwd_src)
         else:
             rf = roofline("block_fwd", "naju::fwd_mfma_kernel<true> (naju_block_fwd)")
 
