@@ -238,6 +238,8 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
     // chunk and the B rows, wave 3 the C rows): a wave's wait for its own
     // memory operations covers every one it issued, and waves 0 and 1, which
     // run the look-back, must not wait for a tile copy on every flag read.
+    // The copies and the y stores carry the nontemporal hint (aux = 2): every
+    // byte is used once, so it should not displace the look-back traffic in L2.
     auto prefetch = [&](uint32_t tk, int lane) {
         const int ch = (int)(tk / per_chunk);
         const int rm = (int)(tk % per_chunk);
@@ -252,13 +254,13 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
             const int64_t off = ((int64_t)b_ * L + n) * Di + cg;
             __builtin_amdgcn_global_load_lds((const void *)(hu + off),
                                              (__attribute__((address_space(3))) void *)&sU[H + r0 + 8 * k][0],
-                                             16, 0, 0);
+                                             16, 0, 2);
             __builtin_amdgcn_global_load_lds((const void *)(a + off),
                                              (__attribute__((address_space(3))) void *)&sAB[0][r0 + 8 * k][0],
-                                             16, 0, 0);
+                                             16, 0, 2);
             __builtin_amdgcn_global_load_lds((const void *)(bg + off),
                                              (__attribute__((address_space(3))) void *)&sAB[1][r0 + 8 * k][0],
-                                             16, 0, 0);
+                                             16, 0, 2);
         }
         if (BLOCK && wv == 2) {
             // rows n0-8 .. n0-1 of u (the first chunk's are replaced after the copy)
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
             if (n >= L) n = L - 1;
             __builtin_amdgcn_global_load_lds((const void *)(hu + ((int64_t)b_ * L + n) * Di + cg),
                                              (__attribute__((address_space(3))) void *)&sU[0][0],
-                                             16, 0, 0);
+                                             16, 0, 2);
         }
         const bf16 *bcs = wv == 2 ? Bm : Cm;
 #pragma unroll
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
             const int64_t boff = ((int64_t)b_ * L + n) * N + 8 * (lane & 1);
             __builtin_amdgcn_global_load_lds((const void *)(bcs + boff),
                                              (__attribute__((address_space(3))) void *)&sBC[wv - 2][32 * k][0],
-                                             16, 0, 0);
+                                             16, 0, 2);
         }
     };
 
@@ -693,7 +695,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                                 (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rz, vo, so, 0) << 16);
                             yv *= zv * sigm(zv);
                         }
-                        __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(yv), ry, vo, so, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(yv), ry, vo, so, 2);
                     }
                 }
             }
