@@ -204,6 +204,23 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
                                              0x00020000);
 }
+
+// 16 bytes per lane HBM -> LDS through a buffer descriptor (buffer_load_dwordx4
+// ... lds, nontemporal): lane i copies bytes voff + soff of r (zeros past its
+// range) to lds + 16 i.  Issued through inline assembly so that the compiler's
+// memory-counter bookkeeping does not see it: it would otherwise wait for the
+// copy before LDS reads it cannot prove disjoint from it and before later uses
+// of ordinary loads.  The caller waits for the copy (vmcnt(0)) before reading
+// it.  M0 holds the LDS address; the compiler does not use M0 in this kernel.
+__device__ __forceinline__ void dma16b(rsrc_t r, uint32_t voff, uint32_t soff, const void *lds)
+{
+    const uint32_t la = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)lds);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen nt lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(la), "s"(soff)
+                 : "memory", "m0");
+}
 }  // namespace
 
 template <bool BLOCK>
@@ -244,42 +261,45 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         const int ch = (int)(tk / per_chunk);
         const int rm = (int)(tk % per_chunk);
         const int b_ = rm / n_tiles;
-        const int64_t cb = (int64_t)(rm % n_tiles) * 64 + 8 * (lane & 7);
-        const int64_t cg = cb < Di ? cb : 0;  // whole 8-channel groups: Di % 8 == 0
+        const int64_t cbase_t = (int64_t)(rm % n_tiles) * 64;
         const int r0 = 64 * (wv - 2);
+        const int64_t n_0 = (int64_t)ch * kRows;
+        const int rows = (int)(L - n_0 < kRows ? L - n_0 : kRows);
+        const uint32_t rowb = (uint32_t)Di * 2;
+        const int64_t tb = ((int64_t)b_ * L + n_0) * Di + cbase_t;  // the tile's first element
+        // lane: row lane / 8 of an 8-row group, 16-byte column chunk lane % 8,
+        // relative to the tile's first channel; the range ends with the last
+        // row's channel Di, so rows past L read 0 (channels past Di of the
+        // other rows read the next row's first channels; no output uses them)
+        const uint32_t range = (uint32_t)rows * rowb - (uint32_t)cbase_t * 2;
+        const uint32_t vo = ((uint32_t)(r0 + (lane >> 3)) * (uint32_t)Di + 8 * (lane & 7)) * 2;
+        const rsrc_t rh = make_rsrc(hu + tb, range);
+        const rsrc_t ra = make_rsrc(a + tb, range);
+        const rsrc_t rb = make_rsrc(bg + tb, range);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            int64_t n = (int64_t)ch * kRows + r0 + 8 * k + (lane >> 3);
-            if (n >= L) n = L - 1;  // rows past the end are never used
-            const int64_t off = ((int64_t)b_ * L + n) * Di + cg;
-            __builtin_amdgcn_global_load_lds((const void *)(hu + off),
-                                             (__attribute__((address_space(3))) void *)&sU[H + r0 + 8 * k][0],
-                                             16, 0, 2);
-            __builtin_amdgcn_global_load_lds((const void *)(a + off),
-                                             (__attribute__((address_space(3))) void *)&sAB[0][r0 + 8 * k][0],
-                                             16, 0, 2);
-            __builtin_amdgcn_global_load_lds((const void *)(bg + off),
-                                             (__attribute__((address_space(3))) void *)&sAB[1][r0 + 8 * k][0],
-                                             16, 0, 2);
+            const uint32_t so = (uint32_t)(8 * k) * rowb;
+            dma16b(rh, vo, so, &sU[H + r0 + 8 * k][0]);
+            dma16b(ra, vo, so, &sAB[0][r0 + 8 * k][0]);
+            dma16b(rb, vo, so, &sAB[1][r0 + 8 * k][0]);
         }
         if (BLOCK && wv == 2) {
             // rows n0-8 .. n0-1 of u (the first chunk's are replaced after the copy)
-            int64_t n = (int64_t)ch * kRows - 8 + (lane >> 3);
-            if (n < 0) n = 0;
-            if (n >= L) n = L - 1;
-            __builtin_amdgcn_global_load_lds((const void *)(hu + ((int64_t)b_ * L + n) * Di + cg),
-                                             (__attribute__((address_space(3))) void *)&sU[0][0],
-                                             16, 0, 2);
+            const rsrc_t rs = make_rsrc(hu + (ch > 0 ? tb - 8 * Di : tb),
+                                        ch > 0 ? 8u * rowb - (uint32_t)cbase_t * 2 : 0u);
+            const uint32_t vh = ((uint32_t)(lane >> 3) * (uint32_t)Di + 8 * (lane & 7)) * 2;
+            dma16b(rs, vh, 0u, &sU[0][0]);
         }
-        const bf16 *bcs = wv == 2 ? Bm : Cm;
+        // B rows (wave 2) or C rows (wave 3): lane = row lane / 2 of a 32-row group
+        const uint32_t vb = (uint32_t)((lane >> 1) * N + 8 * (lane & 1)) * 2;
+        if (wv == 2) {
+            const rsrc_t rs = make_rsrc(Bm + ((int64_t)b_ * L + n_0) * N, (uint32_t)rows * (N * 2));
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            int64_t n = (int64_t)ch * kRows + 32 * k + (lane >> 1);
-            if (n >= L) n = L - 1;
-            const int64_t boff = ((int64_t)b_ * L + n) * N + 8 * (lane & 1);
-            __builtin_amdgcn_global_load_lds((const void *)(bcs + boff),
-                                             (__attribute__((address_space(3))) void *)&sBC[wv - 2][32 * k][0],
-                                             16, 0, 2);
+            for (int k = 0; k < 4; ++k) dma16b(rs, vb, (uint32_t)(32 * k * N * 2), &sBC[0][32 * k][0]);
+        } else {
+            const rsrc_t rs = make_rsrc(Cm + ((int64_t)b_ * L + n_0) * N, (uint32_t)rows * (N * 2));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dma16b(rs, vb, (uint32_t)(32 * k * N * 2), &sBC[1][32 * k][0]);
         }
     };
 

@@ -34,6 +34,12 @@ SMALL = [
     (2, 530, 70, 64, "bf16"),
     (3, 1, 64, 16, "f32"),
     (1, 513, 129, 16, "bf16"),
+    # bf16 with d_inner % 8 == 0 takes the matrix-core kernels: ragged channel
+    # tiles, a partial last chunk, several look-back predecessors, more
+    # tickets than resident workgroups
+    (2, 300, 200, 16, "bf16"),
+    (3, 1000, 136, 16, "bf16"),
+    (4, 2100, 264, 16, "bf16"),
 ]
 
 
