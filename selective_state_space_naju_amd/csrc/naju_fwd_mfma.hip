@@ -39,12 +39,6 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8 &a, const bf16x8 &b, const f
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void split(float v, __bf16 &hi, __bf16 &lo)
-{
-    hi = (__bf16)v;
-    lo = (__bf16)(v - (float)hi);
-}
-
 __device__ __forceinline__ __bf16 as_bf(bf16 v) { return __builtin_bit_cast(__bf16, v); }
 
 // ------------------------------------------------------------------ fallback
@@ -203,6 +197,57 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
                                              0x00020000);
+}
+
+// value of lane l ^ 32 (v_permlane32_swap)
+__device__ __forceinline__ float xhalf(float v, bool upper)
+{
+    const uint32_t u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(upper ? r[0] : r[1]);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Split 16 fp32 values (K-slots i = 8kb + e) into bf16 hi + lo operands: hi
+// keeps the top 16 bits (truncation), lo = v - hi exactly, rounded to bf16;
+// hi + lo is within 2^-16 of v.
+__device__ __forceinline__ void split16(const float (&v)[16], bf16x8 (&hi)[2], bf16x8 (&lo)[2])
+{
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float v0 = v[8 * kb + 2 * e], v1 = v[8 * kb + 2 * e + 1];
+            const uint32_t b0 = __float_as_uint(v0), b1 = __float_as_uint(v1);
+            h[e] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+            const f32x2 r = {v0 - __uint_as_float(b0 & 0xffff0000u),
+                             v1 - __uint_as_float(b1 & 0xffff0000u)};
+            l[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+        }
+        const uint4 hq = {h[0], h[1], h[2], h[3]}, lq = {l[0], l[1], l[2], l[3]};
+        hi[kb] = __builtin_bit_cast(bf16x8, hq);
+        lo[kb] = __builtin_bit_cast(bf16x8, lq);
+    }
+}
+
+__device__ __forceinline__ void split8(const float (&v)[8], bf16x8 &hi, bf16x8 &lo)
+{
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float v0 = v[2 * e], v1 = v[2 * e + 1];
+        const uint32_t b0 = __float_as_uint(v0), b1 = __float_as_uint(v1);
+        h[e] = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
+        const f32x2 r = {v0 - __uint_as_float(b0 & 0xffff0000u),
+                         v1 - __uint_as_float(b1 & 0xffff0000u)};
+        l[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+    }
+    const uint4 hq = {h[0], h[1], h[2], h[3]}, lq = {l[0], l[1], l[2], l[3]};
+    hi = __builtin_bit_cast(bf16x8, hq);
+    lo = __builtin_bit_cast(bf16x8, lq);
 }
 
 // 16 bytes per lane HBM -> LDS through a buffer descriptor (buffer_load_dwordx4
@@ -383,7 +428,10 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                     cw2 = conv_w[cc * 4 + 2];
                     cw3 = conv_w[cc * 4 + 3];
                 }
-                float invf[16], wr[16], hv[16];
+                // e_a = e^{-a}, e_b = e^{-b}; invP_n = prod_{k<=n} (1 + e_a) = 1/P_n in
+                // the wave's 32 tokens.  One reciprocal r = 1 / (invP (1 + e_b))
+                // gives sigma(b) = r invP and P = r (1 + e_b).
+                float cum[16], eb[16], hv[16], tot[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int rg = 32 * wv + 8 * q + 4 * hh;  // tile row of the group's first token
@@ -392,6 +440,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
 #pragma unroll
                         for (int k = 0; k < 7; ++k) uw[k] = to_f(sU[H + rg - 3 + k][chn]);
                     }
+                    float run = 1.f;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int i = 4 * q + r;
@@ -403,52 +452,42 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                         } else {
                             h = to_f(sU[rg + r][chn]);
                         }
-                        float e = ex2(-to_f(sAB[0][rg + r][chn]) * kLog2e);
-                        float w = sigm(to_f(sAB[1][rg + r][chn])) * h;
+                        float ea = ex2(to_f(sAB[0][rg + r][chn]) * -kLog2e);
+                        eb[i] = ex2(to_f(sAB[1][rg + r][chn]) * -kLog2e);
                         if (TL) {
                             const bool tv = tok(i) < Lw;
-                            e = tv ? e : 0.f;
-                            w = tv ? w : 0.f;
+                            ea = tv ? ea : 0.f;
+                            h = tv ? h : 0.f;
                         }
-                        invf[i] = 1.f + e;
-                        wr[i] = w;
+                        run = fmaf(run, ea, run);  // prod (1 + e^{-a})
+                        cum[i] = run;
                         hv[i] = h;
-                        FT[j][i] = Dc * h;
-                    }
-                }
-                float tot[4], cum[16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float run = 1.f;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        run *= invf[4 * q + r];
-                        cum[4 * q + r] = run;
                     }
                     tot[q] = run;
                 }
                 float E[4], acc = 1.f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float pt = __shfl_xor(tot[q], 32);  // partner group (q, 1-h)
+                    const float pt = xhalf(tot[q], upper);  // partner group (q, 1-h)
                     // token order of the groups: (0,0) (0,1) (1,0) (1,1) ...
                     E[q] = upper ? acc * pt : acc;
                     acc *= tot[q] * pt;
                 }
                 ok = ok && (acc <= 18446744073709551616.f);  // 2^64; false for NaN
                 Ptot[j] = rcp(acc);
+                float wp[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float invP = E[i >> 2] * cum[i];
-                    const float wp = wr[i] * invP;
-                    ok = ok && (__builtin_fabsf(wp) < 1e30f) && (__builtin_fabsf(hv[i]) < 1e30f);
-                    Pv[j][i] = rcp(invP);
-                    FT[j][i] *= invP;  // y = P (G W' + C x_in + D h / P)
-                    __bf16 hi, lo;
-                    split(wp, hi, lo);
-                    Whi[j][i >> 3][i & 7] = hi;
-                    Wlo[j][i >> 3][i & 7] = lo;
+                    const float qv = fmaf(invP, eb[i], invP);  // invP (1 + e^{-b})
+                    const float r = rcp(qv);
+                    const float t = hv[i] * invP;
+                    wp[i] = t * (r * invP);     // h sigma(b) / P
+                    Pv[j][i] = fmaf(r, eb[i], r);  // P
+                    FT[j][i] = Dc * t;          // y = P (G W' + C x_in + D h / P)
+                    ok = ok && (__builtin_fabsf(wp[i]) < 1e30f) && (qv < 1.329228e36f);  // 2^120
                 }
+                split16(wp, Whi[j], Wlo[j]);
             }
         };
         if (Lw < T)
@@ -491,14 +530,10 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
             f32x16 g = {};
             g = mfma(Bop, Cop, g);  // g[i] = C_{col} . B_{tok(i)} = G[col][tok(i)]
             bf16x8 Ghi[2], Glo[2];
+            float gv[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float v = (tok(i) <= col) ? g[i] * scale : 0.f;
-                __bf16 hi, lo;
-                split(v, hi, lo);
-                Ghi[i >> 3][i & 7] = hi;
-                Glo[i >> 3][i & 7] = lo;
-            }
+            for (int i = 0; i < 16; ++i) gv[i] = (tok(i) <= col) ? g[i] * scale : 0.f;
+            split16(gv, Ghi, Glo);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 f32x16 acc;
@@ -692,13 +727,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 bf16x8 xh, xl;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    __bf16 hi, lo;
-                    split(xs[j][k], hi, lo);
-                    xh[k] = hi;
-                    xl[k] = lo;
-                }
+                split8(xs[j], xh, xl);
                 Y[j] = mfma(Csc, xh, Y[j]);
                 Y[j] = mfma(Csc, xl, Y[j]);
                 const bool vc = cbase + 32 * j + col < Di;
