@@ -514,22 +514,29 @@ __global__ __launch_bounds__(256) void dd_reduce1_kernel(const int64_t rows, con
     }
 }
 
-// Pass 2: the RG row-group partials of each channel, in group order.
-__global__ void dd_reduce2_kernel(const int64_t Di, const int RG, const float *__restrict__ part2,
-                                  float *__restrict__ dD, float *__restrict__ dconv_w)
+// Pass 2: the RG row-group partials of each (channel, quantity), in group
+// order; one thread per (channel, quantity) -- consecutive in memory -- with
+// the group loads issued before the ordered sum.
+__global__ __launch_bounds__(256) void dd_reduce2_kernel(const int64_t Di, const int RG,
+                                                         const float *__restrict__ part2,
+                                                         float *__restrict__ dD,
+                                                         float *__restrict__ dconv_w)
 {
-    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (c >= Di) return;
-    float t[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int g = 0; g < RG; ++g)
-        for (int k = 0; k < 5; ++k) t[k] += part2[((int64_t)g * Di + c) * 5 + k];
-    dD[c] = t[0];
-    if (dconv_w) {
-        dconv_w[c * 4 + 0] = t[1];
-        dconv_w[c * 4 + 1] = t[2];
-        dconv_w[c * 4 + 2] = t[3];
-        dconv_w[c * 4 + 3] = t[4];
-    }
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // c * 5 + k
+    if (i >= Di * 5) return;
+    float v[kDdGroups];
+#pragma unroll
+    for (int g = 0; g < kDdGroups; ++g) v[g] = g < RG ? part2[(int64_t)g * Di * 5 + i] : 0.f;
+    float t = 0.f;
+#pragma unroll
+    for (int g = 0; g < kDdGroups; ++g)
+        if (g < RG) t += v[g];
+    const int64_t c = i / 5;
+    const int k = (int)(i % 5);
+    if (k == 0)
+        dD[c] = t;
+    else if (dconv_w)
+        dconv_w[c * 4 + (k - 1)] = t;
 }
 
 // Completes du for the last three tokens of every wave with the dpre of the
@@ -550,26 +557,36 @@ __global__ void edge_fix_kernel(const int64_t Bt, const int64_t L, const int64_t
     const float w[4] = {conv_w[c * 4 + 0], conv_w[c * 4 + 1], conv_w[c * 4 + 2],
                         conv_w[c * 4 + 3]};
     const float *eg = edge + ((bi * n_waves + wrow) * 6) * Di + c;
-    const float *en = edge + ((bi * n_waves + wrow + 1) * 6) * Di + c;  // next wave
     const int64_t n0 = wrow * T;
+    // the next wave's dpre at its first three tokens (rows 0..2 of its record)
+    float en[3] = {0.f, 0.f, 0.f};
+    if (n0 + T < L) {
+        const float *ep = edge + ((bi * n_waves + wrow + 1) * 6) * Di + c;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) en[k] = n0 + T + k < L ? ep[k * Di] : 0.f;
+    }
+    // this wave's partial du at its last three tokens (rows 3..5)
+#pragma unroll
     for (int q = 0; q < 3; ++q) {
         const int64_t m = n0 + T - 3 + q;
-        if (m >= L) break;
-        float acc = eg[(3 + q) * Di];
-        for (int k = 0; k < 4; ++k) {
-            const int64_t n = m + 3 - k;
-            if (n >= n0 + T && n < L) acc += w[k] * en[(n - (n0 + T)) * Di];
+        if (m < L) {
+            float acc = eg[(3 + q) * Di];
+            // du_m gets w[k] dpre_{m+3-k} for m+3-k = n0+T+q-k in the next wave
+#pragma unroll
+            for (int k = 0; k <= q; ++k) acc += w[k] * en[q - k];
+            du[(bi * L + m) * Di + c] = from_f<IO>(acc);
         }
-        du[(bi * L + m) * Di + c] = from_f<IO>(acc);
     }
     if (wrow == 0 && dconv_state) {
+        // inputs before u_0: dconv_state[q] (token q - 3) gets w[k] dpre_{q-k}
+        float e0[3];
+#pragma unroll
+        for (int n = 0; n < 3; ++n) e0[n] = n < L ? eg[n * Di] : 0.f;
+#pragma unroll
         for (int q = 0; q < 3; ++q) {
-            const int64_t m = q - 3;
             float acc = 0.f;
-            for (int k = 0; k < 4; ++k) {
-                const int64_t n = m + 3 - k;
-                if (n >= 0 && n < L && n < 3) acc += w[k] * eg[n * Di];
-            }
+#pragma unroll
+            for (int k = 0; k <= q; ++k) acc += w[k] * e0[q - k];
             dconv_state[(bi * 3 + q) * Di + c] = from_f<IO>(acc);
         }
     }
@@ -632,7 +649,7 @@ static hipError_t launch_bwd_finish(const BwdArgs &g, int n_parts, hipStream_t s
                            dim3(256), 0, stream, rows, g.Di, RG, (const float *)dd,
                            g.block ? (const float *)dw : (const float *)nullptr, part2);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(dd_reduce2_kernel, dim3((unsigned)((g.Di + 255) / 256)), dim3(256), 0,
+        hipLaunchKernelGGL(dd_reduce2_kernel, dim3((unsigned)((g.Di * 5 + 255) / 256)), dim3(256), 0,
                            stream, g.Di, RG, (const float *)part2, g.dD,
                            g.block ? g.dconv_w : (float *)nullptr);
         if ((e = hipGetLastError()) != hipSuccess) return e;
