@@ -194,6 +194,25 @@ def main():
         if ws.error_flags():
             raise RuntimeError("a cross-workgroup wait gave up: results invalid")
 
+    # decode step (one token per call, state and conv window carried in place) at the
+    # workload's batch and width: per-call latency and bytes moved
+    t_ds = None
+    if args.only == "all":
+        xs = torch.zeros((Bt, Di, N), dtype=torch.float32, device=dev)
+        cst = torch.zeros((Bt, 3, Di), dtype=torch.bfloat16, device=dev)
+        yst = torch.empty((Bt, Di), dtype=torch.bfloat16, device=dev)
+        dec = [{k: sets[i][k][:, i].contiguous() for k in ("u", "z", "a", "b", "B", "C")}
+               for i in range(NSETS)]
+
+        def block_step(i):
+            s = dec[i]
+            nb.check(L_.naju_block_step(ctypes.byref(dims), p(s["u"]), p(s["z"]), p(cw), p(cst),
+                                        p(s["a"]), p(s["b"]), p(s["B"]), p(s["C"]), p(D), p(xs),
+                                        p(yst), stream))
+        for k in range(10):
+            block_step(k % NSETS)
+        t_ds = timed_launches(block_step, 100)
+
     tokens = Bt * L
     parts = {}
     for name, tt, kind in (("scan_fwd", t_sf, "scan_fwd"), ("block_fwd", t_bf, "block_fwd"),
@@ -206,6 +225,16 @@ def main():
                        "tokens_per_s": round(tokens / (ms * 1e-3), 1),
                        "alg_bytes": int(by), "GB_per_s": round(by / (ms * 1e-3) / 1e9, 1),
                        "pct_hbm_peak": round(100 * by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+
+    if t_ds is not None:
+        ms = float(np.median(t_ds))
+        # state read + write, u z a b read, y write, conv window read + write, B C, D, conv_w
+        by = Bt * Di * N * 8 + Bt * Di * 5 * e + Bt * 3 * Di * e * 2 + Bt * N * 2 * e + Di * 4 * 5
+        parts["block_step"] = {"what": "naju_block_step, one token for each of the %d rows" % Bt,
+                               "us_median": round(ms * 1e3, 2),
+                               "us_mean": round(float(t_ds.mean()) * 1e3, 2),
+                               "tokens_per_s": round(Bt / (ms * 1e-3), 1), "alg_bytes": int(by),
+                               "GB_per_s": round(by / (ms * 1e-3) / 1e9, 1)}
 
     def roofline(part, kernel, traffic_md=None, sources=()):
         by = parts[part]["alg_bytes"]

@@ -179,6 +179,37 @@ naju_status_t naju_block_bwd(const naju_dims_t *dims, const void *u, const void 
                              void *dconv_state, void *da, void *db, void *dB, void *dC,
                              float *dD, float *dx0, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Decode step: one token of the scan for every batch row, with the state
+ * carried in place -- the streaming-generation form of the same recurrence
+ * and readout (naju_scan_fwd on one token with x0 = x, x_final written back
+ * to x).  dims->seqlen is not used; no workspace.
+ *   h, a, b   [Bt][Di] io         this token's activation and gate pre-activations
+ *   B, C      [Bt][N]  io
+ *   D         [Di] fp32
+ *   x         [Bt][Di][N] fp32, 16-byte aligned: the state before the token on
+ *             entry, after it on return (read and written by the call)
+ *   y         [Bt][Di] io         output (written)
+ * batch <= 65535.
+ */
+naju_status_t naju_scan_step(const naju_dims_t *dims, const void *h, const void *a,
+                             const void *b, const void *B, const void *C, const float *D,
+                             float *x, void *y, void *stream);
+
+/*
+ * Block decode step: one token of the block (naju_block_fwd on one token with
+ * x0 = x and conv_state, both updated in place).
+ *   u, z          [Bt][Di] io
+ *   conv_w        [Di][K] fp32
+ *   conv_state    [Bt][K-1][Di] io: the K-1 inputs before u (oldest first) on
+ *                 entry; shifted by one token (u appended) on return
+ *   a, b, B, C, D, x, y   as naju_scan_step
+ */
+naju_status_t naju_block_step(const naju_dims_t *dims, const void *u, const void *z,
+                              const float *conv_w, void *conv_state, const void *a,
+                              const void *b, const void *B, const void *C, const float *D,
+                              float *x, void *y, void *stream);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char *naju_last_error(void);
 

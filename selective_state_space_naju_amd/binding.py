@@ -26,7 +26,8 @@ D_CONV = 4
 # every function the header declares (the CPU tests check the exports)
 EXPORTS = ("naju_workspace_bytes", "naju_ckpt_bytes", "naju_workspace_init",
            "naju_workspace_check", "naju_scan_fwd", "naju_scan_bwd", "naju_block_fwd",
-           "naju_block_bwd", "naju_last_error", "naju_version")
+           "naju_block_bwd", "naju_scan_step", "naju_block_step", "naju_last_error",
+           "naju_version")
 
 
 class NajuError(RuntimeError):
@@ -75,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.naju_scan_bwd.restype = st
         L.naju_block_bwd.argtypes = [dp] + [vp] * 24 + [sz, vp]
         L.naju_block_bwd.restype = st
+        L.naju_scan_step.argtypes = [dp] + [vp] * 9
+        L.naju_scan_step.restype = st
+        L.naju_block_step.argtypes = [dp] + [vp] * 12
+        L.naju_block_step.restype = st
         L.naju_last_error.argtypes = []
         L.naju_last_error.restype = ctypes.c_char_p
         L.naju_version.argtypes = []
@@ -290,3 +295,44 @@ def block_bwd(u, z, conv_w, a, b, B, C, D, dy, x0=None, dx_final=None, conv_stat
                                _p(out["dB"]), _p(out["dC"]), _p(out["dD"]), _p(out["dx0"]),
                                ws.ptr, ws.nbytes, stream_handle(dev)))
     return out
+
+
+def scan_step(h, a, b, B, C, D, x):
+    """y = naju_scan_step(h, a, b, B, C, D, x); x ([Bt, Di, N] fp32) is updated in place."""
+    Bt, Di = h.shape
+    N = B.shape[-1]
+    dt, dev = h.dtype, h.device
+    io = _io_of(h)
+    for nm, t in (("h", h), ("a", a), ("b", b)):
+        _req(t, nm, (Bt, Di), dt, dev)
+    _req(B, "B", (Bt, N), dt, dev)
+    _req(C, "C", (Bt, N), dt, dev)
+    _req(D, "D", (Di,), torch.float32, dev)
+    _req(x, "x", (Bt, Di, N), torch.float32, dev)
+    dims = make_dims(Bt, 1, Di, N, io)
+    y = torch.empty((Bt, Di), dtype=dt, device=dev)
+    check(lib().naju_scan_step(ctypes.byref(dims), _p(h), _p(a), _p(b), _p(B), _p(C), _p(D),
+                               _p(x), _p(y), stream_handle(dev)))
+    return y
+
+
+def block_step(u, z, conv_w, conv_state, a, b, B, C, D, x):
+    """y = naju_block_step(...); x and conv_state ([Bt, K-1, Di]) are updated in place."""
+    Bt, Di = u.shape
+    N = B.shape[-1]
+    dt, dev = u.dtype, u.device
+    io = _io_of(u)
+    for nm, t in (("u", u), ("z", z), ("a", a), ("b", b)):
+        _req(t, nm, (Bt, Di), dt, dev)
+    _req(B, "B", (Bt, N), dt, dev)
+    _req(C, "C", (Bt, N), dt, dev)
+    _req(D, "D", (Di,), torch.float32, dev)
+    _req(conv_w, "conv_w", (Di, D_CONV), torch.float32, dev)
+    _req(conv_state, "conv_state", (Bt, D_CONV - 1, Di), dt, dev)
+    _req(x, "x", (Bt, Di, N), torch.float32, dev)
+    dims = make_dims(Bt, 1, Di, N, io)
+    y = torch.empty((Bt, Di), dtype=dt, device=dev)
+    check(lib().naju_block_step(ctypes.byref(dims), _p(u), _p(z), _p(conv_w), _p(conv_state),
+                                _p(a), _p(b), _p(B), _p(C), _p(D), _p(x), _p(y),
+                                stream_handle(dev)))
+    return y

@@ -360,6 +360,66 @@ naju_status_t naju_workspace_check(const void *ws, size_t ws_bytes, void *stream
     return hip_status(e, "workspace check");
 }
 
+// ------------------------------------------------------------ decode step
+static naju_status_t step_common(bool block, const naju_dims_t *d, const void *hu, const void *z,
+                                 const float *conv_w, void *conv_state, const void *a,
+                                 const void *b, const void *B, const void *C, const float *D,
+                                 float *x, void *y, void *stream)
+{
+    TRY(check_dims(d, block));
+    if (empty(d)) return NAJU_OK;
+    const size_t e = d->io == NAJU_F32 ? 4 : 2;
+    TRY(need(hu, block ? "u" : "h", e));
+    TRY(need(a, "a", e));
+    TRY(need(b, "b", e));
+    TRY(need(B, "B", e));
+    TRY(need(C, "C", e));
+    TRY(need(D, "D", 4));
+    TRY(need(x, "x", 16));
+    TRY(need(y, "y", e));
+    if (block) {
+        TRY(need(z, "z", e));
+        TRY(need(conv_w, "conv_w", 4));
+        TRY(need(conv_state, "conv_state", e));
+    }
+    if (d->batch > 65535) return fail(NAJU_EINVAL, "batch %lld too large for a step (65535 max)",
+                                      (long long)d->batch);
+    StepArgs g{};
+    g.io = d->io;
+    g.N = (int)d->d_state;
+    g.block = block;
+    g.Bt = d->batch;
+    g.Di = d->d_inner;
+    g.scale = (float)(1.0 / sqrt((double)d->d_state));
+    g.hu = hu;
+    g.a = a;
+    g.b = b;
+    g.B = B;
+    g.C = C;
+    g.D = D;
+    g.z = z;
+    g.conv_w = conv_w;
+    g.conv_state = conv_state;
+    g.x = x;
+    g.y = y;
+    return hip_status(launch_step(g, (hipStream_t)stream), "step launch");
+}
+
+naju_status_t naju_scan_step(const naju_dims_t *dims, const void *h, const void *a, const void *b,
+                             const void *B, const void *C, const float *D, float *x, void *y,
+                             void *stream)
+{
+    return step_common(false, dims, h, nullptr, nullptr, nullptr, a, b, B, C, D, x, y, stream);
+}
+
+naju_status_t naju_block_step(const naju_dims_t *dims, const void *u, const void *z,
+                              const float *conv_w, void *conv_state, const void *a, const void *b,
+                              const void *B, const void *C, const float *D, float *x, void *y,
+                              void *stream)
+{
+    return step_common(true, dims, u, z, conv_w, conv_state, a, b, B, C, D, x, y, stream);
+}
+
 naju_status_t naju_scan_fwd(const naju_dims_t *dims, const void *h, const void *a,
                             const void *b, const void *B, const void *C, const float *D,
                             const float *x0, void *y, float *x_final, float *ckpt, void *ws,

@@ -182,6 +182,22 @@ struct BwdArgs {
 
 hipError_t launch_fwd(const FwdArgs &g, hipStream_t stream);
 hipError_t launch_fwd_mfma(const FwdArgs &g, hipStream_t stream);  // bf16, d_state 16
+
+// one-token step with the state (and, for the block, the conv window) in place
+struct StepArgs {
+    int io, N;
+    bool block;
+    int64_t Bt, Di;
+    float scale;
+    const void *hu, *a, *b, *B, *C;  // [Bt][Di] / [Bt][N]
+    const float *D;
+    const void *z;
+    const float *conv_w;
+    void *conv_state;  // [Bt][3][Di], shifted by one token
+    float *x;          // [Bt][Di][N], updated
+    void *y;           // [Bt][Di]
+};
+hipError_t launch_step(const StepArgs &g, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs &g, hipStream_t stream);
 hipError_t launch_bwd_mfma(const BwdArgs &g, hipStream_t stream);  // bf16, d_state 16
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);

@@ -101,6 +101,28 @@ def test_validation_errors_block(lib):
     assert "du is NULL" in nb.last_error()
 
 
+def test_validation_errors_step(lib):
+    d = dims()
+    v = [FAKE] * 9  # h, a, b, B, C, D, x, y, stream
+    v[-1] = None
+    vx = list(v)
+    vx[6] = None  # x
+    assert lib.naju_scan_step(ctypes.byref(d), *vx) == nb.EINVAL
+    assert "x is NULL" in nb.last_error()
+    vx[6] = FAKE + 4  # x must be 16-byte aligned (float4 state rows)
+    assert lib.naju_scan_step(ctypes.byref(d), *vx) == nb.EINVAL
+    assert "aligned" in nb.last_error()
+    assert lib.naju_scan_step(ctypes.byref(dims(d_state=32)), *vx) == nb.EUNSUPPORTED
+    assert lib.naju_scan_step(ctypes.byref(dims(batch=70000)), *v) == nb.EINVAL
+    assert lib.naju_scan_step(ctypes.byref(dims(batch=0)), *([None] * 9)) == nb.OK
+    vb = [FAKE] * 12  # u, z, conv_w, conv_state, a, b, B, C, D, x, y, stream
+    vb[-1] = None
+    vb[3] = None  # conv_state is required (it is updated in place)
+    assert lib.naju_block_step(ctypes.byref(d), *vb) == nb.EINVAL
+    assert "conv_state is NULL" in nb.last_error()
+    assert lib.naju_block_step(ctypes.byref(dims(d_conv=3)), *vb) == nb.EUNSUPPORTED
+
+
 def test_workspace_and_ckpt_sizes(lib):
     d = dims(batch=8, seqlen=2048, d_inner=1536)
     for op in range(4):
