@@ -88,18 +88,24 @@ def main():
     from selective_state_space_naju_amd import inputs
 
     dev = torch.device("cuda:0")
-    if args.only == "copy":
-        nbytes = 1 << 30
+    def plain_copy(nbytes, warmup, steps):
+        """A plain device copy of nbytes (the HIP runtime's copy kernel): seconds per copy."""
         src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             dst.copy_(src)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(steps):
             dst.copy_(src)
         torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / args.steps
+        dt = (time.perf_counter() - t0) / steps
+        del src, dst
+        return dt
+
+    if args.only == "copy":
+        nbytes = 1 << 30
+        dt = plain_copy(nbytes, args.warmup, args.steps)
         print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
                           "ms": round(dt * 1e3, 4), "GB_per_s": round(2 * nbytes / dt / 1e9, 1)}))
         return
@@ -282,6 +288,14 @@ def main():
                "sample": "block fwd+bwd of the whole workload (%d x %d tokens x %d channels, "
                          "d_state %d), fp64, %.2f s wall on %d threads" % (Bt, L, Di, N, tc, cores)}
 
+    # the practical HBM ceiling on this machine: a plain 1 GiB device copy (read + write)
+    copy_ceiling = None
+    if args.only == "all":
+        dt = plain_copy(1 << 30, 3, 10)
+        copy_ceiling = {"what": "plain 1 GiB device copy (HIP runtime copy kernel), read + write",
+                        "GB_per_s": round(2 * (1 << 30) / dt / 1e9, 1),
+                        "frac_of_peak": round(2 * (1 << 30) / dt / 1e9 / HBM_PEAK_GBS, 4)}
+
     out = {
         "metric": METRIC,
         "value": round(tokens / t_step, 1) if t_step == t_step else None,
@@ -301,6 +315,7 @@ def main():
         "roofline": rf,
         "roofline_scan_fwd": rf_scan,
         "cpu_baseline": cpu,
+        "hbm_copy_ceiling": copy_ceiling,
         "parts": parts,
     }
     print(json.dumps(out), flush=True)
