@@ -672,7 +672,9 @@ static bool use_bwd_mfma(const BwdArgs &g)
         const char *v = getenv("NAJU_BWD_VARIANT");
         return v && v[0] == 'r' && v[1] == 'r';
     }();
-    if (forced_rr || g.io != 1 || g.N != 16 || ((uintptr_t)g.B % 16) != 0 ||
+    // (the carry pass loads channel pairs as 4-byte words: whole 8-channel groups,
+    // as in the forward's matrix-core path)
+    if (forced_rr || g.io != 1 || g.N != 16 || g.Di % 8 != 0 || ((uintptr_t)g.B % 16) != 0 ||
         ((uintptr_t)g.C % 16) != 0)
         return false;
     // buffer ranges of 32 token rows and 32-bit fix-list keys

@@ -649,8 +649,11 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
 // The adjoint crossing a chunk boundary only needs, per 128-token chunk of a
 // 32-channel tile, the chunk's reverse carry  mu_out = Q mu_in + R  with
 // Q = P_last (per channel) and R = Gp^T C / sqrt(N) (per channel and state).
-// Four waves compute their 32-token carries with the same products as the
+// A workgroup takes 64 channels (two tiles, whole 128-byte rows) of one chunk;
+// its four waves compute their 32-token carries with the same products as the
 // gradient kernel and compose them (the adjoint passes the later waves first).
+// Lane (col, h) holds the channel pair 64p + 2 col, 64p + 2 col + 1 (one 4-byte
+// load per token and tensor); MFMA column tile j takes the channels 64p + 2 col + j.
 template <bool BLOCK>
 __global__ __launch_bounds__(64 * kTW) void bwd_carry_kernel(
     const int64_t Bt, const int64_t L, const int64_t Di, const int n_tiles, const int n_chunks,
@@ -663,24 +666,19 @@ __global__ __launch_bounds__(64 * kTW) void bwd_carry_kernel(
     const int col = lane & 31;
     const int hh = lane >> 5;
     const bool upper = hh != 0;
-    __shared__ float sQ[kTW][32];
-    __shared__ float sR[kTW][16][32];
+    __shared__ float sQ[kTW][2][32];
+    __shared__ float sR[kTW][2][16][32];
 
-    uint32_t pr;
-    int hf;
-    pair_of(blockIdx.x, pr, hf);
-    const uint32_t n_tp = (uint32_t)(n_tiles + 1) / 2;  // tile pairs
-    if (pr >= (uint32_t)Bt * (uint32_t)n_chunks * n_tp) return;
-    const int tile = (int)(pr % n_tp) * 2 + hf;
-    if (tile >= n_tiles) return;
-    const int chunk = (int)((pr / n_tp) % (uint32_t)n_chunks);
-    const int bi = (int)(pr / n_tp / (uint32_t)n_chunks);
+    const int n_pairs = (n_tiles + 1) / 2;  // 64-channel groups
+    const int pr = (int)(blockIdx.x % (uint32_t)n_pairs);
+    const int chunk = (int)((blockIdx.x / (uint32_t)n_pairs) % (uint32_t)n_chunks);
+    const int bi = (int)(blockIdx.x / (uint32_t)n_pairs / (uint32_t)n_chunks);
     const int64_t n0 = (int64_t)chunk * (kTW * T) + (int64_t)tw * T;
     const bool active = n0 < L;
     const int Lw = active ? (int)(L - n0 < T ? L - n0 : T) : 0;
     const int64_t tokbase = (int64_t)bi * L;
-    const int64_t c = (int64_t)tile * 32 + col;
-    const bool valid = c < Di;
+    const int64_t c0 = (int64_t)pr * 64 + 2 * col;  // channel of column tile j: c0 + j
+    const bool valid = c0 < Di;                      // Di is even: both or neither
     auto tok = [&](int i) -> int { return 8 * (i >> 2) + 4 * hh + (i & 3); };
 
     bf16x8 Csv[2];
@@ -692,77 +690,94 @@ __global__ __launch_bounds__(64 * kTW) void bwd_carry_kernel(
             Csv[i >> 3][i & 7] = (__bf16)(ldb(rC, o) * scale);
         }
     }
-    const int64_t ebase = (tokbase + (active ? n0 : 0)) * Di + (int64_t)tile * 32;
+    const int64_t ebase = (tokbase + (active ? n0 : 0)) * Di + (int64_t)pr * 64;
     const uint32_t row2 = (uint32_t)Di * 2;
     uint32_t vr[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) vr[r] = valid ? (uint32_t)((4 * hh + r) * Di + col) * 2 : kOOB;
-    auto LD = [&](const bf16 *t, int i) -> float {
-        return ldb(make_rsrc(t + ebase, (uint32_t)Lw * row2), vr[i & 3], (uint32_t)(8 * (i >> 2)) * row2);
+    for (int r = 0; r < 4; ++r) vr[r] = valid ? (uint32_t)((4 * hh + r) * Di + 2 * col) * 2 : kOOB;
+    // the two channels of slot i as one 4-byte load
+    auto LD2 = [&](const bf16 *t, int i) -> uint32_t {
+        return __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(t + ebase, (uint32_t)Lw * row2),
+                                                    vr[i & 3], (uint32_t)(8 * (i >> 2)) * row2, 0);
     };
-    float invf[16], g[16];
+    float invf[2][16], g[2][16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const float av = LD(a, i);
-        float dv = LD(dy, i);
-        // tokens past the end keep the state (f = 1)
-        invf[i] = 1.f + (tok(i) < Lw ? ex2(-av * kLog2e) : 0.f);
-        if (BLOCK) {
-            const float zv = LD(z, i);
-            dv *= zv * rcp(1.f + ex2(-zv * kLog2e));  // dy SiLU(z)
+        const uint32_t av = LD2(a, i), dv = LD2(dy, i);
+        uint32_t zv = 0;
+        if (BLOCK) zv = LD2(z, i);
+        const bool tv = tok(i) < Lw;  // tokens past the end keep the state (f = 1)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const float aj = __uint_as_float(j ? (av & 0xffff0000u) : (av << 16));
+            float dj = __uint_as_float(j ? (dv & 0xffff0000u) : (dv << 16));
+            invf[j][i] = 1.f + (tv ? ex2(-aj * kLog2e) : 0.f);
+            if (BLOCK) {
+                const float zj = __uint_as_float(j ? (zv & 0xffff0000u) : (zv << 16));
+                dj *= zj * rcp(1.f + ex2(-zj * kLog2e));  // dy SiLU(z)
+            }
+            g[j][i] = dj;
         }
-        g[i] = dv;
     }
-    float tot[4], cum[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        float run = 1.f;
+    for (int j = 0; j < 2; ++j) {
+        float tot[4], cum[16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            run *= invf[4 * q + r];
-            cum[4 * q + r] = run;
+        for (int q = 0; q < 4; ++q) {
+            float run = 1.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                run *= invf[j][4 * q + r];
+                cum[4 * q + r] = run;
+            }
+            tot[q] = run;
         }
-        tot[q] = run;
-    }
-    float E[4], acc = 1.f;
+        float E[4], acc = 1.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const float pt = xhalf(tot[q], upper);
-        E[q] = upper ? acc * pt : acc;
-        acc *= tot[q] * pt;
-    }
-    bf16x8 GpH[2], GpL[2];
+        for (int q = 0; q < 4; ++q) {
+            const float pt = xhalf(tot[q], upper);
+            E[q] = upper ? acc * pt : acc;
+            acc *= tot[q] * pt;
+        }
+        bf16x8 GpH[2], GpL[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        __bf16 hi, lo;
-        split2(g[i] * rcp(E[i >> 2] * cum[i]), hi, lo);
-        GpH[i >> 3][i & 7] = hi;
-        GpL[i >> 3][i & 7] = lo;
-    }
-    f32x16 r = {};
+        for (int i = 0; i < 16; ++i) {
+            __bf16 hi, lo;
+            split2(g[j][i] * rcp(E[i >> 2] * cum[i]), hi, lo);
+            GpH[i >> 3][i & 7] = hi;
+            GpL[i >> 3][i & 7] = lo;
+        }
+        f32x16 r = {};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        r = mma(Csv[kb], GpH[kb], r);  // rows: state, columns: channel
-        r = mma(Csv[kb], GpL[kb], r);
-    }
+        for (int kb = 0; kb < 2; ++kb) {
+            r = mma(Csv[kb], GpH[kb], r);  // rows: state, columns: channel
+            r = mma(Csv[kb], GpL[kb], r);
+        }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sR[tw][tok(i)][col] = r[i];
-    if (upper) sQ[tw][col] = rcp(E[3] * cum[15]);
+        for (int i = 0; i < 8; ++i) sR[tw][j][tok(i)][col] = r[i];
+        if (upper) sQ[tw][j][col] = rcp(E[3] * cum[15]);
+    }
     __syncthreads();
-    if (tw == 0) {
-        float Qt = 1.f, Rt[8];
+    if (tw == 0 && valid) {
+        // lane (col, h) composes states 8h..8h+7 of its two channels
 #pragma unroll
-        for (int k = 0; k < 8; ++k) Rt[k] = 0.f;
-        for (int w = kTW - 1; w >= 0; --w) {
-            const float qw = sQ[w][col];
+        for (int j = 0; j < 2; ++j) {
+            float Qt = 1.f, Rt[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) Rt[k] = fmaf(qw, Rt[k], sR[w][8 * hh + k][col]);
-            Qt *= qw;
+            for (int k = 0; k < 8; ++k) Rt[k] = 0.f;
+            for (int w = kTW - 1; w >= 0; --w) {
+                const float qw = sQ[w][j][col];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) Rt[k] = fmaf(qw, Rt[k], sR[w][j][8 * hh + k][col]);
+                Qt *= qw;
+            }
+            const int64_t ch = c0 + j;  // its 32-channel tile and column there
+            const int tile = (int)(ch >> 5), cc = (int)(ch & 31);
+            float *ag = agg + (((size_t)bi * n_tiles + tile) * n_chunks + chunk) * (17 * 32);
+            if (!upper) ag[cc] = Qt;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) ag[(1 + 8 * hh + k) * 32 + cc] = Rt[k];
         }
-        float *ag = agg + (((size_t)bi * n_tiles + tile) * n_chunks + chunk) * (17 * 32);
-        if (!upper) ag[col] = Qt;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) ag[(1 + 8 * hh + k) * 32 + col] = Rt[k];
     }
 }
 
@@ -1016,8 +1031,8 @@ static hipError_t launch_bwd_mfma_t(const BwdArgs &g, hipStream_t stream)
     uint32_t *flist = (uint32_t *)(ws + pl.off_fixlist);
     float *fmu = (float *)(ws + pl.off_fixmu);
     hipError_t e;
-    const int64_t k1_pairs = g.Bt * m.n_chunks * ((m.n_tiles + 1) / 2);
-    hipLaunchKernelGGL((bwd_carry_kernel<BLOCK>), dim3((unsigned)(16 * ((k1_pairs + 7) / 8))),
+    const int64_t k1_wgs = g.Bt * m.n_chunks * ((m.n_tiles + 1) / 2);
+    hipLaunchKernelGGL((bwd_carry_kernel<BLOCK>), dim3((unsigned)k1_wgs),
                        dim3(64 * kTW), 0, stream, g.Bt, g.L, g.Di, m.n_tiles, m.n_chunks, g.scale,
                        (const bf16 *)g.a, (const bf16 *)g.C, (const bf16 *)g.z, (const bf16 *)g.dy,
                        agg);
