@@ -331,13 +331,15 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
         half2_t hd2[8];
         bf16x8 WB[2];
         {
-            float uv[16];
+            float uv[16], bv[16];
+            // every load issued before any is used (one round trip, not one per token)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 if (!BLOCK) uv[i] = LD(hu, i);
-                const float bv = LD(bg, i);
-                ib[i] = rcp(1.f + ex2(-bv * kLog2e));
+                bv[i] = LD(bg, i);
             }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ib[i] = rcp(1.f + ex2(-bv[i] * kLog2e));
             if (BLOCK) fill_window();
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
