@@ -39,6 +39,16 @@ __device__ __forceinline__ void sigm2(float v, float &sp, float &sm) {
     sm = (e < __builtin_huge_valf()) ? e * sp : 1.f;
 }
 
+// Sum over the 4 lanes of each aligned quad (lanes 4k..4k+3), in every lane:
+// two DPP quad permutes (xor 1, then xor 2), no LDS round trip.
+__device__ __forceinline__ float quad_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
+                                                            0xF, 0xF, false));  // [1,0,3,2]
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E,
+                                                            0xF, 0xF, false));  // [2,3,0,1]
+    return v;
+}
+
 // ------------------------------------------------- cross-workgroup traffic
 // Stores/loads with agent scope bypass the non-coherent caches (sc1 on
 // gfx950), so a value published by one workgroup is visible to workgroups on

@@ -30,7 +30,36 @@
 
 namespace naju {
 
-template <typename IO, int N, bool BLOCK, int T, int W>
+namespace {
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+// 16 bytes per lane HBM -> LDS through a buffer descriptor (zeros past its
+// range): lane i copies bytes voff + soff of r to lds + 16 i.  Issued through
+// inline assembly, so the compiler's memory-counter bookkeeping does not see
+// it; the caller waits (vmcnt(0)) before reading the copy.  M0 holds the LDS
+// address; the compiler does not use M0 in this kernel.
+__device__ __forceinline__ void dma16b(rsrc_t r, uint32_t voff, uint32_t soff, const void *lds)
+{
+    const uint32_t la = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)lds);
+    // (the row offset joins the lane offset: a constant soffset operand would be
+    // emitted as a literal, which the instruction does not accept)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                 :
+                 : "v"(voff + soff), "s"(r), "s"(la)
+                 : "memory", "m0");
+}
+}  // namespace
+
+// STG (bf16, d_state 64, d_inner % 8 == 0): each wave first copies its own
+// 32 tokens of h|u, a, b (and z), B and C into a private LDS region with a few
+// 16-byte-per-lane copies and one wait, instead of two dependent round trips
+// to memory per token (the per-token loads of a lane are a handful of bytes).
+template <typename IO, int N, bool BLOCK, int T, int W, bool STG = false>
 __global__ __launch_bounds__(64 * W) void fwd_kernel(
     const int64_t Bt, const int64_t L, const int64_t Di, const int n_tiles, const int n_chunks,
     const float scale, const IO *__restrict__ hu, const IO *__restrict__ a,
@@ -43,8 +72,14 @@ __global__ __launch_bounds__(64 * W) void fwd_kernel(
     constexpr int LPC = N / 16;   // lanes per channel
     constexpr int CPW = 64 / LPC; // channels per wave
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    // wave-uniform (readfirstlane keeps what derives from it, such as the staging
+    // copies' buffer descriptors, in scalar registers)
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
+    // per-wave staging (STG): [tok][16 ch] for h|u, a, b, z, then [tok][N] for B and C
+    constexpr int kCh = 64 / LPC;
+    constexpr int kStg = STG ? (4 * T * kCh + 2 * T * N) : 8;
+    __shared__ __attribute__((aligned(16))) IO sStg[STG ? W : 1][kStg];
     __shared__ uint32_t s_ticket, s_epoch;
     __shared__ float sP[W][64];
     __shared__ float sS[W][16][64];
@@ -68,6 +103,32 @@ __global__ __launch_bounds__(64 * W) void fwd_kernel(
     const bool valid = c < Di;
     const int64_t n0 = (int64_t)chunk * (W * T) + (int64_t)wv * T;
     const float Dc = valid ? D[c] : 0.f;
+    IO *stg = sStg[STG ? wv : 0];
+    if constexpr (STG) {
+        static_assert(sizeof(IO) == 2 && N == 64 && T == 32, "staging layout");
+        // [tok][16 ch] blocks: lane = (row lane/2, 8-channel half lane%2); the range
+        // ends with the wave's last valid token (rows past it read 0)
+        const int rows = n0 < L ? (int)(L - n0 < T ? L - n0 : T) : 0;
+        const int64_t eb = ((int64_t)bi * L + (n0 < L ? n0 : 0)) * Di + (int64_t)tile * kCh;
+        const uint32_t rng = (uint32_t)rows * (uint32_t)Di * 2 - (uint32_t)tile * kCh * 2;
+        const uint32_t vo = ((uint32_t)(lane >> 1) * (uint32_t)Di + 8 * (lane & 1)) * 2;
+        dma16b(make_rsrc(hu + eb, rows ? rng : 0u), vo, 0u, stg);
+        dma16b(make_rsrc(a + eb, rows ? rng : 0u), vo, 0u, stg + T * kCh);
+        dma16b(make_rsrc(bg + eb, rows ? rng : 0u), vo, 0u, stg + 2 * T * kCh);
+        if (BLOCK) dma16b(make_rsrc(z + eb, rows ? rng : 0u), vo, 0u, stg + 3 * T * kCh);
+        // B, C rows: [tok][N], 8 rows per copy (lane = row lane/8, chunk lane%8)
+        const int64_t tb = ((int64_t)bi * L + (n0 < L ? n0 : 0)) * N;
+        const uint32_t vb = ((uint32_t)(lane >> 3) * N + 8 * (lane & 7)) * 2;
+        const rsrc_t rB = make_rsrc(Bm + tb, (uint32_t)rows * N * 2);
+        const rsrc_t rC = make_rsrc(Cm + tb, (uint32_t)rows * N * 2);
+#pragma unroll
+        for (int k = 0; k < T / 8; ++k) {
+            dma16b(rB, vb, (uint32_t)(8 * k * N * 2), stg + 4 * T * kCh + 8 * k * N);
+            dma16b(rC, vb, (uint32_t)(8 * k * N * 2), stg + 4 * T * kCh + T * N + 8 * k * N);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    const int cl = lane / LPC;  // this lane's channel inside the tile
 
     // ---------------------------------------------------------- block front end
     float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f, um1 = 0.f, um2 = 0.f, um3 = 0.f;
@@ -109,33 +170,32 @@ __global__ __launch_bounds__(64 * W) void fwd_kernel(
             const int64_t t = ((int64_t)bi * L + n) * Di + c;
             float av = 0.f, bv = 0.f, hv = 0.f;
             if (valid) {
-                av = to_f(a[t]);
-                bv = to_f(bg[t]);
+                av = to_f(STG ? stg[T * kCh + j * kCh + cl] : a[t]);
+                bv = to_f(STG ? stg[2 * T * kCh + j * kCh + cl] : bg[t]);
                 if constexpr (BLOCK) {
-                    const float uv = to_f(hu[t]);
+                    const float uv = to_f(STG ? stg[j * kCh + cl] : hu[t]);
                     const float pre = w0 * um3 + w1 * um2 + w2 * um1 + w3 * uv;
                     um3 = um2;
                     um2 = um1;
                     um1 = uv;
                     hv = pre * sigm(pre);
                 } else {
-                    hv = to_f(hu[t]);
+                    hv = to_f(STG ? stg[j * kCh + cl] : hu[t]);
                 }
             }
             const float f = sigm(av);
             const float wr = sigm(bv) * hv;
-            const IO *Bn = Bm + ((int64_t)bi * L + n) * N + sg * 16;
-            const IO *Cn = Cm + ((int64_t)bi * L + n) * N + sg * 16;
+            const IO *Bn = STG ? stg + 4 * T * kCh + j * N + sg * 16
+                               : Bm + ((int64_t)bi * L + n) * N + sg * 16;
+            const IO *Cn = STG ? stg + 4 * T * kCh + T * N + j * N + sg * 16
+                               : Cm + ((int64_t)bi * L + n) * N + sg * 16;
             float acc = 0.f;
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
                 x[s] = fmaf(f, x[s], wr * to_f(Bn[s]));
                 acc = fmaf(x[s], to_f(Cn[s]), acc);
             }
-            if constexpr (LPC > 1) {
-                acc += __shfl_xor(acc, 1);
-                acc += __shfl_xor(acc, 2);
-            }
+            if constexpr (LPC > 1) acc = quad_sum(acc);  // the channel's 4 lanes
             P *= f;
             ysl[j] = fmaf(scale, acc, Dc * hv);
             Pn[j] = P;
@@ -256,19 +316,17 @@ __global__ __launch_bounds__(64 * W) void fwd_kernel(
         for (int j = 0; j < T; ++j) {
             const int64_t n = n0 + j;
             if (n < L) {
-                const IO *Cn = Cm + ((int64_t)bi * L + n) * N + sg * 16;
+                const IO *Cn = STG ? stg + 4 * T * kCh + T * N + j * N + sg * 16
+                                   : Cm + ((int64_t)bi * L + n) * N + sg * 16;
                 float dot = 0.f;
 #pragma unroll
                 for (int s = 0; s < 16; ++s) dot = fmaf(xin[s], to_f(Cn[s]), dot);
-                if constexpr (LPC > 1) {
-                    dot += __shfl_xor(dot, 1);
-                    dot += __shfl_xor(dot, 2);
-                }
+                if constexpr (LPC > 1) dot = quad_sum(dot);
                 float yv = fmaf(scale * Pn[j], dot, ysl[j]);
                 const int64_t t = ((int64_t)bi * L + n) * Di + c;
                 if (valid && sg == 0) {
                     if constexpr (BLOCK) {
-                        const float zv = to_f(z[t]);
+                        const float zv = to_f(STG ? stg[3 * T * kCh + j * kCh + cl] : z[t]);
                         yv *= zv * sigm(zv);
                     }
                     y[t] = from_f<IO>(yv);
@@ -291,7 +349,7 @@ __global__ __launch_bounds__(64 * W) void fwd_kernel(
 }
 
 // ---------------------------------------------------------------- launcher
-template <typename IO, int N, bool BLOCK>
+template <typename IO, int N, bool BLOCK, bool STG = false>
 static hipError_t launch_fwd_t(const FwdArgs &g, hipStream_t stream)
 {
     constexpr int T = kFwdT, W = kFwdW;
@@ -300,7 +358,7 @@ static hipError_t launch_fwd_t(const FwdArgs &g, hipStream_t stream)
     uint32_t *flags = (uint32_t *)((char *)g.ws + pl.off_flags);
     float *agg = (float *)((char *)g.ws + pl.off_agg);
     float *incl = (float *)((char *)g.ws + pl.off_incl);
-    hipLaunchKernelGGL((fwd_kernel<IO, N, BLOCK, T, W>), dim3(pl.n_wg), dim3(64 * W), 0, stream,
+    hipLaunchKernelGGL((fwd_kernel<IO, N, BLOCK, T, W, STG>), dim3(pl.n_wg), dim3(64 * W), 0, stream,
                        g.Bt, g.L, g.Di, pl.n_tiles, pl.n_chunks, g.scale, (const IO *)g.hu,
                        (const IO *)g.a, (const IO *)g.b, (const IO *)g.B, (const IO *)g.C, g.D,
                        g.x0, (const IO *)g.z, g.conv_w, (const IO *)g.conv_state, (IO *)g.y,
@@ -333,6 +391,11 @@ hipError_t launch_fwd(const FwdArgs &g, hipStream_t stream)
     }
     if (g.N == 16) return g.block ? launch_fwd_t<bf16, 16, true>(g, stream)
                                   : launch_fwd_t<bf16, 16, false>(g, stream);
+    const bool stg = g.Di % 8 == 0 && g.Di < ((int64_t)1 << 24) && ((uintptr_t)g.B % 16) == 0 &&
+                     ((uintptr_t)g.C % 16) == 0;
+    if (stg)
+        return g.block ? launch_fwd_t<bf16, 64, true, true>(g, stream)
+                       : launch_fwd_t<bf16, 64, false, true>(g, stream);
     return g.block ? launch_fwd_t<bf16, 64, true>(g, stream)
                    : launch_fwd_t<bf16, 64, false>(g, stream);
 }

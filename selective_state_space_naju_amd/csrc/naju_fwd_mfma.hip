@@ -261,9 +261,11 @@ __device__ __forceinline__ void dma16b(rsrc_t r, uint32_t voff, uint32_t soff, c
 {
     const uint32_t la = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)lds);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen nt lds"
+    // (the row offset joins the lane offset: a constant soffset operand would be
+    // emitted as a literal, which the instruction does not accept)
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
                  :
-                 : "v"(voff), "s"(r), "s"(la), "s"(soff)
+                 : "v"(voff + soff), "s"(r), "s"(la)
                  : "memory", "m0");
 }
 }  // namespace
