@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnaju.so")
-SOURCES = ["naju_api.hip", "naju_fwd.hip", "naju_fwd_mfma.hip", "naju_bwd.hip", "naju_bwd_mfma.hip",
+SOURCES = ["naju_api.hip", "naju_fwd.hip", "naju_fwd_mfma.hip", "naju_fwd_mfma64.hip", "naju_bwd.hip",
+           "naju_bwd_mfma.hip",
            "naju_step.hip"]
 ARCH = os.environ.get("NAJU_OFFLOAD_ARCH", "gfx950")
 

@@ -27,33 +27,9 @@
 
 #include "naju_device.h"
 #include "naju_launch.h"
+#include "naju_mfma.h"
 
 namespace naju {
-
-namespace {
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
-                                             0x00020000);
-}
-// 16 bytes per lane HBM -> LDS through a buffer descriptor (zeros past its
-// range): lane i copies bytes voff + soff of r to lds + 16 i.  Issued through
-// inline assembly, so the compiler's memory-counter bookkeeping does not see
-// it; the caller waits (vmcnt(0)) before reading the copy.  M0 holds the LDS
-// address; the compiler does not use M0 in this kernel.
-__device__ __forceinline__ void dma16b(rsrc_t r, uint32_t voff, uint32_t soff, const void *lds)
-{
-    const uint32_t la = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)lds);
-    // (the row offset joins the lane offset: a constant soffset operand would be
-    // emitted as a literal, which the instruction does not accept)
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
-                 :
-                 : "v"(voff + soff), "s"(r), "s"(la)
-                 : "memory", "m0");
-}
-}  // namespace
 
 // STG (bf16, d_state 64, d_inner % 8 == 0): each wave first copies its own
 // 32 tokens of h|u, a, b (and z), B and C into a private LDS region with a few
@@ -366,17 +342,23 @@ static hipError_t launch_fwd_t(const FwdArgs &g, hipStream_t stream)
     return hipGetLastError();
 }
 
-// The matrix-core variant serves bf16 activations with d_state 16 when B and
-// C allow 16-byte loads; NAJU_FWD_VARIANT=rr forces the register recurrence.
+// The matrix-core variants serve bf16 activations (d_state 16; d_state 64 when
+// its rows fill the device) when the operands allow 16-byte loads;
+// NAJU_FWD_VARIANT=rr forces the register recurrence.
+static bool forced_rr()
+{
+    static const bool v = [] {
+        const char *e = getenv("NAJU_FWD_VARIANT");
+        return e && e[0] == 'r' && e[1] == 'r';
+    }();
+    return v;
+}
+
 static bool use_mfma(const FwdArgs &g)
 {
-    static const bool forced_rr = [] {
-        const char *v = getenv("NAJU_FWD_VARIANT");
-        return v && v[0] == 'r' && v[1] == 'r';
-    }();
     const auto al16 = [](const void *p) { return ((uintptr_t)p % 16) == 0; };
     // (buffer ranges of 32 token rows / 16 checkpoint rows stay below 2^31 bytes)
-    return !forced_rr && g.io == 1 && g.N == 16 && g.Di % 8 == 0 && g.Di < ((int64_t)1 << 24) &&
+    return !forced_rr() && g.io == 1 && g.N == 16 && g.Di % 8 == 0 && g.Di < ((int64_t)1 << 24) &&
            al16(g.B) && al16(g.C) && al16(g.hu) && al16(g.a) && al16(g.b);
 }
 
@@ -391,6 +373,7 @@ hipError_t launch_fwd(const FwdArgs &g, hipStream_t stream)
     }
     if (g.N == 16) return g.block ? launch_fwd_t<bf16, 16, true>(g, stream)
                                   : launch_fwd_t<bf16, 16, false>(g, stream);
+    if (!forced_rr() && use_fwd_mfma64(g)) return launch_fwd_mfma64(g, stream);
     const bool stg = g.Di % 8 == 0 && g.Di < ((int64_t)1 << 24) && ((uintptr_t)g.B % 16) == 0 &&
                      ((uintptr_t)g.C % 16) == 0;
     if (stg)

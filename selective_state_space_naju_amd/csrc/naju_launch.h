@@ -182,6 +182,9 @@ struct BwdArgs {
 
 hipError_t launch_fwd(const FwdArgs &g, hipStream_t stream);
 hipError_t launch_fwd_mfma(const FwdArgs &g, hipStream_t stream);  // bf16, d_state 16
+bool use_fwd_mfma64(const FwdArgs &g);                              // bf16, d_state 64
+hipError_t launch_fwd_mfma64(const FwdArgs &g, hipStream_t stream);
+int device_cu_count();  // compute units of the current device (cached)
 
 // one-token step with the state (and, for the block, the conv window) in place
 struct StepArgs {

@@ -43,6 +43,9 @@ SMALL = [
     # bf16, d_state 64, d_inner % 8 == 0: the staged register forward (a ragged
     # 16-channel tile, a partial last chunk)
     (2, 333, 72, 64, "bf16"),
+    # bf16, d_state 64 with at least 32 rows of 32 channels: the matrix-core
+    # forward (a ragged last tile, a partial last chunk with an idle wave)
+    (2, 333, 1000, 64, "bf16"),
 ]
 
 
@@ -219,17 +222,44 @@ def test_repeat_runs_agree_and_workspace_clean():
 
 
 @pytest.mark.parametrize("block", [False, True], ids=["scan", "block"])
-def test_bf16_fallback_chunks(block):
-    """bf16 / d_state 16 runs on the matrix-core path; chunks whose prod(1/f) leaves
-    the safe range (a = -inf, or a drawn wide so f is often tiny) or that hold a NaN
-    gate are recomputed by the register recurrence.  Both kinds mix in one call."""
-    Bt, L, Di, N = 2, 700, 160, 16
+def test_mfma64_rows_beyond_grid(block):
+    """d_state 64 matrix-core forward with more (batch row, 32-channel tile) rows
+    than resident workgroups, so workgroups walk a second row: the carried state,
+    per-channel constants and conv window restart at each row."""
+    Bt, L, Di, N = (3, 200, 5600, 64) if not block else (2, 130, 8200, 64)
+    d = inputs.draw(Bt, L, Di, N, io="bf16", seed=21, x0=True, block=block, conv_state=block)
+    print("mfma64 rows", block, flush=True)
+    D, x0 = f32_dev(d["D"]), f32_dev(d["x0"])
+    if block:
+        yo, xfo, cso = oracle.block_fwd(d["u"], d["z"], d["conv_w"], d["a"], d["b"], d["B"],
+                                        d["C"], d["D"], d["x0"], d["conv_state"])
+        t = {k: to_dev(d[k], "bf16") for k in ("u", "z", "a", "b", "B", "C", "conv_state")}
+        y, xf, cs = nb.block_fwd(t["u"], t["z"], f32_dev(d["conv_w"]), t["a"], t["b"], t["B"],
+                                 t["C"], D, x0, t["conv_state"])
+        torch.cuda.synchronize()
+        assert np.array_equal(host(cs), cso)
+    else:
+        yo, xfo = oracle.scan_fwd(d["h"], d["a"], d["b"], d["B"], d["C"], d["D"], d["x0"])
+        t = {k: to_dev(d[k], "bf16") for k in ("h", "a", "b", "B", "C")}
+        y, xf = nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], D, x0)
+        torch.cuda.synchronize()
+    assert_close("y", host(y), yo, TOL["bf16"])
+    assert_close("x_final", host(xf), xfo, TOL["bf16"])
+
+
+@pytest.mark.parametrize("N", [16, 64])
+@pytest.mark.parametrize("block", [False, True], ids=["scan", "block"])
+def test_bf16_fallback_chunks(block, N):
+    """bf16 runs on the matrix-core paths; chunks whose prod(1/f) leaves the safe
+    range (a = -inf, or a drawn wide so f is often tiny) or that hold a NaN gate
+    are recomputed by the register recurrence.  Both kinds mix in one call."""
+    Bt, L, Di = (2, 700, 160) if N == 16 else (2, 400, 512)
     d = inputs.draw(Bt, L, Di, N, io="bf16", seed=19, x0=True, block=block, conv_state=block)
     d["a"][0, 100, :10] = -np.inf                      # f = 0: full reset
     d["a"][1, 300:364, 64:] = inputs.bf16_round(       # wide gates: prod(1/f) overflows
         (np.random.default_rng(3).standard_normal((64, Di - 64)) * 6 - 6).astype(np.float32))
-    d["a"][1, 500, 5] = np.nan
-    print("fallback", block, flush=True)
+    d["a"][1, min(500, L - 1), 5] = np.nan
+    print("fallback", block, N, flush=True)
     hk = "u" if block else "h"
     t = {k: to_dev(d[k], "bf16") for k in (hk, "a", "b", "B", "C") + (("z", "conv_state") if block else ())}
     D, x0 = f32_dev(d["D"]), f32_dev(d["x0"])
