@@ -14,9 +14,9 @@
 // Decomposition.  A workgroup (four waves, 32 tokens each) owns one row
 // (batch row, 32-channel tile) at a time and walks its 128-token chunks in
 // order, so the state entering a chunk is the one its own previous chunk left:
-// no cross-workgroup look-back and no workspace.  Waves 0 and 1 carry that
-// state in registers (lane = channel, 16 states) and compose it with the four
-// waves' chunk aggregates through LDS.  A wave whose chunk cannot take the
+// no cross-workgroup look-back and no workspace.  The four waves carry that
+// state in registers (wave w: states 16 w .. 16 w + 15 of the 32 channels) and
+// compose it with the waves' chunk aggregates through LDS.  A wave whose chunk cannot take the
 // rescaled form (prod 1/f beyond 2^64, a non-finite gate or h) runs the plain
 // register recurrence for it instead.  The host uses this kernel when the
 // rows alone fill the device (Bt * d_inner / 32 at least a few dozen).
@@ -173,7 +173,7 @@ __device__ void rr64_output(int64_t L, int64_t Di, int bi, int64_t c, bool valid
 template <bool BLOCK>
 __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
     const int64_t Bt, const int64_t L, const int64_t Di, const int n_tiles, const int n_chunks,
-    const float scale, const bf16 *__restrict__ hu, const bf16 *__restrict__ a,
+    const int n_slots, const float scale, const bf16 *__restrict__ hu, const bf16 *__restrict__ a,
     const bf16 *__restrict__ bg, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
     const float *__restrict__ D, const float *__restrict__ x0, const bf16 *__restrict__ z,
     const float *__restrict__ conv_w, const bf16 *__restrict__ conv_state, bf16 *__restrict__ y,
@@ -194,13 +194,15 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
     const uint32_t rowb = (uint32_t)Di * 2;
 
     // Copy the h|u, a, b tile and the B rows of chunk ch of row `row` into LDS
-    // (waves 2 and 3, 64 token rows each; wave 2 also the 16 rows of u before
+    // (every wave its own 32 token rows; wave 0 also the 16 rows of u before
     // the chunk).  A 32-channel row is 64 bytes: four lanes per row.  The
-    // range ends with the last row's channel Di, so rows past L read 0.
+    // range ends with the last row's channel Di, so rows past L read 0.  No
+    // nontemporal hint: the other half of each 128-byte line belongs to the
+    // neighbouring tile, whose workgroup asks the same L2 for it.
     auto prefetch = [&](int row, int ch, int lane) {
         const int b_ = row / n_tiles;
         const int64_t cb = (int64_t)(row % n_tiles) * kCT;
-        const int r0 = 64 * (wv - 2);
+        const int r0 = 32 * wv;
         const int64_t n_0 = (int64_t)ch * kRw;
         const int rows = (int)(L - n_0 < kRw ? L - n_0 : kRw);
         const int64_t tb = ((int64_t)b_ * L + n_0) * Di + cb;  // the tile's first element
@@ -210,24 +212,24 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
         const rsrc_t ra = make_rsrc(a + tb, range);
         const rsrc_t rb = make_rsrc(bg + tb, range);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 2; ++k) {
             const uint32_t so = (uint32_t)(16 * k) * rowb;
-            dma16b(rh, vo, so, &sU[H + r0 + 16 * k][0]);
-            dma16b(ra, vo, so, &sAB[0][r0 + 16 * k][0]);
-            dma16b(rb, vo, so, &sAB[1][r0 + 16 * k][0]);
+            dma16b<false>(rh, vo, so, &sU[H + r0 + 16 * k][0]);
+            dma16b<false>(ra, vo, so, &sAB[0][r0 + 16 * k][0]);
+            dma16b<false>(rb, vo, so, &sAB[1][r0 + 16 * k][0]);
         }
-        if (BLOCK && wv == 2) {
+        if (BLOCK && wv == 0) {
             // rows n0-16 .. n0-1 of u (the first chunk's are replaced after the copy)
             const rsrc_t rs = make_rsrc(hu + (ch > 0 ? tb - 16 * Di : tb),
                                         ch > 0 ? 16u * rowb - (uint32_t)cb * 2 : 0u);
             const uint32_t vh = ((uint32_t)(lane >> 2) * (uint32_t)Di + 8 * (lane & 3)) * 2;
-            dma16b(rs, vh, 0u, &sU[0][0]);
+            dma16b<false>(rs, vh, 0u, &sU[0][0]);
         }
         // B rows: 128 bytes, eight lanes per row
         const rsrc_t rB = make_rsrc(Bm + ((int64_t)b_ * L + n_0) * N, (uint32_t)rows * (N * 2));
         const uint32_t vb = (uint32_t)((r0 + (lane >> 3)) * N + 8 * (lane & 7)) * 2;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) dma16b(rB, vb, (uint32_t)(8 * k * N * 2), &sB[r0 + 8 * k][0]);
+        for (int k = 0; k < 4; ++k) dma16b<false>(rB, vb, (uint32_t)(8 * k * N * 2), &sB[r0 + 8 * k][0]);
     };
     // C rows of this wave's 32 tokens as MFMA operands: token lane % 32,
     // K-block kb = states 16 kb + 8 (lane / 32) .. + 7 (rows past L read 0)
@@ -244,16 +246,24 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
                                         __builtin_amdgcn_raw_buffer_load_b128(rc, vc, 32 * kb, 0));
     };
 
-    int row = blockIdx.x, chunk = 0;
-    bf16x8 Cop[4];
-    if (row < n_rows) {
-        if (wv >= 2) prefetch(row, 0, threadIdx.x & 63);
-        load_c(row, 0, threadIdx.x & 63, Cop);
-    }
-    float xr[16];  // waves 0, 1: the state carried along the row (lane = channel, 16 states)
+    // Rows are visited in slot order: workgroup w takes slots w, w + G, w + 2G,
+    // ...  Slots s and s + 8 hold rows 2k and 2k + 1 (neighbouring tiles, whose
+    // 64-byte row pieces share 128-byte lines), and workgroups w and w + 8 are
+    // dispatched to the same XCD (round robin over the eight), so both halves
+    // of a line are asked of one L2 at about the same time.
+    const auto slot_row = [](int sl) { return (sl & ~15) + 2 * (sl & 7) + ((sl >> 3) & 1); };
+    const auto next_slot = [&](int sl) {  // first slot from sl on that holds a row
+        while (sl < n_slots && slot_row(sl) >= n_rows) sl += gridDim.x;
+        return sl;
+    };
+    int slot = next_slot(blockIdx.x), chunk = 0;
+    int row = slot_row(slot);
+    if (slot < n_slots) prefetch(row, 0, threadIdx.x & 63);
+    float xr[8];  // the state carried along the row: wave w, lane (channel, half h) holds
+                  // states 16 w + 8 h .. + 7
     float Dc = 0.f, cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f;
 
-    while (row < n_rows) {
+    while (slot < n_slots) {
         wait_mem();
         __syncthreads();  // the tile of (row, chunk) is in LDS
         // lane-dependent values are re-derived every chunk (kept out of
@@ -283,10 +293,10 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
                 cw2 = conv_w[cc * 4 + 2];
                 cw3 = conv_w[cc * 4 + 3];
             }
-            if (wv < 2) {
-                const int s0 = 32 * wv + 16 * hh;
+            {
+                const int s0 = 16 * wv + 8 * hh;
 #pragma unroll
-                for (int k = 0; k < 16; ++k)
+                for (int k = 0; k < 8; ++k)
                     xr[k] = (x0 && c_col < Di) ? x0[((int64_t)bi * Di + c_col) * N + s0 + k] : 0.f;
             }
             if (BLOCK) {
@@ -303,30 +313,15 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
         }
 
         // the next chunk (of this row, else the first of the next row)
-        int nrow = row, nchunk = chunk + 1;
+        int nslot = slot, nrow = row, nchunk = chunk + 1;
         if (nchunk == n_chunks) {
             nchunk = 0;
-            nrow = row + gridDim.x;
+            nslot = next_slot(slot + gridDim.x);
+            nrow = slot_row(nslot);
         }
-        const bool has_next = nrow < n_rows;
-        bf16x8 Cnx[4];
-        if (has_next) load_c(nrow, nchunk, lane, Cnx);  // consumed next chunk
-
-        // --------------------------------------------- B operands, G = C B^T
-        bf16x8 Bsv[2][2];  // A operand of B^T W': rows = states 32 rt + col, K = tokens
-        f32x16 g = {};
-        {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const uint4 q = *(const uint4 *)&sB[32 * wv + col][16 * kb + 8 * hh];
-                g = mfma(__builtin_bit_cast(bf16x8, q), Cop[kb], g);  // g[i] = B_tok(i) . C_col
-            }
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    Bsv[rt][i >> 3][i & 7] = as_bf(sB[32 * wv + tok(i)][32 * rt + col]);
-        }
+        const bool has_next = nslot < n_slots;
+        bf16x8 Cop[4];
+        load_c(row, chunk, lane, Cop);  // arrives during the gates
 
         // ------------------------------------------------------ gates, W', P
         // Tokens past the end of the sequence (only in the last chunk of a row)
@@ -402,8 +397,27 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
         else
             gates(std::false_type{});
         const bool wave_ok = __all(ok);
+
+        // --------------------------------------------- B operands, G = C B^T
+        bf16x8 Bop[4], Bsv[2][2];  // Bsv: A operand of B^T W' (rows = states 32 rt + col)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+            Bop[kb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&sB[32 * wv + col][16 * kb + 8 * hh]);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                Bsv[rt][i >> 3][i & 7] = as_bf(sB[32 * wv + tok(i)][32 * rt + col]);
+        // (before the copy below: a wait for C issued after it would wait for the copy too)
+        f32x16 g = {};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) g = mfma(Bop[kb], Cop[kb], g);  // g[i] = B_tok(i) . C_col
+        if (chunk == 0) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) asm volatile("" ::"v"(xr[k]));  // x0 has arrived
+        }
         __syncthreads();  // every wave is done with the tile
-        if (has_next && wv >= 2) prefetch(nrow, nchunk, lane);
+        if (has_next) prefetch(nrow, nchunk, lane);
 
         // ------------- wave aggregate (P_T, S = P_T W'^T B) -> LDS, and G @ W'
         f32x16 Y;
@@ -449,19 +463,19 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
         __syncthreads();
 
         // ----------------- compose: entering state of every wave, carried state
-        // Waves 0 and 1 hold states 32 wv .. 32 wv + 31 (lane = channel, 16
-        // states per half).  Each wave's aggregate is replaced by the state
-        // entering that wave; the carried state moves past the whole chunk.
-        if (wv < 2) {
-            const int s0 = 32 * wv + 16 * hh;
+        // Wave w holds states 16 w .. 16 w + 15 (lane = channel, 8 states per
+        // half).  Each wave's aggregate is replaced by the state entering that
+        // wave; the carried state moves past the whole chunk.
+        {
+            const int s0 = 16 * wv + 8 * hh;
 #pragma unroll
             for (int w = 0; w < W; ++w) {
                 const float pw = sP[w][col];
-                float4 t[4];
+                float4 t[2];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) t[m] = *(const float4 *)&sS[w][col][s0 + 4 * m];
+                for (int m = 0; m < 2; ++m) t[m] = *(const float4 *)&sS[w][col][s0 + 4 * m];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
+                for (int m = 0; m < 2; ++m) {
                     *(float4 *)&sS[w][col][s0 + 4 * m] =
                         float4{xr[4 * m], xr[4 * m + 1], xr[4 * m + 2], xr[4 * m + 3]};
                     xr[4 * m + 0] = fmaf(pw, xr[4 * m + 0], t[m].x);
@@ -473,7 +487,7 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
             if (chunk == n_chunks - 1 && c_col < Di) {
                 if (x_final) {
 #pragma unroll
-                    for (int k = 0; k < 16; ++k)
+                    for (int k = 0; k < 8; ++k)
                         x_final[((int64_t)bi * Di + c_col) * N + s0 + k] = xr[k];
                 }
                 if (BLOCK && wv == 0 && !upper && conv_state_out) {
@@ -502,12 +516,16 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
             xs[kb][0] = u0.x, xs[kb][1] = u0.y, xs[kb][2] = u0.z, xs[kb][3] = u0.w;
             xs[kb][4] = u1.x, xs[kb][5] = u1.y, xs[kb][6] = u1.z, xs[kb][7] = u1.w;
         }
-        if (ckpt && active && c_col < Di) {
-            float *cp = ckpt + (((int64_t)bi * n_waves + (int64_t)chunk * W + wv) * N) * Di + c_col;
+        if (ckpt && active) {
+            float *cp = ckpt + (((int64_t)bi * n_waves + (int64_t)chunk * W + wv) * N) * Di + cbase;
+            const rsrc_t rc = make_rsrc(cp, (uint32_t)(N * Di * 4));
+            const uint32_t vo = c_col < Di ? (uint32_t)((8 * hh) * Di + col) * 4 : kOOB;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) cp[(int64_t)(16 * kb + 8 * hh + e) * Di] = xs[kb][e];
+                for (int e = 0; e < 8; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xs[kb][e]), rc, vo,
+                                                          (uint32_t)((16 * kb + e) * Di) * 4, 0);
         }
 
         if (!wave_ok) {
@@ -556,10 +574,7 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
                 }
             }
         }
-        if (has_next) {
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) Cop[kb] = Cnx[kb];
-        }
+        slot = nslot;
         row = nrow;
         chunk = nchunk;
     }
@@ -578,19 +593,20 @@ hipError_t launch_fwd_mfma64(const FwdArgs &g, hipStream_t stream)
 {
     const int n_tiles = (int)((g.Di + kCT - 1) / kCT);
     const int n_chunks = (int)((g.L + kRw - 1) / kRw);
-    const int64_t rows = g.Bt * n_tiles;
-    const int64_t slots = 2 * (int64_t)device_cu_count();  // two workgroups per CU
-    const int64_t grid = rows < slots ? rows : slots;
+    const int64_t n_slots = (g.Bt * n_tiles + 15) / 16 * 16;
+    int64_t slots = 2 * (int64_t)device_cu_count() / 8 * 8;  // two workgroups per CU
+    if (slots < 16) slots = 16;
+    const int64_t grid = n_slots < slots ? n_slots : slots;
     if (g.block)
         hipLaunchKernelGGL(fwd_mfma64_kernel<true>, dim3(grid), dim3(64 * kWv), 0, stream, g.Bt,
-                           g.L, g.Di, n_tiles, n_chunks, g.scale, (const bf16 *)g.hu,
+                           g.L, g.Di, n_tiles, n_chunks, (int)n_slots, g.scale, (const bf16 *)g.hu,
                            (const bf16 *)g.a, (const bf16 *)g.b, (const bf16 *)g.B,
                            (const bf16 *)g.C, g.D, g.x0, (const bf16 *)g.z, g.conv_w,
                            (const bf16 *)g.conv_state, (bf16 *)g.y, g.x_final,
                            (bf16 *)g.conv_state_out, g.ckpt);
     else
         hipLaunchKernelGGL(fwd_mfma64_kernel<false>, dim3(grid), dim3(64 * kWv), 0, stream, g.Bt,
-                           g.L, g.Di, n_tiles, n_chunks, g.scale, (const bf16 *)g.hu,
+                           g.L, g.Di, n_tiles, n_chunks, (int)n_slots, g.scale, (const bf16 *)g.hu,
                            (const bf16 *)g.a, (const bf16 *)g.b, (const bf16 *)g.B,
                            (const bf16 *)g.C, g.D, g.x0, (const bf16 *)g.z, g.conv_w,
                            (const bf16 *)g.conv_state, (bf16 *)g.y, g.x_final,

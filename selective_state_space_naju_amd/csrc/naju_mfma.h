@@ -69,22 +69,30 @@ __device__ __forceinline__ void split16(const float (&v)[16], bf16x8 (&hi)[2], b
 }
 
 // 16 bytes per lane HBM -> LDS through a buffer descriptor (buffer_load_dwordx4
-// ... lds, nontemporal): lane i copies bytes voff + soff of r (zeros past its
-// range) to lds + 16 i.  Issued through inline assembly so that the compiler's
-// memory-counter bookkeeping does not see it: it would otherwise wait for the
-// copy before LDS reads it cannot prove disjoint from it and before later uses
-// of ordinary loads.  The caller waits for the copy (vmcnt(0)) before reading
-// it.  M0 holds the LDS address; the kernels using this do not use M0 otherwise.
+// ... lds; NT: with the nontemporal hint): lane i copies bytes voff + soff of r
+// (zeros past its range) to lds + 16 i.  Issued through inline assembly so that
+// the compiler's memory-counter bookkeeping does not see it: it would otherwise
+// wait for the copy before LDS reads it cannot prove disjoint from it and
+// before later uses of ordinary loads.  The caller waits for the copy
+// (vmcnt(0)) before reading it.  M0 holds the LDS address; the kernels using
+// this do not use M0 otherwise.
+template <bool NT = true>
 __device__ __forceinline__ void dma16b(rsrc_t r, uint32_t voff, uint32_t soff, const void *lds)
 {
     const uint32_t la = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char *)lds);
     // (the row offset joins the lane offset: a constant soffset operand would be
     // emitted as a literal, which the instruction does not accept)
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
-                 :
-                 : "v"(voff + soff), "s"(r), "s"(la)
-                 : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                     :
+                     : "v"(voff + soff), "s"(r), "s"(la)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :
+                     : "v"(voff + soff), "s"(r), "s"(la)
+                     : "memory", "m0");
 }
 
 }  // namespace naju
