@@ -12,6 +12,10 @@ Also timed in the same run: the scan forward alone (the kernel with the
 70%-of-HBM-peak target), the block forward alone, and the CPU oracle on a
 bounded sample of the same workload (the cpu_baseline leg).
 
+`--workload NAME` instead times naju_scan_fwd alone on another named workload
+of the hot path (for instance the 4 x 8192 x 4096, d_state 64 scan), with its
+roofline; the default run is the training step above.
+
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -77,6 +81,8 @@ def main():
     ap.add_argument("--only", choices=["all", "scan_fwd", "step", "copy"], default="all",
                     help="restrict the timed work (for profiling runs); 'copy' runs a plain "
                          "1 GiB device copy, the reference for HBM byte counters")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="another named scan workload: time naju_scan_fwd alone on it")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Naju scan path has no multi-GPU "
@@ -109,6 +115,8 @@ def main():
         print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
                           "ms": round(dt * 1e3, 4), "GB_per_s": round(2 * nbytes / dt / 1e9, 1)}))
         return
+    if args.workload != WORKLOAD:
+        return bench_scan_workload(args, torch, nb, inputs)
     w = inputs.WORKLOADS[WORKLOAD]
     Bt, L, Di, N = w.Bt, w.L, w.Di, w.N
     e = 2
@@ -252,6 +260,7 @@ def main():
                 "ms_per_launch": round(ms, 4), "alg_bytes_per_launch": int(by)}
 
     fwd_src = ("selective_state_space_naju_amd/csrc/naju_fwd_mfma.hip",
+               "selective_state_space_naju_amd/csrc/naju_mfma.h",
                "selective_state_space_naju_amd/csrc/naju_device.h",
                "selective_state_space_naju_amd/csrc/naju_launch.h")
     rf_scan = (roofline("scan_fwd", "naju::fwd_mfma_kernel<false> (naju_scan_fwd)",
@@ -317,6 +326,91 @@ def main():
         "cpu_baseline": cpu,
         "hbm_copy_ceiling": copy_ceiling,
         "parts": parts,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_scan_workload(args, torch, nb, inputs):
+    """naju_scan_fwd alone on a named scan workload, inputs resident in HBM."""
+    w = inputs.WORKLOADS[args.workload]
+    if w.block or w.backward:
+        raise SystemExit("--workload takes a scan workload")
+    Bt, L, Di, N = w.Bt, w.L, w.Di, w.N
+    e = 2 if w.io == "bf16" else 4
+    dev = torch.device("cuda:0")
+    io_t = torch.bfloat16 if w.io == "bf16" else torch.float32
+    d = inputs.draw_workload(w)
+    base = {k: torch.from_numpy(d[k]).to(io_t).to(dev) for k in ("h", "a", "b", "B", "C")}
+    D = torch.from_numpy(d["D"]).to(dev)
+    del d
+    # two input sets (a third would not fit the point: each set is well past the
+    # 256 MB Infinity Cache at this size)
+    sets = [base, {k: v.clone() for k, v in base.items()}]
+    dims = nb.make_dims(Bt, L, Di, N, nb.BF16 if w.io == "bf16" else nb.F32)
+    ws = nb.Workspace(nb.workspace_bytes(nb.OP_SCAN_FWD, dims), dev)
+    y = torch.empty((Bt, L, Di), dtype=io_t, device=dev)
+    xf = torch.empty((Bt, Di, N), dtype=torch.float32, device=dev)
+    L_, stream = nb.lib(), nb.stream_handle(dev)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+
+    def call(i):
+        s = sets[i % 2]
+        nb.check(L_.naju_scan_fwd(ctypes.byref(dims), p(s["h"]), p(s["a"]), p(s["b"]),
+                                  p(s["B"]), p(s["C"]), p(D), None, p(y), p(xf), None, ws.ptr,
+                                  ws.nbytes, stream))
+    for k in range(args.warmup):
+        call(k)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record()
+        call(k)
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    t_all = (time.perf_counter() - t0) / args.steps
+    if ws.error_flags():
+        raise RuntimeError("a cross-workgroup wait gave up: results invalid")
+    tt = np.array([a.elapsed_time(b) for a, b in ev])
+    ms = float(tt.mean())
+    by = alg_bytes("scan_fwd", Bt, L, Di, N, e)
+    ach = by / (ms * 1e-3) / 1e9
+    traffic = None
+    if N == 64 and e == 2:
+        kernel = "naju::fwd_mfma64_kernel<false> (naju_scan_fwd)"
+        traffic = measured_traffic(
+            "hbm_traffic_fwd_mfma64_%s.md" % w.name,
+            ("selective_state_space_naju_amd/csrc/naju_fwd_mfma64.hip",
+             "selective_state_space_naju_amd/csrc/naju_mfma.h",
+             "selective_state_space_naju_amd/csrc/naju_device.h",
+             "selective_state_space_naju_amd/csrc/naju_launch.h"))
+    else:
+        kernel = "naju_scan_fwd (d_state %d)" % N
+    out = {
+        "metric": METRIC,
+        "value": round(Bt * L / (t_all), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_all * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": Bt, "seq_len": L, "d_inner": Di, "d_state": N,
+                   "io": w.io, "state": "f32", "step": "scan fwd"},
+        "roofline": {"kernel": kernel, "bound": "hbm", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "ms_per_launch": round(ms, 4),
+                     "alg_bytes_per_launch": int(by)},
+        "cpu_baseline": None,
+        "parts": {"scan_fwd": {"ms_median": round(float(np.median(tt)), 4), "ms_mean": round(ms, 4),
+                               "tokens_per_s": round(Bt * L / (ms * 1e-3), 1), "alg_bytes": int(by),
+                               "GB_per_s": round(ach, 1),
+                               "pct_hbm_peak": round(100 * ach / HBM_PEAK_GBS, 2)}},
     }
     print(json.dumps(out), flush=True)
 
