@@ -637,11 +637,26 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                                         BLOCK ? (uint32_t)Lw * row2 : 0u);
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
+                const bool vc = cbase + 32 * j + col < Di;
+                // z of the column tile first, all at once: the y stores below may
+                // alias it as far as the compiler can tell, so a load placed between
+                // them would wait out a full round trip per element
+                uint32_t zb[16];
+                if (BLOCK) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t vo =
+                            vc ? (uint32_t)((4 * hh + r) * Di + 32 * j + col) * 2 : kOOB;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            zb[4 * q + r] = __builtin_amdgcn_raw_buffer_load_b16(
+                                rz, vo, (uint32_t)(8 * q) * row2, 0);
+                    }
+                }
                 bf16x8 xh, xl;
                 split8(xs[j], xh, xl);
                 Y[j] = mfma(Csc, xh, Y[j]);
                 Y[j] = mfma(Csc, xl, Y[j]);
-                const bool vc = cbase + 32 * j + col < Di;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const uint32_t vo = vc ? (uint32_t)((4 * hh + r) * Di + 32 * j + col) * 2 : kOOB;
@@ -651,8 +666,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                         const uint32_t so = (uint32_t)(8 * q) * row2;
                         float yv = Pv[j][i] * Y[j][i];
                         if (BLOCK) {
-                            const float zv = __uint_as_float(
-                                (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rz, vo, so, 0) << 16);
+                            const float zv = __uint_as_float(zb[i] << 16);
                             yv *= zv * sigm(zv);
                         }
                         __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(yv), ry, vo, so, 2);

@@ -557,6 +557,19 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
             const rsrc_t rz = make_rsrc(BLOCK ? (const void *)(z + ebase) : (const void *)y,
                                         BLOCK ? (uint32_t)Lw * row2 : 0u);
             const bool vc = c_col < Di;
+            // z first, all at once: the y stores below may alias it as far as the
+            // compiler can tell, so a load between them would wait out a round trip
+            uint32_t zb[16];
+            if (BLOCK) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t vo = vc ? (uint32_t)((4 * hh + r) * Di + col) * 2 : kOOB;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        zb[4 * q + r] =
+                            __builtin_amdgcn_raw_buffer_load_b16(rz, vo, (uint32_t)(8 * q) * row2, 0);
+                }
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const uint32_t vo = vc ? (uint32_t)((4 * hh + r) * Di + col) * 2 : kOOB;
@@ -566,8 +579,7 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
                     const uint32_t so = (uint32_t)(8 * q) * row2;
                     float yv = Pv[i] * Y[i];
                     if (BLOCK) {
-                        const float zv = __uint_as_float(
-                            (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rz, vo, so, 0) << 16);
+                        const float zv = __uint_as_float(zb[i] << 16);
                         yv *= zv * sigm(zv);
                     }
                     __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(yv), ry, vo, so, 2);
