@@ -69,6 +69,20 @@ __device__ __forceinline__ uint32_t ld_agent(const uint32_t *p) {
 __device__ __forceinline__ uint32_t add_agent(uint32_t *p, uint32_t v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A published value as one 64-bit word: the fp32 value in the low half, the
+// tag of the call and kind that wrote it (make_flag) in the high half.  One
+// agent-scope store writes both, so a reader that sees the current tag sees the
+// value stored with it: no separate flag and no wait between value and flag.
+__device__ __forceinline__ void st_tagged(uint64_t *p, float v, uint32_t tag) {
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_tagged(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float tagged_value(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ uint32_t tagged_tag(uint64_t w) { return (uint32_t)(w >> 32); }
+
 // Waits until every memory operation this wave issued has completed; also a
 // compiler barrier for memory accesses.
 __device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

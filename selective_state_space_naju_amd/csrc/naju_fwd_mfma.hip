@@ -187,7 +187,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
     const float *__restrict__ D, const float *__restrict__ x0, const bf16 *__restrict__ z,
     const float *__restrict__ conv_w, const bf16 *__restrict__ conv_state, bf16 *__restrict__ y,
     float *__restrict__ x_final, bf16 *__restrict__ conv_state_out, float *__restrict__ ckpt,
-    WsHeader *hdr, uint32_t *flags, float *agg, float *incl)
+    WsHeader *hdr, uint64_t *agg, uint64_t *incl)
 {
     constexpr int N = 16, T = kFwdT, W = kMfmaW, H = BLOCK ? kHalo : 0;
     static_assert(T == 32, "one 32x32 MFMA tile of tokens per wave");
@@ -465,12 +465,16 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
 
         // -------------------------------- look-back for the entering state
         // Waves 0 and 1 (which issue no tile copies) carry states 8w..8w+7 of
-        // the 64 channels (lane = channel); each publishes / reads its own flags,
-        // so the two look back in parallel.  Up to kLB predecessors' flags are
-        // read at once; when every one up to the nearest inclusive state is
-        // published, their payloads are loaded together and folded in order.
+        // the 64 channels (lane = channel); each publishes and reads its own
+        // slots, so the two look back in parallel.  Every published value is a
+        // tagged word (the call's epoch and the kind: aggregate or inclusive
+        // state) written by one agent-scope store, so publishing needs no wait
+        // and no flag, and a reader takes a predecessor's values once all 64
+        // lanes' words carry the current tag: one round trip when the nearest
+        // predecessor's inclusive state is out, else its aggregate is folded
+        // and the look-back moves one chunk further.
         if (wv < 2) {
-            constexpr int kLB = 2, SG = 8;
+            constexpr int SG = 8;
             const int s0 = SG * wv;
             float Pt = 1.f, St[SG];
 #pragma unroll
@@ -482,85 +486,70 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                 Pt *= pw;
             }
             const size_t me = ((size_t)bi * n_tiles + tile) * n_chunks + chunk;
-            const size_t mg = me * 2 + wv;  // this wave's flag / payload slot
+            const size_t mg = me * 2 + wv;  // this wave's payload slot
+            const uint32_t tagA = make_flag(ep, kFlagAgg), tagI = make_flag(ep, kFlagIncl);
             float xin[SG];
             if (chunk == 0) {
 #pragma unroll
                 for (int k = 0; k < SG; ++k)
                     xin[k] = (x0 && valid_lane) ? x0[(bi * Di + c_lane) * N + s0 + k] : 0.f;
             } else {
-                float *ag = agg + mg * ((SG + 1) * 64);
-                st_agent(ag + lane, Pt);
+                uint64_t *ag = agg + mg * ((SG + 1) * 64);
+                st_tagged(ag + lane, Pt, tagA);
 #pragma unroll
-                for (int k = 0; k < SG; ++k) st_agent(ag + (1 + k) * 64 + lane, St[k]);
-                wait_mem();
-                if (lane == 0) st_agent(&flags[mg], make_flag(ep, kFlagAgg));
+                for (int k = 0; k < SG; ++k) st_tagged(ag + (1 + k) * 64 + lane, St[k], tagA);
                 float accP = 1.f, accS[SG];
 #pragma unroll
                 for (int k = 0; k < SG; ++k) accS[k] = 0.f;
                 size_t jx = me - 1;  // nearest predecessor not folded in yet
-                int left = chunk;    // predecessors not folded in yet
                 uint32_t spins = 0;
                 for (;;) {
-                    const int K = left < kLB ? left : kLB;
-                    uint32_t st = 0;
-                    if (lane < K) {
-                        const uint32_t f = ld_agent(&flags[(jx - lane) * 2 + wv]);
-                        st = (f >> 2) == ep ? (f & 3u) : 0u;
-                    }
-                    const uint64_t im = __ballot(lane < K && st == kFlagIncl);
-                    const uint64_t rm = __ballot(lane < K && st != 0u);
-                    const int d = im ? (int)__builtin_ctzll(im) : K;  // aggregates before it
-                    const uint64_t need = im ? ((2ull << d) - 1) : ((1ull << K) - 1);
-                    if ((rm & need) != need) {
-                        if (++spins > kSpinLimit) {
-                            __hip_atomic_fetch_or(&hdr->error, 1u, __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT);
+                    // (a row's first chunk publishes only its inclusive state, so
+                    // the walk always ends at one)
+                    const uint64_t *pi = incl + (jx * 2 + wv) * (SG * 64);
+                    uint64_t iv[SG];
 #pragma unroll
-                            for (int k = 0; k < SG; ++k) xin[k] = 0.f;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(1);
-                        continue;
-                    }
-                    float pj[kLB], sj[kLB][SG], in[SG];
+                    for (int k = 0; k < SG; ++k) iv[k] = ld_tagged(pi + k * 64 + lane);
+                    bool ri = true;
 #pragma unroll
-                    for (int o = 0; o < kLB; ++o) {
-                        if (o < d) {
-                            const float *pa = agg + ((jx - o) * 2 + wv) * ((SG + 1) * 64);
-                            pj[o] = ld_agent(pa + lane);
+                    for (int k = 0; k < SG; ++k) ri = ri && tagged_tag(iv[k]) == tagI;
+                    if (__all(ri)) {
 #pragma unroll
-                            for (int k = 0; k < SG; ++k) sj[o][k] = ld_agent(pa + (1 + k) * 64 + lane);
-                        }
-                    }
-                    if (im) {
-                        const float *pi = incl + ((jx - d) * 2 + wv) * (SG * 64);
-#pragma unroll
-                        for (int k = 0; k < SG; ++k) in[k] = ld_agent(pi + k * 64 + lane);
-                    }
-#pragma unroll
-                    for (int o = 0; o < kLB; ++o) {
-                        if (o < d) {
-#pragma unroll
-                            for (int k = 0; k < SG; ++k) accS[k] = fmaf(accP, sj[o][k], accS[k]);
-                            accP *= pj[o];
-                        }
-                    }
-                    if (im) {
-#pragma unroll
-                        for (int k = 0; k < SG; ++k) xin[k] = fmaf(accP, in[k], accS[k]);
+                        for (int k = 0; k < SG; ++k)
+                            xin[k] = fmaf(accP, tagged_value(iv[k]), accS[k]);
                         break;
                     }
-                    jx -= K;
-                    left -= K;
+                    const uint64_t *pa = agg + (jx * 2 + wv) * ((SG + 1) * 64);
+                    uint64_t av[SG + 1];
+#pragma unroll
+                    for (int k = 0; k <= SG; ++k) av[k] = ld_tagged(pa + k * 64 + lane);
+                    bool ra = true;
+#pragma unroll
+                    for (int k = 0; k <= SG; ++k) ra = ra && tagged_tag(av[k]) == tagA;
+                    if (__all(ra)) {
+#pragma unroll
+                        for (int k = 0; k < SG; ++k)
+                            accS[k] = fmaf(accP, tagged_value(av[1 + k]), accS[k]);
+                        accP *= tagged_value(av[0]);
+                        --jx;
+                        continue;
+                    }
+                    if (++spins > kSpinLimit) {
+                        __hip_atomic_fetch_or(&hdr->error, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                        for (int k = 0; k < SG; ++k) xin[k] = 0.f;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
                 }
             }
-            float *ic = incl + mg * (SG * 64);
+            uint64_t *ic = incl + mg * (SG * 64);
             float xo[SG];
 #pragma unroll
             for (int k = 0; k < SG; ++k) {
                 xo[k] = fmaf(Pt, xin[k], St[k]);
-                st_agent(ic + k * 64 + lane, xo[k]);
+                st_tagged(ic + k * 64 + lane, xo[k], tagI);
                 sX[s0 + k][lane] = xin[k];
             }
             if (valid_lane && chunk == n_chunks - 1) {
@@ -581,8 +570,6 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                     }
                 }
             }
-            wait_mem();
-            if (lane == 0) st_agent(&flags[mg], make_flag(ep, kFlagIncl));
         }
         __syncthreads();
 
@@ -703,9 +690,8 @@ hipError_t launch_fwd_mfma(const FwdArgs &g, hipStream_t stream)
 {
     const FwdPlan pl = fwd_plan(g.Bt, g.L, g.Di, g.N, kMfmaW);
     WsHeader *hdr = (WsHeader *)g.ws;
-    uint32_t *flags = (uint32_t *)((char *)g.ws + pl.off_flags);
-    float *agg = (float *)((char *)g.ws + pl.off_agg);
-    float *incl = (float *)((char *)g.ws + pl.off_incl);
+    uint64_t *agg = (uint64_t *)((char *)g.ws + pl.off_agg);
+    uint64_t *incl = (uint64_t *)((char *)g.ws + pl.off_incl);
     const int64_t slots = 2 * (int64_t)device_cu_count();  // two workgroups per CU
     const int64_t grid = pl.n_wg < slots ? pl.n_wg : slots;
     if (g.block)
@@ -714,14 +700,14 @@ hipError_t launch_fwd_mfma(const FwdArgs &g, hipStream_t stream)
                            (const bf16 *)g.a, (const bf16 *)g.b, (const bf16 *)g.B,
                            (const bf16 *)g.C, g.D, g.x0, (const bf16 *)g.z, g.conv_w,
                            (const bf16 *)g.conv_state, (bf16 *)g.y, g.x_final,
-                           (bf16 *)g.conv_state_out, g.ckpt, hdr, flags, agg, incl);
+                           (bf16 *)g.conv_state_out, g.ckpt, hdr, agg, incl);
     else
         hipLaunchKernelGGL(fwd_mfma_kernel<false>, dim3(grid), dim3(64 * kMfmaW), 0, stream,
                            g.Bt, g.L, g.Di, pl.n_tiles, pl.n_chunks, g.scale, (const bf16 *)g.hu,
                            (const bf16 *)g.a, (const bf16 *)g.b, (const bf16 *)g.B,
                            (const bf16 *)g.C, g.D, g.x0, (const bf16 *)g.z, g.conv_w,
                            (const bf16 *)g.conv_state, (bf16 *)g.y, g.x_final,
-                           (bf16 *)g.conv_state_out, g.ckpt, hdr, flags, agg, incl);
+                           (bf16 *)g.conv_state_out, g.ckpt, hdr, agg, incl);
     return hipGetLastError();
 }
 

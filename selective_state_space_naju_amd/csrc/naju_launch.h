@@ -39,12 +39,14 @@ inline FwdPlan fwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N, int W = kF
     p.n_wg = Bt * p.n_tiles * p.n_chunks;
     p.n_waves = (L + kFwdT - 1) / kFwdT;
     // the matrix-core forward looks back in two state groups of eight: two
-    // flags and two (P, S[8]) aggregates per workgroup chunk
+    // (P, S[8]) aggregates and two x_out[8] per workgroup chunk, each value a
+    // tagged 64-bit word; the register forward uses flags and fp32 payloads
     const size_t fl = W == kMfmaW ? 2 : 1, ar = W == kMfmaW ? 18 : 17;
+    const size_t vb = W == kMfmaW ? 8 : 4;  // bytes per published value
     p.off_flags = 256;
     p.off_agg = align256(p.off_flags + 4 * fl * (size_t)p.n_wg);
-    p.off_incl = align256(p.off_agg + ar * 64 * 4 * (size_t)p.n_wg);
-    p.bytes = align256(p.off_incl + 16 * 64 * 4 * (size_t)p.n_wg);
+    p.off_incl = align256(p.off_agg + ar * 64 * vb * (size_t)p.n_wg);
+    p.bytes = align256(p.off_incl + 16 * 64 * vb * (size_t)p.n_wg);
     return p;
 }
 
