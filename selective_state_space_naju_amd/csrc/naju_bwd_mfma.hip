@@ -369,12 +369,17 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
             for (int i = 0; i < 16; ++i) sWT[tw][tok(i)][col] = bits_of(WB[i >> 3], i & 7);
         }
         const bool wave_ok = __all(ok);
-        // x_in (forward checkpoint): states 8h..8h+7 of channel col
-        float xin[8];
+        // x_in (forward checkpoint): states 8h..8h+7 of channel col; and the
+        // workgroup's entering adjoint, loaded here so that both round trips
+        // overlap the products and the barrier below
+        float xin[8], mu0[8];
+        const size_t me = ((size_t)bi * n_tiles + tile) * n_chunks + chunk;
         {
             const float *ck = ckpt + (((int64_t)bi * n_waves + wrow) * N + 8 * hh) * Di + c;
 #pragma unroll
             for (int k = 0; k < 8; ++k) xin[k] = (active && valid) ? ck[(int64_t)k * Di] : 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) mu0[k] = muin[me * (16 * 32) + (8 * hh + k) * 32 + col];
         }
         {
             f32x16 r = {};
@@ -392,8 +397,6 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
         }
         __syncthreads();
 
-        const size_t me = ((size_t)bi * n_tiles + tile) * n_chunks + chunk;
-
         // ------------------------------------------------------- phase B
         // this wave's entering adjoint (the later waves pass it first), Mu,
         // x_in and Phi_0 = mu_out . x_in
@@ -401,7 +404,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
         // later waves (states 8h..8h+7 of channel col)
         auto entering = [&](float (&mu)[8]) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) mu[k] = muin[me * (16 * 32) + (8 * hh + k) * 32 + col];
+            for (int k = 0; k < 8; ++k) mu[k] = mu0[k];
             for (int w = kTW - 1; w > tw; --w) {
                 const float qw = sQ[w][col];
 #pragma unroll
