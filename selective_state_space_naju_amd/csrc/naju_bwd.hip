@@ -452,13 +452,17 @@ __global__ __launch_bounds__(64 * kBwdW) void bwd_kernel(
     }
 }
 
+// The finish of a backward call: three independent jobs, each too small to
+// fill the device alone, run as block ranges of one launch (finish_kernel),
+// then the second dD / dconv_w pass.  Every job keeps its fixed summation order.
+
 // dB / dC: sum the per-tile partials in tile order.
 template <typename IO>
-__global__ void bc_reduce_kernel(const int64_t rows, const int n_tiles, const int N2,
-                                 const float *__restrict__ part, IO *__restrict__ dB,
-                                 IO *__restrict__ dC)
+__device__ __forceinline__ void bc_reduce_block(int blk, const int64_t rows, const int n_tiles,
+                                                const int N2, const float *__restrict__ part,
+                                                IO *__restrict__ dB, IO *__restrict__ dC)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over rows * N2
+    const int64_t i = (int64_t)blk * 256 + threadIdx.x;  // over rows * N2
     if (i >= rows * N2) return;
     const int64_t row = i / N2;
     const int s = (int)(i % N2);
@@ -476,16 +480,15 @@ __global__ void bc_reduce_kernel(const int64_t rows, const int n_tiles, const in
 // fixed order (deterministic).  Pass 1: row group g of RG (consecutive rows)
 // for 64 channels, its four waves taking every fourth row, summed in wave order.
 
-__global__ __launch_bounds__(256) void dd_reduce1_kernel(const int64_t rows, const int64_t Di,
-                                                         const int RG,
-                                                         const float *__restrict__ dd_part,
-                                                         const float *__restrict__ dw_part,
-                                                         float *__restrict__ part2)
+__device__ __forceinline__ void dd_reduce1_block(int bx, int g, const int64_t rows,
+                                                 const int64_t Di, const int RG,
+                                                 const float *__restrict__ dd_part,
+                                                 const float *__restrict__ dw_part,
+                                                 float *__restrict__ part2)
 {
     __shared__ float red[4][5][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int64_t c = (int64_t)blockIdx.x * 64 + lane;
-    const int g = blockIdx.y;
+    const int64_t c = (int64_t)bx * 64 + lane;
     const int64_t r0 = rows * g / RG, r1 = rows * (g + 1) / RG;
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, s4 = 0.f;
     if (c < Di) {
@@ -543,13 +546,14 @@ __global__ __launch_bounds__(256) void dd_reduce2_kernel(const int64_t Di, const
 // next wave's first tokens, and writes dconv_state (inputs before u_0).
 //   du_m = sum_k w[k] dpre_{m+3-k}
 template <typename IO>
-__global__ void edge_fix_kernel(const int64_t Bt, const int64_t L, const int64_t Di,
-                                const int64_t n_waves, const float *__restrict__ conv_w,
-                                const float *__restrict__ edge, IO *__restrict__ du,
-                                IO *__restrict__ dconv_state)
+__device__ __forceinline__ void edge_fix_block(int blk, const int64_t Bt, const int64_t L,
+                                               const int64_t Di, const int64_t n_waves,
+                                               const float *__restrict__ conv_w,
+                                               const float *__restrict__ edge, IO *__restrict__ du,
+                                               IO *__restrict__ dconv_state)
 {
     constexpr int T = kBwdT;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // over Bt*n_waves*Di
+    const int64_t i = (int64_t)blk * 256 + threadIdx.x;  // over Bt*n_waves*Di
     if (i >= Bt * n_waves * Di) return;
     const int64_t c = i % Di;
     const int64_t wrow = (i / Di) % n_waves;
@@ -590,6 +594,31 @@ __global__ void edge_fix_kernel(const int64_t Bt, const int64_t L, const int64_t
             dconv_state[(bi * 3 + q) * Di + c] = from_f<IO>(acc);
         }
     }
+}
+
+// Blocks [0, nb_bc): dB/dC; then nb_dd blocks of the first dD/dconv_w pass
+// (nbx channel blocks per row group); then nb_edge blocks of the edge fix.
+template <typename IO>
+__global__ __launch_bounds__(256) void finish_kernel(
+    const int nb_bc, const int64_t bc_rows, const int n_parts, const int N2,
+    const float *__restrict__ bc, IO *__restrict__ dB, IO *__restrict__ dC, const int nb_dd,
+    const int nbx, const int64_t dd_rows, const int RG, const float *__restrict__ dd_part,
+    const float *__restrict__ dw_part, float *__restrict__ part2, const int64_t Bt,
+    const int64_t L, const int64_t Di, const int64_t n_waves, const float *__restrict__ conv_w,
+    const float *__restrict__ edge, IO *__restrict__ du, IO *__restrict__ dconv_state)
+{
+    int b = blockIdx.x;  // block-uniform job selection
+    if (b < nb_bc) {
+        bc_reduce_block<IO>(b, bc_rows, n_parts, N2, bc, dB, dC);
+        return;
+    }
+    b -= nb_bc;
+    if (b < nb_dd) {
+        dd_reduce1_block(b % nbx, b / nbx, dd_rows, Di, RG, dd_part, dw_part, part2);
+        return;
+    }
+    b -= nb_dd;
+    edge_fix_block<IO>(b, Bt, L, Di, n_waves, conv_w, edge, du, dconv_state);
 }
 
 template <typename IO>
@@ -633,34 +662,25 @@ static hipError_t launch_bwd_finish(const BwdArgs &g, int n_parts, hipStream_t s
     float *dw = (float *)(ws + pl.off_dw);
     float *edge = (float *)(ws + pl.off_edge);
     hipError_t e;
-    {
-        const int64_t rows = g.Bt * g.L;
-        const int64_t tot = rows * 2 * N;
-        hipLaunchKernelGGL((bc_reduce_kernel<IO>), dim3((unsigned)((tot + 255) / 256)), dim3(256),
-                           0, stream, rows, n_parts, 2 * N, (const float *)bc, (IO *)g.dB,
-                           (IO *)g.dC);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    {
-        const int64_t rows = g.Bt * pl.n_waves;
-        const int RG = (int)(rows / 8 < 1 ? 1 : rows / 8 > kDdGroups ? kDdGroups : rows / 8);
-        float *part2 = (float *)(ws + pl.off_dd2);
-        hipLaunchKernelGGL(dd_reduce1_kernel, dim3((unsigned)((g.Di + 63) / 64), (unsigned)RG),
-                           dim3(256), 0, stream, rows, g.Di, RG, (const float *)dd,
-                           g.block ? (const float *)dw : (const float *)nullptr, part2);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        hipLaunchKernelGGL(dd_reduce2_kernel, dim3((unsigned)((g.Di * 5 + 255) / 256)), dim3(256), 0,
-                           stream, g.Di, RG, (const float *)part2, g.dD,
-                           g.block ? g.dconv_w : (float *)nullptr);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    if (g.block) {
-        const int64_t tot = g.Bt * pl.n_waves * g.Di;
-        hipLaunchKernelGGL((edge_fix_kernel<IO>), dim3((unsigned)((tot + 255) / 256)), dim3(256), 0,
-                           stream, g.Bt, g.L, g.Di, pl.n_waves, g.conv_w, (const float *)edge,
-                           (IO *)g.dhu, (IO *)g.dconv_state);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
+    const int64_t bc_rows = g.Bt * g.L;
+    const int nb_bc = (int)((bc_rows * 2 * N + 255) / 256);
+    const int64_t dd_rows = g.Bt * pl.n_waves;
+    const int RG = (int)(dd_rows / 8 < 1 ? 1 : dd_rows / 8 > kDdGroups ? kDdGroups : dd_rows / 8);
+    const int nbx = (int)((g.Di + 63) / 64);
+    const int nb_dd = nbx * RG;
+    const int nb_edge = g.block ? (int)((g.Bt * pl.n_waves * g.Di + 255) / 256) : 0;
+    float *part2 = (float *)(ws + pl.off_dd2);
+    hipLaunchKernelGGL((finish_kernel<IO>), dim3((unsigned)(nb_bc + nb_dd + nb_edge)), dim3(256), 0,
+                       stream, nb_bc, bc_rows, n_parts, 2 * N, (const float *)bc, (IO *)g.dB,
+                       (IO *)g.dC, nb_dd, nbx, dd_rows, RG, (const float *)dd,
+                       g.block ? (const float *)dw : (const float *)nullptr, part2, g.Bt, g.L,
+                       g.Di, pl.n_waves, g.conv_w, (const float *)edge, (IO *)g.dhu,
+                       (IO *)g.dconv_state);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(dd_reduce2_kernel, dim3((unsigned)((g.Di * 5 + 255) / 256)), dim3(256), 0,
+                       stream, g.Di, RG, (const float *)part2, g.dD,
+                       g.block ? g.dconv_w : (float *)nullptr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     return hipSuccess;
 }
 
