@@ -211,8 +211,11 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
     // chunk and the B rows, wave 3 the C rows): a wave's wait for its own
     // memory operations covers every one it issued, and waves 0 and 1, which
     // run the look-back, must not wait for a tile copy on every flag read.
-    // The copies and the y stores carry the nontemporal hint (aux = 2): every
-    // byte is used once, so it should not displace the look-back traffic in L2.
+    // The copies carry the nontemporal hint (aux = 2): every byte is used once,
+    // so it should not displace the look-back traffic in L2.  The y stores do
+    // not: each store instruction writes 64-byte pieces of lines, which L2 merges
+    // into whole lines before writing back (with the hint: scan forward 5 %
+    // slower).
     auto prefetch = [&](uint32_t tk, int lane) {
         const int ch = (int)(tk / per_chunk);
         const int rm = (int)(tk % per_chunk);
@@ -659,7 +662,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                             const float zv = __uint_as_float(zb[i] << 16);
                             yv *= zv * sigm(zv);
                         }
-                        __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(yv), ry, vo, so, 2);
+                        __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(yv), ry, vo, so, 0);
                     }
                 }
             }

@@ -582,7 +582,8 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
                         const float zv = __uint_as_float(zb[i] << 16);
                         yv *= zv * sigm(zv);
                     }
-                    __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(yv), ry, vo, so, 2);
+                    // (no nontemporal hint: L2 merges the 64-byte pieces into whole lines)
+                    __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(yv), ry, vo, so, 0);
                 }
             }
         }
