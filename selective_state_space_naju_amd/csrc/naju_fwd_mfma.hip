@@ -603,8 +603,9 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                     cbase + 32 * j + col < Di ? (uint32_t)((8 * hh) * Di + 32 * j + col) * 4 : kOOB;
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
+                    // (nontemporal: read back only by the backward, much later)
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xs[j][k]), rc, vo,
-                                                          (uint32_t)(k * Di) * 4, 0);
+                                                          (uint32_t)(k * Di) * 4, 2);
             }
         }
 
