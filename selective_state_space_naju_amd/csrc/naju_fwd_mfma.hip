@@ -250,15 +250,16 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
             dma16b(rs, vh, 0u, &sU[0][0]);
         }
         // B rows (wave 2) or C rows (wave 3): lane = row lane / 2 of a 32-row group
+        // (no nontemporal hint: every channel tile of the batch row reads them)
         const uint32_t vb = (uint32_t)((lane >> 1) * N + 8 * (lane & 1)) * 2;
         if (wv == 2) {
             const rsrc_t rs = make_rsrc(Bm + ((int64_t)b_ * L + n_0) * N, (uint32_t)rows * (N * 2));
 #pragma unroll
-            for (int k = 0; k < 4; ++k) dma16b(rs, vb, (uint32_t)(32 * k * N * 2), &sBC[0][32 * k][0]);
+            for (int k = 0; k < 4; ++k) dma16b<false>(rs, vb, (uint32_t)(32 * k * N * 2), &sBC[0][32 * k][0]);
         } else {
             const rsrc_t rs = make_rsrc(Cm + ((int64_t)b_ * L + n_0) * N, (uint32_t)rows * (N * 2));
 #pragma unroll
-            for (int k = 0; k < 4; ++k) dma16b(rs, vb, (uint32_t)(32 * k * N * 2), &sBC[1][32 * k][0]);
+            for (int k = 0; k < 4; ++k) dma16b<false>(rs, vb, (uint32_t)(32 * k * N * 2), &sBC[1][32 * k][0]);
         }
     };
 
