@@ -137,26 +137,43 @@ __global__ __launch_bounds__(64 * W) void fwd_kernel(
     for (int s = 0; s < 16; ++s) x[s] = 0.f;
     float P = 1.f;
     float ysl[T], Pn[T];
+    // Without staging, the per-token activations of each group of 8 tokens are
+    // loaded together: one round trip per group instead of one per token.  The
+    // loads are unconditional (rows past L and lanes past Di read element 0 and
+    // the value is dropped), so none waits inside a branch of its own.
+    constexpr int G = 8;
+    float ga[G], gb[G], gh[G];
 #pragma unroll
     for (int j = 0; j < T; ++j) {
         const int64_t n = n0 + j;
+        if (!STG && j % G == 0) {
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
+                const int64_t nk = n0 + j + k;
+                const bool ok = valid && nk < L;
+                const int64_t tk = ok ? ((int64_t)bi * L + nk) * Di + c : 0;
+                const float va = to_f(a[tk]), vb = to_f(bg[tk]), vh = to_f(hu[tk]);
+                ga[k] = ok ? va : 0.f;
+                gb[k] = ok ? vb : 0.f;
+                gh[k] = ok ? vh : 0.f;
+            }
+        }
         ysl[j] = 0.f;
         Pn[j] = P;
         if (n < L) {
-            const int64_t t = ((int64_t)bi * L + n) * Di + c;
             float av = 0.f, bv = 0.f, hv = 0.f;
             if (valid) {
-                av = to_f(STG ? stg[T * kCh + j * kCh + cl] : a[t]);
-                bv = to_f(STG ? stg[2 * T * kCh + j * kCh + cl] : bg[t]);
+                av = STG ? to_f(stg[T * kCh + j * kCh + cl]) : ga[j % G];
+                bv = STG ? to_f(stg[2 * T * kCh + j * kCh + cl]) : gb[j % G];
                 if constexpr (BLOCK) {
-                    const float uv = to_f(STG ? stg[j * kCh + cl] : hu[t]);
+                    const float uv = STG ? to_f(stg[j * kCh + cl]) : gh[j % G];
                     const float pre = w0 * um3 + w1 * um2 + w2 * um1 + w3 * uv;
                     um3 = um2;
                     um2 = um1;
                     um1 = uv;
                     hv = pre * sigm(pre);
                 } else {
-                    hv = to_f(STG ? stg[j * kCh + cl] : hu[t]);
+                    hv = STG ? to_f(stg[j * kCh + cl]) : gh[j % G];
                 }
             }
             const float f = sigm(av);
