@@ -509,16 +509,15 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                 int left = chunk;    // predecessors of this row not folded in yet
                 uint32_t spins = 0;
                 for (;;) {
-                    // the predecessor's inclusive state and aggregate in one round
-                    // trip (a row's first chunk publishes only its inclusive state,
-                    // so the walk always ends at one)
+                    // the predecessor's inclusive state, else its aggregate (loading
+                    // both together measured slower: the extra words cost more than
+                    // the round trip they save; a row's first chunk publishes only
+                    // its inclusive state, so the walk always ends at one)
                     const uint64_t *pi = incl + (jx * 2 + wv) * (SG * 64);
                     const uint64_t *pa = agg + (jx * 2 + wv) * ((SG + 1) * 64);
                     uint64_t iv[SG], av[SG + 1];
 #pragma unroll
                     for (int k = 0; k < SG; ++k) iv[k] = ld_tagged(pi + k * 64 + lane);
-#pragma unroll
-                    for (int k = 0; k <= SG; ++k) av[k] = ld_tagged(pa + k * 64 + lane);
                     bool ri = true;
 #pragma unroll
                     for (int k = 0; k < SG; ++k) ri = ri && tagged_tag(iv[k]) == tagI;
@@ -528,6 +527,8 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                             xin[k] = fmaf(accP, tagged_value(iv[k]), accS[k]);
                         break;
                     }
+#pragma unroll
+                    for (int k = 0; k <= SG; ++k) av[k] = ld_tagged(pa + k * 64 + lane);
                     // (only the inclusive state of the row's first chunk ends the walk)
                     bool ra = left > 1;
 #pragma unroll
