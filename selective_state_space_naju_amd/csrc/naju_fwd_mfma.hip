@@ -187,7 +187,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
     const float *__restrict__ D, const float *__restrict__ x0, const bf16 *__restrict__ z,
     const float *__restrict__ conv_w, const bf16 *__restrict__ conv_state, bf16 *__restrict__ y,
     float *__restrict__ x_final, bf16 *__restrict__ conv_state_out, float *__restrict__ ckpt,
-    WsHeader *hdr, uint64_t *agg, uint64_t *incl)
+    WsHeader *hdr, uint64_t *agg, uint64_t *incl, const int lazy_agg)
 {
     constexpr int N = 16, T = kFwdT, W = kMfmaW, H = BLOCK ? kHalo : 0;
     static_assert(T == 32, "one 32x32 MFMA tile of tokens per wave");
@@ -498,10 +498,22 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                 for (int k = 0; k < SG; ++k)
                     xin[k] = (x0 && valid_lane) ? x0[(bi * Di + c_lane) * N + s0 + k] : 0.f;
             } else {
-                uint64_t *ag = agg + mg * ((SG + 1) * 64);
-                st_tagged(ag + lane, Pt, tagA);
+                // The aggregate is published before the walk, or (lazy_agg) only
+                // once this chunk finds it has to wait: a successor needs it only
+                // while this chunk's inclusive state is not out, and the stores are
+                // a sixth of the call's traffic.  Lazy publication pays when a round
+                // of resident workgroups spans few chunks of each row (the nearest
+                // predecessor is then usually done); with deep chains every chunk
+                // waits, and publishing late delays the walks behind it.
+                bool published = false;
+                auto publish = [&]() {
+                    uint64_t *ag = agg + mg * ((SG + 1) * 64);
+                    st_tagged(ag + lane, Pt, tagA);
 #pragma unroll
-                for (int k = 0; k < SG; ++k) st_tagged(ag + (1 + k) * 64 + lane, St[k], tagA);
+                    for (int k = 0; k < SG; ++k) st_tagged(ag + (1 + k) * 64 + lane, St[k], tagA);
+                    published = true;
+                };
+                if (!lazy_agg) publish();
                 float accP = 1.f, accS[SG];
 #pragma unroll
                 for (int k = 0; k < SG; ++k) accS[k] = 0.f;
@@ -527,6 +539,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                             xin[k] = fmaf(accP, tagged_value(iv[k]), accS[k]);
                         break;
                     }
+                    if (!published) publish();
 #pragma unroll
                     for (int k = 0; k <= SG; ++k) av[k] = ld_tagged(pa + k * 64 + lane);
                     // (only the inclusive state of the row's first chunk ends the walk)
@@ -703,20 +716,22 @@ hipError_t launch_fwd_mfma(const FwdArgs &g, hipStream_t stream)
     uint64_t *incl = (uint64_t *)((char *)g.ws + pl.off_incl);
     const int64_t slots = 2 * (int64_t)device_cu_count();  // two workgroups per CU
     const int64_t grid = pl.n_wg < slots ? pl.n_wg : slots;
+    // lazy aggregates when a round of `grid` tickets spans at most ~4 chunks of a row
+    const int lazy = (int64_t)g.Bt * pl.n_tiles * 4 >= grid ? 1 : 0;
     if (g.block)
         hipLaunchKernelGGL(fwd_mfma_kernel<true>, dim3(grid), dim3(64 * kMfmaW), 0, stream, g.Bt,
                            g.L, g.Di, pl.n_tiles, pl.n_chunks, g.scale, (const bf16 *)g.hu,
                            (const bf16 *)g.a, (const bf16 *)g.b, (const bf16 *)g.B,
                            (const bf16 *)g.C, g.D, g.x0, (const bf16 *)g.z, g.conv_w,
                            (const bf16 *)g.conv_state, (bf16 *)g.y, g.x_final,
-                           (bf16 *)g.conv_state_out, g.ckpt, hdr, agg, incl);
+                           (bf16 *)g.conv_state_out, g.ckpt, hdr, agg, incl, lazy);
     else
         hipLaunchKernelGGL(fwd_mfma_kernel<false>, dim3(grid), dim3(64 * kMfmaW), 0, stream,
                            g.Bt, g.L, g.Di, pl.n_tiles, pl.n_chunks, g.scale, (const bf16 *)g.hu,
                            (const bf16 *)g.a, (const bf16 *)g.b, (const bf16 *)g.B,
                            (const bf16 *)g.C, g.D, g.x0, (const bf16 *)g.z, g.conv_w,
                            (const bf16 *)g.conv_state, (bf16 *)g.y, g.x_final,
-                           (bf16 *)g.conv_state_out, g.ckpt, hdr, agg, incl);
+                           (bf16 *)g.conv_state_out, g.ckpt, hdr, agg, incl, lazy);
     return hipGetLastError();
 }
 
