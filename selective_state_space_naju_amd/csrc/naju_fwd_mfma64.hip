@@ -8,18 +8,21 @@
 // W'_k = w_k / P_k,
 //     y_n = P_n ( sum_{k<=n} G[n,k] W'_k + C_n x_in / sqrt(N) ) + D h_n,
 //     G   = tril(C B^T) / sqrt(N),      x_out = P_T (x_in + W'^T B),
-// where G now contracts over 64 states (four MFMA K-blocks) and the state of a
-// 32-channel tile is 64 x 32.
+// where G now contracts over 64 states (four MFMA K-blocks) and a wave's
+// state (32 channels) is 64 x 32.
 //
-// Decomposition.  A workgroup (four waves, 32 tokens each) owns one row
-// (batch row, 32-channel tile) at a time and walks its 128-token chunks in
-// order, so the state entering a chunk is the one its own previous chunk left:
-// no cross-workgroup look-back and no workspace.  The four waves carry that
-// state in registers (wave w: states 16 w .. 16 w + 15 of the 32 channels) and
-// compose it with the waves' chunk aggregates through LDS.  A wave whose chunk cannot take the
+// Decomposition.  A workgroup of eight waves owns one row (batch row,
+// 64-channel tile) at a time and walks its 128-token chunks in order, so the
+// state entering a chunk is the one its own previous chunk left: no
+// cross-workgroup look-back and no workspace.  Wave (t, c) takes token block t
+// (32 tokens) of channel half c (32 channels); the four waves of a channel half
+// carry its state in registers (token block t: states 16 t .. 16 t + 15) and
+// compose it with their chunk aggregates through LDS.  A 64-channel row is a
+// whole 128-byte line, so the tile copies fetch no half lines; one workgroup
+// fills a CU (136 KB of LDS).  A wave whose chunk cannot take the
 // rescaled form (prod 1/f beyond 2^64, a non-finite gate or h) runs the plain
 // register recurrence for it instead.  The host uses this kernel when the
-// rows alone fill the device (Bt * d_inner / 32 at least a few dozen).
+// rows alone keep a good part of the device busy (Bt * d_inner / 64 >= 32).
 #include <type_traits>
 
 #include "naju_device.h"
@@ -30,10 +33,11 @@ namespace naju {
 
 namespace {
 constexpr int kN = 64;          // d_state
-constexpr int kCT = 32;         // channels per tile
+constexpr int kCT = 64;         // channels per tile
+constexpr int kCW = 32;         // channels per wave
 constexpr int kTk = 32;         // tokens per wave
-constexpr int kWv = 4;          // waves per workgroup
-constexpr int kRw = kTk * kWv;  // tokens per chunk
+constexpr int kWv = 8;          // waves per workgroup: 4 token blocks x 2 channel halves
+constexpr int kRw = kTk * 4;    // tokens per chunk
 constexpr int kHl = 16;         // rows of u kept before the chunk (block)
 constexpr int kSP = kN + 4;     // padded per-channel state row of the LDS aggregates
 }  // namespace
@@ -171,9 +175,9 @@ __device__ void rr64_output(int64_t L, int64_t Di, int bi, int64_t c, bool valid
 
 // ------------------------------------------------------------------- kernel
 template <bool BLOCK>
-__global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
+__global__ __launch_bounds__(64 * kWv, 1) void fwd_mfma64_kernel(
     const int64_t Bt, const int64_t L, const int64_t Di, const int n_tiles, const int n_chunks,
-    const int n_slots, const float scale, const bf16 *__restrict__ hu, const bf16 *__restrict__ a,
+    const float scale, const bf16 *__restrict__ hu, const bf16 *__restrict__ a,
     const bf16 *__restrict__ bg, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
     const float *__restrict__ D, const float *__restrict__ x0, const bf16 *__restrict__ z,
     const float *__restrict__ conv_w, const bf16 *__restrict__ conv_state, bf16 *__restrict__ y,
@@ -182,60 +186,60 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
     constexpr int N = kN, T = kTk, W = kWv, H = BLOCK ? kHl : 0;
     // wave-uniform (readfirstlane keeps what derives from it in scalar registers)
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tbw = wv & 3, chh = wv >> 2;  // token block, channel half
 
     __shared__ __attribute__((aligned(16))) bf16 sU[H + kRw][kCT];  // h (scan) or u (block)
     __shared__ __attribute__((aligned(16))) bf16 sAB[2][kRw][kCT];  // a, b
     __shared__ __attribute__((aligned(16))) bf16 sB[kRw][N];        // B rows
-    __shared__ __attribute__((aligned(16))) float sS[W][kCT][kSP];  // wave aggregates / entering states
-    __shared__ float sP[W][kCT];
+    __shared__ __attribute__((aligned(16))) float sS[W][kCW][kSP];  // wave aggregates / entering states
+    __shared__ float sP[W][kCW];
 
     const int n_rows = (int)(Bt * n_tiles);
     const int64_t n_waves = (L + T - 1) / T;
     const uint32_t rowb = (uint32_t)Di * 2;
 
     // Copy the h|u, a, b tile and the B rows of chunk ch of row `row` into LDS
-    // (every wave its own 32 token rows; wave 0 also the 16 rows of u before
-    // the chunk).  A 32-channel row is 64 bytes: four lanes per row.  The
-    // range ends with the last row's channel Di, so rows past L read 0.  No
-    // nontemporal hint: the other half of each 128-byte line belongs to the
-    // neighbouring tile, whose workgroup asks the same L2 for it.
+    // (wave w: token rows 16 w .. 16 w + 15; wave 0 also the 16 rows of u
+    // before the chunk).  A 64-channel row is 128 bytes: eight lanes per row.
+    // The range ends with the last row's channel Di, so rows past L read 0.
     auto prefetch = [&](int row, int ch, int lane) {
         const int b_ = row / n_tiles;
         const int64_t cb = (int64_t)(row % n_tiles) * kCT;
-        const int r0 = 32 * wv;
+        const int r0 = 16 * wv;
         const int64_t n_0 = (int64_t)ch * kRw;
         const int rows = (int)(L - n_0 < kRw ? L - n_0 : kRw);
         const int64_t tb = ((int64_t)b_ * L + n_0) * Di + cb;  // the tile's first element
         const uint32_t range = (uint32_t)rows * rowb - (uint32_t)cb * 2;
-        const uint32_t vo = ((uint32_t)(r0 + (lane >> 2)) * (uint32_t)Di + 8 * (lane & 3)) * 2;
+        const uint32_t vo = ((uint32_t)(r0 + (lane >> 3)) * (uint32_t)Di + 8 * (lane & 7)) * 2;
         const rsrc_t rh = make_rsrc(hu + tb, range);
         const rsrc_t ra = make_rsrc(a + tb, range);
         const rsrc_t rb = make_rsrc(bg + tb, range);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const uint32_t so = (uint32_t)(16 * k) * rowb;
-            dma16b<false>(rh, vo, so, &sU[H + r0 + 16 * k][0]);
-            dma16b<false>(ra, vo, so, &sAB[0][r0 + 16 * k][0]);
-            dma16b<false>(rb, vo, so, &sAB[1][r0 + 16 * k][0]);
+            const uint32_t so = (uint32_t)(8 * k) * rowb;
+            dma16b<false>(rh, vo, so, &sU[H + r0 + 8 * k][0]);
+            dma16b<false>(ra, vo, so, &sAB[0][r0 + 8 * k][0]);
+            dma16b<false>(rb, vo, so, &sAB[1][r0 + 8 * k][0]);
         }
         if (BLOCK && wv == 0) {
             // rows n0-16 .. n0-1 of u (the first chunk's are replaced after the copy)
             const rsrc_t rs = make_rsrc(hu + (ch > 0 ? tb - 16 * Di : tb),
                                         ch > 0 ? 16u * rowb - (uint32_t)cb * 2 : 0u);
-            const uint32_t vh = ((uint32_t)(lane >> 2) * (uint32_t)Di + 8 * (lane & 3)) * 2;
+            const uint32_t vh = ((uint32_t)(lane >> 3) * (uint32_t)Di + 8 * (lane & 7)) * 2;
             dma16b<false>(rs, vh, 0u, &sU[0][0]);
+            dma16b<false>(rs, vh, 8u * rowb, &sU[8][0]);
         }
         // B rows: 128 bytes, eight lanes per row
         const rsrc_t rB = make_rsrc(Bm + ((int64_t)b_ * L + n_0) * N, (uint32_t)rows * (N * 2));
         const uint32_t vb = (uint32_t)((r0 + (lane >> 3)) * N + 8 * (lane & 7)) * 2;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) dma16b<false>(rB, vb, (uint32_t)(8 * k * N * 2), &sB[r0 + 8 * k][0]);
+        for (int k = 0; k < 2; ++k) dma16b<false>(rB, vb, (uint32_t)(8 * k * N * 2), &sB[r0 + 8 * k][0]);
     };
     // C rows of this wave's 32 tokens as MFMA operands: token lane % 32,
     // K-block kb = states 16 kb + 8 (lane / 32) .. + 7 (rows past L read 0)
     auto load_c = [&](int row, int ch, int lane, bf16x8 (&cv)[4]) {
         const int b_ = row / n_tiles;
-        const int64_t nw = (int64_t)ch * kRw + (int64_t)wv * T;
+        const int64_t nw = (int64_t)ch * kRw + (int64_t)tbw * T;
         const int rows = nw < L ? (int)(L - nw < T ? L - nw : T) : 0;
         const rsrc_t rc =
             make_rsrc(Cm + ((int64_t)b_ * L + (nw < L ? nw : 0)) * N, (uint32_t)rows * (N * 2));
@@ -246,24 +250,14 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
                                         __builtin_amdgcn_raw_buffer_load_b128(rc, vc, 32 * kb, 0));
     };
 
-    // Rows are visited in slot order: workgroup w takes slots w, w + G, w + 2G,
-    // ...  Slots s and s + 8 hold rows 2k and 2k + 1 (neighbouring tiles, whose
-    // 64-byte row pieces share 128-byte lines), and workgroups w and w + 8 are
-    // dispatched to the same XCD (round robin over the eight), so both halves
-    // of a line are asked of one L2 at about the same time.
-    const auto slot_row = [](int sl) { return (sl & ~15) + 2 * (sl & 7) + ((sl >> 3) & 1); };
-    const auto next_slot = [&](int sl) {  // first slot from sl on that holds a row
-        while (sl < n_slots && slot_row(sl) >= n_rows) sl += gridDim.x;
-        return sl;
-    };
-    int slot = next_slot(blockIdx.x), chunk = 0;
-    int row = slot_row(slot);
-    if (slot < n_slots) prefetch(row, 0, threadIdx.x & 63);
-    float xr[8];  // the state carried along the row: wave w, lane (channel, half h) holds
-                  // states 16 w + 8 h .. + 7
+    // workgroup w takes rows w, w + G, w + 2G, ...
+    int row = blockIdx.x, chunk = 0;
+    if (row < n_rows) prefetch(row, 0, threadIdx.x & 63);
+    float xr[8];  // the state carried along the row: wave (t, c), lane (channel, half h)
+                  // holds states 16 t + 8 h .. + 7 of channel 32 c + channel
     float Dc = 0.f, cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f;
 
-    while (slot < n_slots) {
+    while (row < n_rows) {
         wait_mem();
         __syncthreads();  // the tile of (row, chunk) is in LDS
         // lane-dependent values are re-derived every chunk (kept out of
@@ -276,12 +270,12 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
 
         const int bi = row / n_tiles;
         const int64_t cbase = (int64_t)(row % n_tiles) * kCT;
-        const int64_t n0 = (int64_t)chunk * kRw + (int64_t)wv * T;
+        const int64_t n0 = (int64_t)chunk * kRw + (int64_t)tbw * T;
         const int64_t tokbase = (int64_t)bi * L;
         const bool active = n0 < L;
         const int Lw = active ? (int)(L - n0 < T ? L - n0 : T) : 0;  // valid tokens of the wave
         auto tok = [&](int i) -> int { return 8 * (i >> 2) + 4 * hh + (i & 3); };
-        const int64_t c_col = cbase + col;
+        const int64_t c_col = cbase + kCW * chh + col;
 
         if (chunk == 0) {
             // per-channel constants of the row
@@ -294,7 +288,7 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
                 cw3 = conv_w[cc * 4 + 3];
             }
             {
-                const int s0 = 16 * wv + 8 * hh;
+                const int s0 = 16 * tbw + 8 * hh;
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
                     xr[k] = (x0 && c_col < Di) ? x0[((int64_t)bi * Di + c_col) * N + s0 + k] : 0.f;
@@ -313,13 +307,12 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
         }
 
         // the next chunk (of this row, else the first of the next row)
-        int nslot = slot, nrow = row, nchunk = chunk + 1;
+        int nrow = row, nchunk = chunk + 1;
         if (nchunk == n_chunks) {
             nchunk = 0;
-            nslot = next_slot(slot + gridDim.x);
-            nrow = slot_row(nslot);
+            nrow = row + gridDim.x;
         }
-        const bool has_next = nslot < n_slots;
+        const bool has_next = nrow < n_rows;
         bf16x8 Cop[4];
         load_c(row, chunk, lane, Cop);  // arrives during the gates
 
@@ -337,11 +330,11 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
             float cum[16], eb[16], hv[16], tot[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int rg = 32 * wv + 8 * q + 4 * hh;  // tile row of the group's first token
+                const int rg = 32 * tbw + 8 * q + 4 * hh;  // tile row of the group's first token
                 float uw[7];
                 if (BLOCK) {
 #pragma unroll
-                    for (int k = 0; k < 7; ++k) uw[k] = to_f(sU[H + rg - 3 + k][col]);
+                    for (int k = 0; k < 7; ++k) uw[k] = to_f(sU[H + rg - 3 + k][kCW * chh + col]);
                 }
                 float run = 1.f;
 #pragma unroll
@@ -353,10 +346,10 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
                             cw0 * uw[r] + cw1 * uw[r + 1] + cw2 * uw[r + 2] + cw3 * uw[r + 3];
                         h = pre * sigm(pre);
                     } else {
-                        h = to_f(sU[rg + r][col]);
+                        h = to_f(sU[rg + r][kCW * chh + col]);
                     }
-                    float ea = ex2(to_f(sAB[0][rg + r][col]) * -kLog2e);
-                    eb[i] = ex2(to_f(sAB[1][rg + r][col]) * -kLog2e);
+                    float ea = ex2(to_f(sAB[0][rg + r][kCW * chh + col]) * -kLog2e);
+                    eb[i] = ex2(to_f(sAB[1][rg + r][kCW * chh + col]) * -kLog2e);
                     if (TL) {
                         const bool tv = tok(i) < Lw;
                         ea = tv ? ea : 0.f;
@@ -402,12 +395,12 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
         bf16x8 Bop[4], Bsv[2][2];  // Bsv: A operand of B^T W' (rows = states 32 rt + col)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-            Bop[kb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&sB[32 * wv + col][16 * kb + 8 * hh]);
+            Bop[kb] = __builtin_bit_cast(bf16x8, *(const uint4 *)&sB[32 * tbw + col][16 * kb + 8 * hh]);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                Bsv[rt][i >> 3][i & 7] = as_bf(sB[32 * wv + tok(i)][32 * rt + col]);
+                Bsv[rt][i >> 3][i & 7] = as_bf(sB[32 * tbw + tok(i)][32 * rt + col]);
         // (before the copy below: a wait for C issued after it would wait for the copy too)
         f32x16 g = {};
 #pragma unroll
@@ -467,9 +460,10 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
         // half).  Each wave's aggregate is replaced by the state entering that
         // wave; the carried state moves past the whole chunk.
         {
-            const int s0 = 16 * wv + 8 * hh;
+            const int s0 = 16 * tbw + 8 * hh;
 #pragma unroll
-            for (int w = 0; w < W; ++w) {
+            for (int w4 = 0; w4 < 4; ++w4) {
+                const int w = 4 * chh + w4;  // the token blocks of this channel half
                 const float pw = sP[w][col];
                 float4 t[2];
 #pragma unroll
@@ -490,7 +484,7 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
                     for (int k = 0; k < 8; ++k)
                         x_final[((int64_t)bi * Di + c_col) * N + s0 + k] = xr[k];
                 }
-                if (BLOCK && wv == 0 && !upper && conv_state_out) {
+                if (BLOCK && tbw == 0 && !upper && conv_state_out) {
 #pragma unroll
                     for (int k = 0; k < 3; ++k) {
                         const int64_t m = L - 3 + k;
@@ -517,7 +511,7 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
             xs[kb][4] = u1.x, xs[kb][5] = u1.y, xs[kb][6] = u1.z, xs[kb][7] = u1.w;
         }
         if (ckpt && active) {
-            float *cp = ckpt + (((int64_t)bi * n_waves + (int64_t)chunk * W + wv) * N) * Di + cbase;
+            float *cp = ckpt + (((int64_t)bi * n_waves + (int64_t)chunk * 4 + tbw) * N) * Di + cbase + kCW * chh;
             const rsrc_t rc = make_rsrc(cp, (uint32_t)(N * Di * 4));
             const uint32_t vo = c_col < Di ? (uint32_t)((8 * hh) * Di + col) * 4 : kOOB;
 #pragma unroll
@@ -563,7 +557,7 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
             if (BLOCK) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const uint32_t vo = vc ? (uint32_t)((4 * hh + r) * Di + col) * 2 : kOOB;
+                    const uint32_t vo = vc ? (uint32_t)((4 * hh + r) * Di + kCW * chh + col) * 2 : kOOB;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
                         zb[4 * q + r] =
@@ -572,7 +566,7 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const uint32_t vo = vc ? (uint32_t)((4 * hh + r) * Di + col) * 2 : kOOB;
+                const uint32_t vo = vc ? (uint32_t)((4 * hh + r) * Di + kCW * chh + col) * 2 : kOOB;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int i = 4 * q + r;
@@ -587,7 +581,6 @@ __global__ __launch_bounds__(64 * kWv, 2) void fwd_mfma64_kernel(
                 }
             }
         }
-        slot = nslot;
         row = nrow;
         chunk = nchunk;
     }
@@ -606,20 +599,19 @@ hipError_t launch_fwd_mfma64(const FwdArgs &g, hipStream_t stream)
 {
     const int n_tiles = (int)((g.Di + kCT - 1) / kCT);
     const int n_chunks = (int)((g.L + kRw - 1) / kRw);
-    const int64_t n_slots = (g.Bt * n_tiles + 15) / 16 * 16;
-    int64_t slots = 2 * (int64_t)device_cu_count() / 8 * 8;  // two workgroups per CU
-    if (slots < 16) slots = 16;
-    const int64_t grid = n_slots < slots ? n_slots : slots;
+    const int64_t rows = g.Bt * n_tiles;
+    const int64_t slots = (int64_t)device_cu_count();  // one workgroup per CU
+    const int64_t grid = rows < slots ? rows : slots;
     if (g.block)
         hipLaunchKernelGGL(fwd_mfma64_kernel<true>, dim3(grid), dim3(64 * kWv), 0, stream, g.Bt,
-                           g.L, g.Di, n_tiles, n_chunks, (int)n_slots, g.scale, (const bf16 *)g.hu,
+                           g.L, g.Di, n_tiles, n_chunks, g.scale, (const bf16 *)g.hu,
                            (const bf16 *)g.a, (const bf16 *)g.b, (const bf16 *)g.B,
                            (const bf16 *)g.C, g.D, g.x0, (const bf16 *)g.z, g.conv_w,
                            (const bf16 *)g.conv_state, (bf16 *)g.y, g.x_final,
                            (bf16 *)g.conv_state_out, g.ckpt);
     else
         hipLaunchKernelGGL(fwd_mfma64_kernel<false>, dim3(grid), dim3(64 * kWv), 0, stream, g.Bt,
-                           g.L, g.Di, n_tiles, n_chunks, (int)n_slots, g.scale, (const bf16 *)g.hu,
+                           g.L, g.Di, n_tiles, n_chunks, g.scale, (const bf16 *)g.hu,
                            (const bf16 *)g.a, (const bf16 *)g.b, (const bf16 *)g.B,
                            (const bf16 *)g.C, g.D, g.x0, (const bf16 *)g.z, g.conv_w,
                            (const bf16 *)g.conv_state, (bf16 *)g.y, g.x_final,
