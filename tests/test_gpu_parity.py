@@ -43,9 +43,13 @@ SMALL = [
     # bf16, d_state 64, d_inner % 8 == 0: the staged register forward (a ragged
     # 16-channel tile, a partial last chunk)
     (2, 333, 72, 64, "bf16"),
-    # bf16, d_state 64 with at least 32 rows of 32 channels: the matrix-core
+    # bf16, d_state 64 with at least 32 rows of 64 channels: the matrix-core
     # forward (a ragged last tile, a partial last chunk with an idle wave)
     (2, 333, 1000, 64, "bf16"),
+    # bf16, d_state 16, two channel tiles and 33 chunks: every chunk's predecessor
+    # is resident at the same time, so the look-back publishes aggregates first and
+    # walks long chains of them
+    (1, 4100, 128, 16, "bf16"),
 ]
 
 
