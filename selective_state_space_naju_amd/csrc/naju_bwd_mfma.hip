@@ -249,7 +249,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                     const float zv = LD(z, i);
                     const float ez = ex2(-zv * kLog2e);
                     const float sz = rcp(1.f + ez);
-                    const float szm = ez < __builtin_huge_valf() ? ez * sz : 1.f;  // sigma(-z)
+                    const float szm = 1.f - sz;  // sigma(-z): only z sigma(-z) is used, absolute error suffices
                     sGZ[tw][i][lane] = dv * sz * fmaf(zv, szm, 1.f);  // dy SiLU'(z)
                     dv *= zv * sz;                                     // dy SiLU(z)
                 }
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                                           cw2 * win(q, r + 2) + cw3 * win(q, r + 3);
                         const float ep_ = ex2(-pre * kLog2e);
                         const float sp = rcp(1.f + ep_);
-                        const float sm = ep_ < __builtin_huge_valf() ? ep_ * sp : 1.f;
+                        const float sm = 1.f - sp;  // sigma(-pre), used as pre sigma(-pre)
                         hv = pre * sp;
                         hd2[i >> 1][i & 1] = (_Float16)(sp * fmaf(pre, sm, 1.f));  // SiLU'(pre)
                     } else {
