@@ -190,6 +190,12 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
     WsHeader *hdr, uint64_t *agg, uint64_t *incl, const int lazy_agg)
 {
     constexpr int N = 16, T = kFwdT, W = kMfmaW, H = BLOCK ? kHalo : 0;
+    // Scan: each wave reads the second column tile's h, a, b into registers
+    // (two tokens per register) before the first tile's gates, so the next
+    // ticket's copy can start halfway through the gate arithmetic instead of
+    // after it (holding all of the tile in registers spills).  The block's conv
+    // window would need twice the registers, so it keeps the later start.
+    constexpr bool EARLY = !BLOCK;
     static_assert(T == 32, "one 32x32 MFMA tile of tokens per wave");
     // wave-uniform (readfirstlane keeps what derives from it in scalar registers)
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -263,8 +269,22 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         }
     };
 
+    // D of a ticket's channels (32 j + lane % 32), loaded one ticket ahead and
+    // before the copy: a load issued after the copy would, when waited for, also
+    // wait for the copy (memory operations complete in order)
+    float Dn[2] = {0.f, 0.f};
+    auto loadD = [&](uint32_t tk, int ln) {
+        const int rm = (int)(tk % per_chunk);
+        const int64_t cb = (int64_t)(rm % n_tiles) * 64;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t c = cb + 32 * j + (ln & 31);
+            Dn[j] = D[c < Di ? c : 0];
+        }
+    };
     if (threadIdx.x == 0) s_epoch = (ld_agent(&hdr->epoch) + 1u) & 0x3FFFFFFFu;
     uint32_t cur = blockIdx.x;
+    if (EARLY && cur < total) loadD(cur, threadIdx.x & 63);
     if (cur < total && wv >= 2) prefetch(cur, threadIdx.x & 63);
     __syncthreads();
     const uint32_t ep = s_epoch;
@@ -314,16 +334,41 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
             Cop = __builtin_bit_cast(bf16x8, col < Lw ? qc : z4);
 #pragma unroll
             for (int s = 0; s < 8; ++s) Csc[s] = (__bf16)((float)Cop[s] * scale);
+            // (the reads are made unconditional: a select after each read would
+            // otherwise become a branch around it, with a wait of its own)
+            uint32_t bv[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const bf16 v = sBC[0][32 * wv + tok(i)][col & 15];
-                Bsv[i >> 3][i & 7] = as_bf((col < N && tok(i) < Lw) ? v : (bf16)0);
-            }
+            for (int i = 0; i < 16; ++i) bv[i] = sBC[0][32 * wv + tok(i)][col & 15];
+            asm volatile(""
+                         : "+v"(bv[0]), "+v"(bv[1]), "+v"(bv[2]), "+v"(bv[3]), "+v"(bv[4]),
+                           "+v"(bv[5]), "+v"(bv[6]), "+v"(bv[7]), "+v"(bv[8]), "+v"(bv[9]),
+                           "+v"(bv[10]), "+v"(bv[11]), "+v"(bv[12]), "+v"(bv[13]),
+                           "+v"(bv[14]), "+v"(bv[15]));
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                Bsv[i >> 3][i & 7] = as_bf((col < N && tok(i) < Lw) ? (bf16)bv[i] : (bf16)0);
         }
 
         // ------------------------------------------------------ gates, W', P
         // Tokens past the end of the sequence (only in the last wave of a row)
         // get f = 1 and w = 0, so they leave the state and the aggregate alone.
+        const uint32_t nxt = cur + gridDim.x;
+        const float Dcur[2] = {Dn[0], Dn[1]};
+        uint32_t rw[3][8];  // h, a, b of column tile 1, tokens (2p, 2p + 1) in the two halves
+        if constexpr (EARLY) {
+            const int chn = 32 + col;
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const int r0 = 32 * wv + tok(2 * p), r1 = 32 * wv + tok(2 * p + 1);
+                rw[0][p] = (uint32_t)sU[r0][chn] | ((uint32_t)sU[r1][chn] << 16);
+                rw[1][p] = (uint32_t)sAB[0][r0][chn] | ((uint32_t)sAB[0][r1][chn] << 16);
+                rw[2][p] = (uint32_t)sAB[1][r0][chn] | ((uint32_t)sAB[1][r1][chn] << 16);
+            }
+        }
+        auto raw = [&](int t, int i) -> float {
+            const uint32_t v = rw[t][i >> 1];
+            return __uint_as_float((i & 1) ? (v & 0xffff0000u) : (v << 16));
+        };
         float Pv[2][16], FT[2][16];
         bf16x8 Whi[2][2], Wlo[2][2];
         float Ptot[2];
@@ -332,10 +377,18 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
             constexpr bool TL = decltype(tail_c)::value;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
+                if (EARLY && j == 1) {
+                    __syncthreads();  // every wave holds what it needs of the tile
+                    if (nxt < total) {
+                        loadD(nxt, lane);
+                        if (wv >= 2) prefetch(nxt, lane);
+                    }
+                }
+                const bool rg1 = EARLY && j == 1;  // tile 1 from registers
                 const int chn = 32 * j + col;
                 const int64_t c = cbase + chn;
                 const int64_t cc = c < Di ? c : 0;
-                const float Dc = D[cc];
+                const float Dc = EARLY ? Dcur[j] : D[cc];
                 float cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f;
                 if (BLOCK) {
                     cw0 = conv_w[cc * 4 + 0];
@@ -365,10 +418,10 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                                 cw0 * uw[r] + cw1 * uw[r + 1] + cw2 * uw[r + 2] + cw3 * uw[r + 3];
                             h = pre * sigm(pre);
                         } else {
-                            h = to_f(sU[rg + r][chn]);
+                            h = rg1 ? raw(0, i) : to_f(sU[rg + r][chn]);
                         }
-                        float ea = ex2(to_f(sAB[0][rg + r][chn]) * -kLog2e);
-                        eb[i] = ex2(to_f(sAB[1][rg + r][chn]) * -kLog2e);
+                        float ea = ex2((rg1 ? raw(1, i) : to_f(sAB[0][rg + r][chn])) * -kLog2e);
+                        eb[i] = ex2((rg1 ? raw(2, i) : to_f(sAB[1][rg + r][chn])) * -kLog2e);
                         if (TL) {
                             const bool tv = tok(i) < Lw;
                             ea = tv ? ea : 0.f;
@@ -410,9 +463,10 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         else
             gates(std::false_type{});
         const bool wave_ok = __all(ok);
-        __syncthreads();  // every wave is done with the tile
-        const uint32_t nxt = cur + gridDim.x;
-        if (nxt < total && wv >= 2) prefetch(nxt, lane);
+        if constexpr (!EARLY) {
+            __syncthreads();  // every wave is done with the tile
+            if (nxt < total && wv >= 2) prefetch(nxt, lane);
+        }
 
         // ------------------------------------- chunk aggregates (P_T, S) -> LDS
         // S = P_T (W'^T B), formed as B^T W' so each lane holds its own channel
