@@ -375,8 +375,11 @@ static bool use_mfma(const FwdArgs &g)
 {
     const auto al16 = [](const void *p) { return ((uintptr_t)p % 16) == 0; };
     // (buffer ranges of 32 token rows / 16 checkpoint rows stay below 2^31 bytes)
+    const auto al = [](const void *p, unsigned n) { return ((uintptr_t)p % n) == 0; };
+    // (y and z are accessed as channel pairs, the checkpoints as float pairs)
     return !forced_rr() && g.io == 1 && g.N == 16 && g.Di % 8 == 0 && g.Di < ((int64_t)1 << 24) &&
-           al16(g.B) && al16(g.C) && al16(g.hu) && al16(g.a) && al16(g.b);
+           al16(g.B) && al16(g.C) && al16(g.hu) && al16(g.a) && al16(g.b) && al(g.y, 4) &&
+           al(g.z, 4) && al(g.ckpt, 8);
 }
 
 hipError_t launch_fwd(const FwdArgs &g, hipStream_t stream)

@@ -15,8 +15,10 @@
 // split into bf16 hi + lo parts (x = hi + lo to ~2^-17 relative), so the
 // products keep close to fp32 accuracy with fp32 accumulation.
 //
-// Lane layout: lane l owns column l%32 of each 32-wide MFMA tile and, in its
-// half h = l/32, the 16 chunk tokens {8q + 4h + r}.  That set is both the
+// Lane layout: lane l owns column l%32 of the two 32-wide MFMA column tiles,
+// which are the adjacent channels 2(l%32) and 2(l%32) + 1 (so a lane's y, z and
+// checkpoint values of a token are one 4- or 8-byte access), and, in its half
+// h = l/32, the 16 chunk tokens {8q + 4h + r}.  That set is both the
 // lane's row set in the 32x32 accumulator and (by choosing the K-slot order)
 // its K-slots in the A/B operands, so gates, W', P and the outputs of a token
 // all live in the lane that needs them.
@@ -269,7 +271,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         }
     };
 
-    // D of a ticket's channels (32 j + lane % 32), loaded one ticket ahead and
+    // D of a ticket's channels (2 (lane % 32) + j), loaded one ticket ahead and
     // before the copy: a load issued after the copy would, when waited for, also
     // wait for the copy (memory operations complete in order)
     float Dn[2] = {0.f, 0.f};
@@ -278,7 +280,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         const int64_t cb = (int64_t)(rm % n_tiles) * 64;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int64_t c = cb + 32 * j + (ln & 31);
+            const int64_t c = cb + 2 * (ln & 31) + j;
             Dn[j] = D[c < Di ? c : 0];
         }
     };
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         const float Dcur[2] = {Dn[0], Dn[1]};
         uint32_t rw[3][8];  // h, a, b of column tile 1, tokens (2p, 2p + 1) in the two halves
         if constexpr (EARLY) {
-            const int chn = 32 + col;
+            const int chn = 2 * col + 1;
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
                 const int r0 = 32 * wv + tok(2 * p), r1 = 32 * wv + tok(2 * p + 1);
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                     }
                 }
                 const bool rg1 = EARLY && j == 1;  // tile 1 from registers
-                const int chn = 32 * j + col;
+                const int chn = 2 * col + j;
                 const int64_t c = cbase + chn;
                 const int64_t cc = c < Di ? c : 0;
                 const float Dc = EARLY ? Dcur[j] : D[cc];
@@ -481,8 +483,8 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
                     sacc = mfma(Bsv[kb], Wlo[j][kb], sacc);
                 }
 #pragma unroll
-                for (int i = 0; i < 8; ++i) sS[wv][tok(i)][32 * j + col] = sacc[i] * Ptot[j];
-                if (!upper) sP[wv][32 * j + col] = Ptot[j];
+                for (int i = 0; i < 8; ++i) sS[wv][tok(i)][2 * col + j] = sacc[i] * Ptot[j];
+                if (!upper) sP[wv][2 * col + j] = Ptot[j];
             }
         } else {
             float P, S[16];
@@ -649,12 +651,12 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         __syncthreads();
 
         // --------------------- this wave's entering state, in the B-operand
-        // layout (channel 32j + col, states 8h..8h+7): the workgroup's entering
+        // layout (channel 2 col + j, states 8h..8h+7): the workgroup's entering
         // state carried through the waves before it
         float xs[2][8];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int chn = 32 * j + col;
+            const int chn = 2 * col + j;
 #pragma unroll
             for (int k = 0; k < 8; ++k) xs[j][k] = sX[8 * hh + k][chn];
             for (int w = 0; w < wv; ++w) {
@@ -666,15 +668,15 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
         if (ckpt && active) {
             float *cp = ckpt + (((int64_t)bi * n_waves + (int64_t)chunk * W + wv) * N) * Di + cbase;
             const rsrc_t rc = make_rsrc(cp, (uint32_t)(N * Di * 4));
+            // channels 2 col and 2 col + 1 (both valid or neither: Di is even)
+            const uint32_t vo = cbase + 2 * col < Di ? (uint32_t)((8 * hh) * Di + 2 * col) * 4 : kOOB;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const uint32_t vo =
-                    cbase + 32 * j + col < Di ? (uint32_t)((8 * hh) * Di + 32 * j + col) * 4 : kOOB;
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    // (nontemporal: read back only by the backward, much later)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xs[j][k]), rc, vo,
-                                                          (uint32_t)(k * Di) * 4, 2);
+            for (int k = 0; k < 8; ++k) {
+                const f32x2 v = {xs[0][k], xs[1][k]};
+                // (nontemporal: read back only by the backward, much later)
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rc, vo,
+                                                      (uint32_t)(k * Di) * 4, 2);
             }
         }
 
@@ -698,42 +700,45 @@ __global__ __launch_bounds__(64 * kMfmaW, 2) void fwd_mfma_kernel(
             const rsrc_t ry = make_rsrc(y + ebase, (uint32_t)Lw * row2);
             const rsrc_t rz = make_rsrc(BLOCK ? (const void *)(z + ebase) : (const void *)y,
                                         BLOCK ? (uint32_t)Lw * row2 : 0u);
+            // the lane's channel pair (2 col, 2 col + 1): both valid or neither (Di is even)
+            const bool vc = cbase + 2 * col < Di;
+            // z first, all at once: the y stores below may alias it as far as the
+            // compiler can tell, so a load placed between them would wait out a
+            // full round trip per element
+            uint32_t zb[16];
+            if (BLOCK) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t vo = vc ? (uint32_t)((4 * hh + r) * Di + 2 * col) * 2 : kOOB;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        zb[4 * q + r] =
+                            __builtin_amdgcn_raw_buffer_load_b32(rz, vo, (uint32_t)(8 * q) * row2, 0);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const bool vc = cbase + 32 * j + col < Di;
-                // z of the column tile first, all at once: the y stores below may
-                // alias it as far as the compiler can tell, so a load placed between
-                // them would wait out a full round trip per element
-                uint32_t zb[16];
-                if (BLOCK) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const uint32_t vo =
-                            vc ? (uint32_t)((4 * hh + r) * Di + 32 * j + col) * 2 : kOOB;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            zb[4 * q + r] = __builtin_amdgcn_raw_buffer_load_b16(
-                                rz, vo, (uint32_t)(8 * q) * row2, 0);
-                    }
-                }
                 bf16x8 xh, xl;
                 split8(xs[j], xh, xl);
                 Y[j] = mfma(Csc, xh, Y[j]);
                 Y[j] = mfma(Csc, xl, Y[j]);
+            }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const uint32_t vo = vc ? (uint32_t)((4 * hh + r) * Di + 32 * j + col) * 2 : kOOB;
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t vo = vc ? (uint32_t)((4 * hh + r) * Di + 2 * col) * 2 : kOOB;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int i = 4 * q + r;
-                        const uint32_t so = (uint32_t)(8 * q) * row2;
-                        float yv = Pv[j][i] * Y[j][i];
-                        if (BLOCK) {
-                            const float zv = __uint_as_float(zb[i] << 16);
-                            yv *= zv * sigm(zv);
-                        }
-                        __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(yv), ry, vo, so, 0);
+                for (int q = 0; q < 4; ++q) {
+                    const int i = 4 * q + r;
+                    const uint32_t so = (uint32_t)(8 * q) * row2;
+                    f32x2 yv = {Pv[0][i] * Y[0][i], Pv[1][i] * Y[1][i]};
+                    if (BLOCK) {
+                        const float z0 = __uint_as_float(zb[i] << 16);
+                        const float z1 = __uint_as_float(zb[i] & 0xffff0000u);
+                        yv[0] *= z0 * sigm(z0);
+                        yv[1] *= z1 * sigm(z1);
                     }
+                    const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(yv, bf16x2));
+                    __builtin_amdgcn_raw_buffer_store_b32(pk, ry, vo, so, 0);
                 }
             }
         }
