@@ -210,6 +210,47 @@ naju_status_t naju_block_step(const naju_dims_t *dims, const void *u, const void
                               const void *b, const void *B, const void *C, const float *D,
                               float *x, void *y, void *stream);
 
+/*
+ * Mixer layer forward (bf16 io only): the block flowchart of the same page
+ * ("Background and main changes") around the scan -- input projection, causal
+ * depthwise conv + SiLU, forget / write gate and B/C projections, the block
+ * scan with readout, feedthrough and SiLU(z) modulation, output projection and
+ * residual.  Per token, with row vectors and weights stored [in][out]:
+ *     u = xn W_u;  z = xn W_z;  h = SiLU(conv(u))             (conv as naju_block_fwd)
+ *     a = h W_a + a_bias;  b = h W_b + b_bias;  B = h W_B;  C = h W_C
+ *     y = naju_block_fwd(u, z, conv_w, conv_state, a, b, B, C, D)
+ *     out = y W_out + res
+ * u, z, h, a, b, B, C and y are bf16 intermediates in the workspace (each
+ * rounded to nearest even from fp32); the projections read the bf16 h, the
+ * scan recomputes h from u in fp32.  The projections run through hipBLASLt
+ * (fp32 accumulation); its handle is created on a device's first call and
+ * kept for the process.
+ *   dims          batch, seqlen, d_inner, d_state as elsewhere; d_conv == 4;
+ *                 io == NAJU_BF16; d_inner % 8 == 0
+ *   d_model       width of the layer's input and output, % 8 == 0
+ *   xn            [Bt][L][d_model] bf16     normalized tokens
+ *   res           [Bt][L][d_model] bf16 or NULL (= no residual)
+ *   W_u, W_z      [d_model][d_inner] bf16   input projection (conv branch, gate branch)
+ *   conv_w        [d_inner][4] fp32;  conv_state [Bt][3][d_inner] bf16 or NULL
+ *   W_a, W_b      [d_inner][d_inner] bf16;  a_bias, b_bias [d_inner] fp32
+ *   W_B, W_C      [d_inner][d_state] bf16
+ *   D             [d_inner] fp32
+ *   W_out         [d_inner][d_model] bf16
+ *   out           [Bt][L][d_model] bf16 (written)
+ *   ws            naju_mixer_workspace_bytes() bytes, 256-byte aligned, zero-filled
+ *                 before first use (as for the other entry points)
+ * Matrices, conv_w and conv_state must be 16-byte aligned.  A hipBLASLt
+ * failure returns NAJU_EHIP; work already enqueued by the call is not undone.
+ */
+size_t naju_mixer_workspace_bytes(const naju_dims_t *dims, int64_t d_model);
+naju_status_t naju_mixer_fwd(const naju_dims_t *dims, int64_t d_model, const void *xn,
+                             const void *res, const void *W_u, const void *W_z,
+                             const float *conv_w, const void *conv_state, const void *W_a,
+                             const float *a_bias, const void *W_b, const float *b_bias,
+                             const void *W_B, const void *W_C, const float *D,
+                             const void *W_out, void *out, void *ws, size_t ws_bytes,
+                             void *stream);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char *naju_last_error(void);
 

@@ -164,3 +164,47 @@ def block_bwd(u, z, w, a, b, B, C, D, x0, dy, dx_final=None, conv_state=None):
                               _p(out["dconv_state"]), _p(out["da"]), _p(out["db"]),
                               _p(out["dB"]), _p(out["dC"]), _p(out["dD"]), _p(out["dx0"]))
     return out
+
+
+def round_bf16(x):
+    """Values rounded to bfloat16 the way a device computing in fp32 stores them:
+    first to the nearest fp32, then to the nearest bfloat16 (ties to the even
+    significand).  Returns fp64 arrays holding the bf16 values."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    bits = f.view(np.uint32).astype(np.uint64)
+    keep = bits >> np.uint64(16)
+    rest = bits & np.uint64(0xFFFF)
+    up = (rest > 0x8000) | ((rest == 0x8000) & ((keep & np.uint64(1)) == 1))
+    keep = keep + up.astype(np.uint64)
+    out = (keep << np.uint64(16)).astype(np.uint32).view(np.float32).astype(np.float64)
+    return out.reshape(np.shape(x))
+
+
+def mixer_fwd(xn, W_u, W_z, conv_w, W_a, a_bias, W_b, b_bias, W_B, W_C, D, W_out, res=None,
+              conv_state=None):
+    """The mixer layer of the block flowchart (reproduction README, "Background
+    and main changes") around block_fwd, in fp64 with bf16 storage of the
+    intermediates: returns a dict with u, z, h, a, b, B, C, y and out.
+
+        u = xn W_u, z = xn W_z;  h = SiLU(conv(u));  a = h W_a + a_bias,
+        b = h W_b + b_bias, B = h W_B, C = h W_C;  y = block_fwd(u, z, ...);
+        out = y W_out + res
+    Every intermediate is stored as bf16 (round_bf16) before its next use; the
+    projections read the stored h, the scan recomputes h from u (block_fwd).
+    The matrix products are numpy matmuls in fp64."""
+    f = lambda t: None if t is None else np.asarray(t, dtype=np.float64)
+    xn, W_u, W_z, W_a, W_b, W_B, W_C, W_out = map(f, (xn, W_u, W_z, W_a, W_b, W_B, W_C, W_out))
+    u = round_bf16(xn @ W_u)
+    z = round_bf16(xn @ W_z)
+    _, h = conv_silu(u, conv_w, conv_state)
+    h = round_bf16(h)
+    a = round_bf16(h @ W_a + f(a_bias))
+    b = round_bf16(h @ W_b + f(b_bias))
+    B = round_bf16(h @ W_B)
+    C = round_bf16(h @ W_C)
+    y, _, _ = block_fwd(u, z, conv_w, a, b, B, C, D, conv_state=conv_state)
+    y = round_bf16(y)
+    o = y @ W_out
+    if res is not None:
+        o = o + f(res)
+    return dict(u=u, z=z, h=h, a=a, b=b, B=B, C=C, y=y, out=round_bf16(o))

@@ -26,8 +26,8 @@ D_CONV = 4
 # every function the header declares (the CPU tests check the exports)
 EXPORTS = ("naju_workspace_bytes", "naju_ckpt_bytes", "naju_workspace_init",
            "naju_workspace_check", "naju_scan_fwd", "naju_scan_bwd", "naju_block_fwd",
-           "naju_block_bwd", "naju_scan_step", "naju_block_step", "naju_last_error",
-           "naju_version")
+           "naju_block_bwd", "naju_scan_step", "naju_block_step", "naju_mixer_workspace_bytes",
+           "naju_mixer_fwd", "naju_last_error", "naju_version")
 
 
 class NajuError(RuntimeError):
@@ -80,6 +80,10 @@ def lib() -> ctypes.CDLL:
         L.naju_scan_step.restype = st
         L.naju_block_step.argtypes = [dp] + [vp] * 12
         L.naju_block_step.restype = st
+        L.naju_mixer_workspace_bytes.argtypes = [dp, ctypes.c_int64]
+        L.naju_mixer_workspace_bytes.restype = sz
+        L.naju_mixer_fwd.argtypes = [dp, ctypes.c_int64] + [vp] * 16 + [sz, vp]
+        L.naju_mixer_fwd.restype = st
         L.naju_last_error.argtypes = []
         L.naju_last_error.restype = ctypes.c_char_p
         L.naju_version.argtypes = []
@@ -336,3 +340,42 @@ def block_step(u, z, conv_w, conv_state, a, b, B, C, D, x):
                                 _p(a), _p(b), _p(B), _p(C), _p(D), _p(x), _p(y),
                                 stream_handle(dev)))
     return y
+
+
+def mixer_fwd(xn, W_u, W_z, conv_w, W_a, a_bias, W_b, b_bias, W_B, W_C, D, W_out, res=None,
+              conv_state=None, *, ws=None):
+    """out = naju_mixer_fwd(...): the mixer layer around the block scan (bf16)."""
+    Bt, L, dm = xn.shape
+    Di = W_u.shape[1]
+    N = W_B.shape[1]
+    dt, dev = xn.dtype, xn.device
+    if dt != torch.bfloat16:
+        raise TypeError("the mixer layer takes bfloat16 activations and weights")
+    _req(xn, "xn", (Bt, L, dm), dt, dev)
+    _opt(res, "res", (Bt, L, dm), dt, dev)
+    _req(W_u, "W_u", (dm, Di), dt, dev)
+    _req(W_z, "W_z", (dm, Di), dt, dev)
+    _req(conv_w, "conv_w", (Di, D_CONV), torch.float32, dev)
+    _opt(conv_state, "conv_state", (Bt, D_CONV - 1, Di), dt, dev)
+    _req(W_a, "W_a", (Di, Di), dt, dev)
+    _req(W_b, "W_b", (Di, Di), dt, dev)
+    _req(a_bias, "a_bias", (Di,), torch.float32, dev)
+    _req(b_bias, "b_bias", (Di,), torch.float32, dev)
+    _req(W_B, "W_B", (Di, N), dt, dev)
+    _req(W_C, "W_C", (Di, N), dt, dev)
+    _req(D, "D", (Di,), torch.float32, dev)
+    _req(W_out, "W_out", (Di, dm), dt, dev)
+    dims = make_dims(Bt, L, Di, N, BF16)
+    out = torch.empty((Bt, L, dm), dtype=dt, device=dev)
+    if ws is None:
+        d = torch.device(dev)
+        key = (d.index, torch.cuda.current_stream(d).cuda_stream, "mixer", Bt, L, dm, Di, N)
+        ws = _ws_cache.get(key)
+        if ws is None:
+            ws = Workspace(int(lib().naju_mixer_workspace_bytes(ctypes.byref(dims), dm)), d)
+            _ws_cache[key] = ws
+    check(lib().naju_mixer_fwd(ctypes.byref(dims), dm, _p(xn), _p(res), _p(W_u), _p(W_z),
+                               _p(conv_w), _p(conv_state), _p(W_a), _p(a_bias), _p(W_b),
+                               _p(b_bias), _p(W_B), _p(W_C), _p(D), _p(W_out), _p(out), ws.ptr,
+                               ws.nbytes, stream_handle(dev)))
+    return out

@@ -319,6 +319,72 @@ static naju_status_t bwd_common(bool block, const naju_dims_t *d, const void *hu
     return hip_status(launch_bwd(g, st), "backward launch");
 }
 
+static naju_status_t mixer_common(const naju_dims_t *d, int64_t dm, const void *xn,
+                                  const void *res, const void *W_u, const void *W_z,
+                                  const float *conv_w, const void *conv_state, const void *W_a,
+                                  const float *a_bias, const void *W_b, const float *b_bias,
+                                  const void *W_B, const void *W_C, const float *D,
+                                  const void *W_out, void *out, void *ws, size_t ws_bytes,
+                                  void *stream)
+{
+    TRY(check_dims(d, true));
+    if (d->io != NAJU_BF16) return fail(NAJU_EUNSUPPORTED, "the mixer is built for bf16 io only");
+    if (dm <= 0 || d->d_inner <= 0)
+        return fail(NAJU_EINVAL, "d_model and d_inner must be positive (d_model=%lld d_inner=%lld)",
+                    (long long)dm, (long long)d->d_inner);
+    if (dm % 8 || d->d_inner % 8)
+        return fail(NAJU_EUNSUPPORTED, "d_model and d_inner must be multiples of 8");
+    if (dm > ((int64_t)1 << 24) || d->d_inner >= ((int64_t)1 << 24))
+        return fail(NAJU_EINVAL, "d_model or d_inner too large");
+    if (d->batch == 0 || d->seqlen == 0) return NAJU_OK;
+    TRY(need(xn, "xn", 16));
+    TRY(opt(res, "res", 16));
+    TRY(need(W_u, "W_u", 16));
+    TRY(need(W_z, "W_z", 16));
+    TRY(need(conv_w, "conv_w", 16));
+    TRY(opt(conv_state, "conv_state", 16));
+    TRY(need(W_a, "W_a", 16));
+    TRY(need(a_bias, "a_bias", 4));
+    TRY(need(W_b, "W_b", 16));
+    TRY(need(b_bias, "b_bias", 4));
+    TRY(need(W_B, "W_B", 16));
+    TRY(need(W_C, "W_C", 16));
+    TRY(need(D, "D", 4));
+    TRY(need(W_out, "W_out", 16));
+    TRY(need(out, "out", 16));
+    const size_t need_b = mixer_ws_bytes(d->batch, d->seqlen, d->d_inner, d->d_state);
+    if (!ws) return fail(NAJU_EWORKSPACE, "workspace is NULL (needs %zu bytes)", need_b);
+    if (((uintptr_t)ws) % 256) return fail(NAJU_EINVAL, "workspace is not 256-byte aligned");
+    if (ws_bytes < need_b)
+        return fail(NAJU_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need_b);
+    MixerArgs g{};
+    g.Bt = d->batch;
+    g.L = d->seqlen;
+    g.dm = dm;
+    g.Di = d->d_inner;
+    g.N = d->d_state;
+    g.scale = (float)(1.0 / sqrt((double)d->d_state));
+    g.xn = xn;
+    g.res = res;
+    g.W_u = W_u;
+    g.W_z = W_z;
+    g.conv_w = conv_w;
+    g.conv_state = conv_state;
+    g.W_a = W_a;
+    g.b_bias = b_bias;
+    g.a_bias = a_bias;
+    g.W_b = W_b;
+    g.W_B = W_B;
+    g.W_C = W_C;
+    g.D = D;
+    g.W_out = W_out;
+    g.out = out;
+    g.ws = ws;
+    const char *e = mixer_fwd(g, (hipStream_t)stream);
+    if (e) return fail(NAJU_EHIP, "mixer: %s", e);
+    return NAJU_OK;
+}
+
 }  // namespace naju
 
 using namespace naju;
@@ -437,6 +503,24 @@ naju_status_t naju_block_fwd(const naju_dims_t *dims, const void *u, const void 
 {
     return fwd_common(true, dims, u, z, conv_w, conv_state, a, b, B, C, D, x0, y, x_final,
                       conv_state_out, ckpt, ws, ws_bytes, stream);
+}
+
+size_t naju_mixer_workspace_bytes(const naju_dims_t *dims, int64_t d_model)
+{
+    if (check_dims(dims, true) != NAJU_OK || d_model <= 0) return 0;
+    return mixer_ws_bytes(dims->batch, dims->seqlen, dims->d_inner, dims->d_state);
+}
+
+naju_status_t naju_mixer_fwd(const naju_dims_t *dims, int64_t d_model, const void *xn,
+                             const void *res, const void *W_u, const void *W_z,
+                             const float *conv_w, const void *conv_state, const void *W_a,
+                             const float *a_bias, const void *W_b, const float *b_bias,
+                             const void *W_B, const void *W_C, const float *D,
+                             const void *W_out, void *out, void *ws, size_t ws_bytes,
+                             void *stream)
+{
+    return mixer_common(dims, d_model, xn, res, W_u, W_z, conv_w, conv_state, W_a, a_bias, W_b,
+                        b_bias, W_B, W_C, D, W_out, out, ws, ws_bytes, stream);
 }
 
 naju_status_t naju_scan_bwd(const naju_dims_t *dims, const void *h, const void *a,

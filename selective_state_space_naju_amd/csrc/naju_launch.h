@@ -210,4 +210,24 @@ hipError_t launch_empty_seq(int io, int64_t Bt, int64_t Di, int64_t N, const flo
                             float *x_final, const void *conv_state, void *conv_state_out,
                             hipStream_t stream);
 
+// mixer layer (bf16): projections around the block forward
+struct MixerArgs {
+    int64_t Bt, L, dm, Di, N;
+    float scale;
+    const void *xn, *res;            // [Bt][L][dm]; res may be null
+    const void *W_u, *W_z;           // [dm][Di]
+    const float *conv_w;             // [Di][4]
+    const void *conv_state;          // [Bt][3][Di] or null
+    const void *W_a, *W_b;           // [Di][Di]
+    const float *a_bias, *b_bias;    // [Di]
+    const void *W_B, *W_C;           // [Di][N]
+    const float *D;                  // [Di]
+    const void *W_out;               // [Di][dm]
+    void *out;                       // [Bt][L][dm]
+    void *ws;                        // mixer_plan layout
+};
+size_t mixer_ws_bytes(int64_t Bt, int64_t L, int64_t Di, int64_t N);
+// enqueues the layer; returns nullptr, or a message on failure
+const char *mixer_fwd(const MixerArgs &g, hipStream_t stream);
+
 }  // namespace naju

@@ -143,3 +143,43 @@ def draw_workload(w: Workload, **kw) -> dict:
                 backward=w.backward)
     args.update(kw)
     return draw(w.Bt, w.L, w.Di, w.N, **args)
+
+
+# ------------------------------------------------------------ mixer layer
+# The layer's weights are drawn so that its activations follow the same
+# distributions as the scan workloads: u ~ N(0, 1) (W_u, W_z std 1/sqrt(d_model)
+# on unit-normal tokens), and a = h W_a + 5, b = h W_b - 2 with unit spread,
+# where h = SiLU(conv(u)) has mean square ~0.355 for std 0.5 taps (so W_a, W_b,
+# W_B, W_C have std 1/sqrt(0.355 d_inner)); the gate biases are the page's
+# preserve-first initialisation (5 and -2); W_out has std 1/sqrt(d_inner).
+MIXER_DRAW_ORDER = ("xn", "res", "W_u", "W_z", "conv_w", "W_a", "W_b", "W_B", "W_C", "D",
+                    "W_out", "conv_state")
+
+MIXER_WORKLOADS = {
+    "mixer_bf16_b8_l2048_dm768_d1536_n16": dict(Bt=8, L=2048, dm=768, Di=1536, N=16, seed=1005),
+}
+
+
+def draw_mixer(Bt: int, L: int, dm: int, Di: int, N: int, *, seed: int = 0,
+               residual: bool = True, conv_state: bool = False, K: int = 4) -> dict:
+    """One input set of the mixer layer (float32 arrays; bf16 ones already rounded)."""
+    rng = np.random.default_rng(seed)
+    h_ms = 0.355
+    shapes = {"xn": (Bt, L, dm), "res": (Bt, L, dm), "W_u": (dm, Di), "W_z": (dm, Di),
+              "conv_w": (Di, K), "W_a": (Di, Di), "W_b": (Di, Di), "W_B": (Di, N),
+              "W_C": (Di, N), "D": (Di,), "W_out": (Di, dm), "conv_state": (Bt, K - 1, Di)}
+    scale = {"W_u": dm ** -0.5, "W_z": dm ** -0.5, "conv_w": 0.5, "W_a": (h_ms * Di) ** -0.5,
+             "W_b": (h_ms * Di) ** -0.5, "W_B": (h_ms * Di) ** -0.5, "W_C": (h_ms * Di) ** -0.5,
+             "W_out": Di ** -0.5}
+    fp32 = {"conv_w", "D"}
+    out = {}
+    for name in MIXER_DRAW_ORDER:
+        if (name == "res" and not residual) or (name == "conv_state" and not conv_state):
+            continue
+        x = rng.standard_normal(shapes[name], dtype=np.float32)
+        if name in scale:
+            x *= np.float32(scale[name])
+        out[name] = x if name in fp32 else bf16_round(x)
+    out["a_bias"] = np.full(Di, 5.0, dtype=np.float32)
+    out["b_bias"] = np.full(Di, -2.0, dtype=np.float32)
+    return out

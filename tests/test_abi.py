@@ -123,6 +123,37 @@ def test_validation_errors_step(lib):
     assert lib.naju_block_step(ctypes.byref(dims(d_conv=3)), *vb) == nb.EUNSUPPORTED
 
 
+def test_validation_errors_mixer(lib):
+    # dims, d_model, xn, res, W_u, W_z, conv_w, conv_state, W_a, a_bias, W_b, b_bias, W_B, W_C,
+    # D, W_out, out, ws, ws_bytes, stream
+    def call(d, dm=64, **over):
+        args = dict(xn=FAKE, res=None, W_u=FAKE, W_z=FAKE, conv_w=FAKE, conv_state=None,
+                    W_a=FAKE, a_bias=FAKE, W_b=FAKE, b_bias=FAKE, W_B=FAKE, W_C=FAKE, D=FAKE,
+                    W_out=FAKE, out=FAKE, ws=FAKE, wsb=1 << 40)
+        args.update(over)
+        v = [args[k] for k in ("xn", "res", "W_u", "W_z", "conv_w", "conv_state", "W_a",
+                               "a_bias", "W_b", "b_bias", "W_B", "W_C", "D", "W_out", "out",
+                               "ws")]
+        return lib.naju_mixer_fwd(ctypes.byref(d), dm, *v, args["wsb"], None)
+    d = dims(d_inner=128)
+    assert call(dims(d_inner=128, io=nb.F32)) == nb.EUNSUPPORTED
+    assert call(dims(d_inner=100)) == nb.EUNSUPPORTED  # d_inner % 8
+    assert call(d, dm=60) == nb.EUNSUPPORTED
+    assert call(d, dm=0) == nb.EINVAL
+    assert call(dims(d_inner=128, d_conv=3)) == nb.EUNSUPPORTED
+    assert call(d, W_a=None) == nb.EINVAL
+    assert "W_a is NULL" in nb.last_error()
+    assert call(d, W_out=FAKE + 2) == nb.EINVAL
+    assert "aligned" in nb.last_error()
+    assert call(d, ws=None) == nb.EWORKSPACE
+    assert call(d, wsb=1024) == nb.EWORKSPACE
+    assert call(dims(d_inner=128, batch=0), xn=None, ws=None) == nb.OK
+    # the workspace holds u, z, h, a, b, y, B, C, the GEMM workspace and the block forward's
+    w = lib.naju_mixer_workspace_bytes(ctypes.byref(dims(batch=8, seqlen=2048, d_inner=1536)), 768)
+    assert w > 6 * 8 * 2048 * 1536 * 2 + 2 * 8 * 2048 * 16 * 2
+    assert lib.naju_mixer_workspace_bytes(ctypes.byref(dims(d_state=48)), 64) == 0
+
+
 def test_workspace_and_ckpt_sizes(lib):
     d = dims(batch=8, seqlen=2048, d_inner=1536)
     for op in range(4):

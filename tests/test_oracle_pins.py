@@ -398,3 +398,90 @@ def test_nonfinite_gate_conventions():
     tail["x0"] = None
     _, xt = oracle.scan_fwd(**tail)
     np.testing.assert_allclose(xf, xt, rtol=1e-14)
+
+
+# ------------------------------------------------------------- mixer layer
+# The layer wiring (input projection into the conv and modulation branches,
+# gate / B / C projections of the conv output, output projection + residual)
+# is the block flowchart of the reproduction README ("Background and main
+# changes"); the gate biases are its preserve-first initialisation.
+
+def test_round_bf16_matches_library_conversion():
+    """bf16 storage rounding against torch's float32 -> bfloat16 conversion,
+    including exact ties (round half to even) and values next to them."""
+    import torch
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-20, 20, 4000),
+                        1.0 + np.arange(64) * 2.0 ** -8,          # ties and exact values
+                        (1.0 + np.arange(64) * 2.0 ** -8) * (1 + 2.0 ** -22)])
+    want = torch.tensor(x, dtype=torch.float64).to(torch.float32).to(torch.bfloat16)
+    np.testing.assert_array_equal(oracle.round_bf16(x), want.double().numpy())
+
+
+def mixer_case(dm=16, Di=16, N=16, Bt=2, L=19, seed=11):
+    d = inputs.draw_mixer(Bt, L, dm, Di, N, seed=seed)
+    return {k: v.astype(np.float64) for k, v in d.items()}
+
+
+def test_mixer_projection_orientation_with_permutations():
+    """With a permutation as input projection (row vectors times W[in][out]),
+    u's channel j is token channel perm[j]; a transposed W would give the
+    inverse permutation.  The same for the output projection."""
+    d = mixer_case()
+    rng = np.random.default_rng(3)
+    p_in, p_out = rng.permutation(16), rng.permutation(16)
+    assert (np.argsort(p_in) != p_in).any() and (np.argsort(p_out) != p_out).any()
+    W_u = np.zeros((16, 16))
+    W_u[p_in, np.arange(16)] = 1.0         # column j picks input channel p_in[j]
+    W_out = np.zeros((16, 16))
+    W_out[p_out, np.arange(16)] = 1.0
+    d.update(W_u=W_u, W_z=np.eye(16), W_out=W_out)
+    r = oracle.mixer_fwd(d["xn"], d["W_u"], d["W_z"], d["conv_w"], d["W_a"], d["a_bias"],
+                         d["W_b"], d["b_bias"], d["W_B"], d["W_C"], d["D"], d["W_out"],
+                         res=d["res"])
+    np.testing.assert_array_equal(r["u"], d["xn"][..., p_in])   # xn is bf16 already
+    np.testing.assert_array_equal(r["z"], d["xn"])
+    np.testing.assert_array_equal(r["out"], oracle.round_bf16(r["y"][..., p_out] + d["res"]))
+
+
+def test_mixer_gate_biases_and_selected_directions():
+    """W_a = W_b = 0 leaves exactly the gate biases; B and C as selections of
+    the conv output read the stored h = bf16(SiLU(conv(u))) channel by channel."""
+    d = mixer_case(Di=24)
+    sel_B, sel_C = np.arange(16) + 3, np.arange(16)[::-1] * 1 + 8
+    W_B = np.zeros((24, 16))
+    W_B[sel_B, np.arange(16)] = 1.0
+    W_C = np.zeros((24, 16))
+    W_C[sel_C, np.arange(16)] = 1.0
+    a_bias = np.linspace(3.0, 6.0, 24)
+    r = oracle.mixer_fwd(d["xn"], d["W_u"], d["W_z"], d["conv_w"], np.zeros((24, 24)), a_bias,
+                         np.zeros((24, 24)), d["b_bias"], W_B, W_C, d["D"], d["W_out"])
+    np.testing.assert_array_equal(r["a"], np.broadcast_to(oracle.round_bf16(a_bias), r["a"].shape))
+    np.testing.assert_array_equal(r["b"], np.full(r["b"].shape, -2.0))
+    _, h = oracle.conv_silu(r["u"], d["conv_w"])
+    np.testing.assert_array_equal(r["h"], oracle.round_bf16(h))
+    np.testing.assert_array_equal(r["B"], r["h"][..., sel_B])
+    np.testing.assert_array_equal(r["C"], r["h"][..., sel_C])
+
+
+def test_mixer_output_is_residual_when_projection_is_zero():
+    d = mixer_case(dm=8, Di=16)
+    r = oracle.mixer_fwd(d["xn"], d["W_u"], d["W_z"], d["conv_w"], d["W_a"], d["a_bias"],
+                         d["W_b"], d["b_bias"], d["W_B"], d["W_C"], d["D"], np.zeros((16, 8)),
+                         res=d["res"])
+    np.testing.assert_array_equal(r["out"], d["res"])
+
+
+def test_mixer_scan_part_is_the_block_forward():
+    """The scan in the middle is the (separately pinned) block forward on the
+    stored projections, and the output is a plain matrix product of its bf16 y."""
+    d = mixer_case(dm=24, Di=32, N=64, L=40)
+    r = oracle.mixer_fwd(d["xn"], d["W_u"], d["W_z"], d["conv_w"], d["W_a"], d["a_bias"],
+                         d["W_b"], d["b_bias"], d["W_B"], d["W_C"], d["D"], d["W_out"])
+    y, _, _ = oracle.block_fwd(r["u"], r["z"], d["conv_w"], r["a"], r["b"], r["B"], r["C"], d["D"])
+    np.testing.assert_array_equal(r["y"], oracle.round_bf16(y))
+    np.testing.assert_allclose(r["out"], oracle.round_bf16(np.einsum("blk,km->blm", r["y"], d["W_out"])),
+                               rtol=0, atol=0)
+    # gate statistics follow the scan workloads' (a around 5, b around -2, unit spread)
+    assert abs(r["a"].mean() - 5.0) < 0.3 and 0.6 < r["a"].std() < 1.5
+    assert abs(r["b"].mean() + 2.0) < 0.3 and 0.6 < r["b"].std() < 1.5
