@@ -14,7 +14,9 @@ bounded sample of the same workload (the cpu_baseline leg).
 
 `--workload NAME` instead times naju_scan_fwd alone on another named workload
 of the hot path (for instance the 4 x 8192 x 4096, d_state 64 scan), with its
-roofline; the default run is the training step above.
+roofline, or, for a mixer workload (mixer_bf16_b8_l2048_dm768_d1536_n16), the
+whole mixer layer forward (naju_mixer_fwd: projections on the matrix cores
+around the block scan); the default run is the training step above.
 
 Prints ONE JSON line.
 """
@@ -82,7 +84,8 @@ def main():
                     help="restrict the timed work (for profiling runs); 'copy' runs a plain "
                          "1 GiB device copy, the reference for HBM byte counters")
     ap.add_argument("--workload", default=WORKLOAD,
-                    help="another named scan workload: time naju_scan_fwd alone on it")
+                    help="another named scan workload (naju_scan_fwd alone) or a mixer "
+                         "workload (naju_mixer_fwd)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Naju scan path has no multi-GPU "
@@ -115,6 +118,8 @@ def main():
         print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
                           "ms": round(dt * 1e3, 4), "GB_per_s": round(2 * nbytes / dt / 1e9, 1)}))
         return
+    if args.workload in inputs.MIXER_WORKLOADS:
+        return bench_mixer_workload(args, torch, nb, inputs)
     if args.workload != WORKLOAD:
         return bench_scan_workload(args, torch, nb, inputs)
     w = inputs.WORKLOADS[WORKLOAD]
@@ -326,6 +331,93 @@ def main():
         "cpu_baseline": cpu,
         "hbm_copy_ceiling": copy_ceiling,
         "parts": parts,
+    }
+    print(json.dumps(out), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+
+
+def bench_mixer_workload(args, torch, nb, inputs):
+    """naju_mixer_fwd on a named mixer workload, inputs and weights resident in HBM;
+    also the block forward alone on inputs of the same shape (the scan inside)."""
+    c = inputs.MIXER_WORKLOADS[args.workload]
+    Bt, L, dm, Di, N = c["Bt"], c["L"], c["dm"], c["Di"], c["N"]
+    dev = torch.device("cuda:0")
+    d = inputs.draw_mixer(Bt, L, dm, Di, N, seed=c["seed"])
+    f32 = ("conv_w", "D", "a_bias", "b_bias")
+    t = {k: torch.from_numpy(v).to(torch.float32 if k in f32 else torch.bfloat16).to(dev)
+         for k, v in d.items()}
+    del d
+    sets = [t["xn"], t["xn"].roll(1, 0).contiguous()]
+    res = [t["res"], t["res"].roll(1, 0).contiguous()]
+
+    def call(i):
+        nb.mixer_fwd(sets[i % 2], t["W_u"], t["W_z"], t["conv_w"], t["W_a"], t["a_bias"],
+                     t["W_b"], t["b_bias"], t["W_B"], t["W_C"], t["D"], t["W_out"],
+                     res=res[i % 2])
+
+    def timed(fn, steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            ev[k][0].record()
+            fn(k)
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        return wall, np.array([a.elapsed_time(b) for a, b in ev])
+
+    for k in range(args.warmup):
+        call(k)
+    t_all, tt = timed(call, args.steps)
+    # the block scan of the same shape alone (synthetic u, z, a, b, B, C)
+    w = inputs.Workload("mixer_scan_part", Bt, L, Di, N, seed=c["seed"] + 1, block=True)
+    db = inputs.draw_workload(w)
+    bt = {k: torch.from_numpy(db[k]).to(torch.bfloat16).to(dev)
+          for k in ("u", "z", "a", "b", "B", "C")}
+    bD, bw = torch.from_numpy(db["D"]).to(dev), torch.from_numpy(db["conv_w"]).to(dev)
+    del db
+    blk = lambda i: nb.block_fwd(bt["u"], bt["z"], bw, bt["a"], bt["b"], bt["B"], bt["C"], bD)  # noqa: E731
+    for k in range(args.warmup):
+        blk(k)
+    _, tb = timed(blk, args.steps)
+    ms, ms_b = float(tt.mean()), float(tb.mean())
+    flops = 2.0 * Bt * L * (2 * dm * Di + 2 * Di * Di + 2 * Di * N + Di * dm)
+    ach = flops / (ms * 1e-3) / 1e12
+    ach_g = flops / ((ms - ms_b) * 1e-3) / 1e12
+    out = {
+        "metric": "mixer layer forward tokens/sec (projections + conv + block scan)",
+        "value": round(Bt * L / t_all, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_all * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": Bt, "seq_len": L, "d_model": dm,
+                   "d_inner": Di, "d_state": N, "io": "bf16",
+                   "step": "mixer layer forward (naju_mixer_fwd)"},
+        "roofline": {"kernel": "the call's hipBLASLt projections (bf16, fp32 accumulation); "
+                               "time = mixer call minus the block forward alone",
+                     "bound": "mfma", "achieved": round(ach_g, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach_g / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "ms_per_launch": round(ms - ms_b, 4), "alg_flops_per_launch": int(flops)},
+        "cpu_baseline": None,
+        "parts": {"mixer_fwd": {"ms_median": round(float(np.median(tt)), 4),
+                                "ms_mean": round(ms, 4),
+                                "tokens_per_s": round(Bt * L / (ms * 1e-3), 1),
+                                "gemm_flops": int(flops),
+                                "TFLOP_per_s_over_call": round(ach, 1)},
+                  "block_fwd_same_shape": {"ms_median": round(float(np.median(tb)), 4),
+                                           "ms_mean": round(ms_b, 4)}},
     }
     print(json.dumps(out), flush=True)
 

@@ -239,8 +239,10 @@ naju_status_t naju_block_step(const naju_dims_t *dims, const void *u, const void
  *   out           [Bt][L][d_model] bf16 (written)
  *   ws            naju_mixer_workspace_bytes() bytes, 256-byte aligned, zero-filled
  *                 before first use (as for the other entry points)
- * Matrices, conv_w and conv_state must be 16-byte aligned.  A hipBLASLt
- * failure returns NAJU_EHIP; work already enqueued by the call is not undone.
+ * Matrices, conv_w and conv_state must be 16-byte aligned; batch <= 65535,
+ * seqlen <= 16 * 65535.  The first call for a shape asks hipBLASLt's heuristic
+ * for each projection's algorithm (host work only) and caches it.  A hipBLASLt
+ * failure returns NAJU_EHIP; work already enqueued is not undone.
  */
 size_t naju_mixer_workspace_bytes(const naju_dims_t *dims, int64_t d_model);
 naju_status_t naju_mixer_fwd(const naju_dims_t *dims, int64_t d_model, const void *xn,

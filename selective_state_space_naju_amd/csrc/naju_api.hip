@@ -336,6 +336,8 @@ static naju_status_t mixer_common(const naju_dims_t *d, int64_t dm, const void *
         return fail(NAJU_EUNSUPPORTED, "d_model and d_inner must be multiples of 8");
     if (dm > ((int64_t)1 << 24) || d->d_inner >= ((int64_t)1 << 24))
         return fail(NAJU_EINVAL, "d_model or d_inner too large");
+    if (d->batch > 65535 || (d->seqlen + 15) / 16 > 65535)
+        return fail(NAJU_EINVAL, "batch or seqlen too large for the mixer's conv launch");
     if (d->batch == 0 || d->seqlen == 0) return NAJU_OK;
     TRY(need(xn, "xn", 16));
     TRY(opt(res, "res", 16));
