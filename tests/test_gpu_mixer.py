@@ -26,12 +26,17 @@ def need_gpu():
     nb.lib()
 
 
+# (with a residual of unit size the output is dominated by it after bf16 rounding, so
+# most cases run without one, where the output is the projected scan result itself)
 CASES = [
     # Bt, L, d_model, d_inner, d_state, residual, conv_state: ragged lengths, both state sizes
-    (2, 200, 64, 128, 16, True, False),
+    (2, 200, 64, 128, 16, False, False),
     (1, 333, 96, 64, 64, False, True),
     (3, 130, 128, 256, 16, True, True),
     (2, 257, 64, 2048, 64, True, False),   # d_state 64 matrix-core form (32 rows)
+    (1, 1, 32, 64, 16, False, True),       # one token: conv window entirely from conv_state
+    (3, 17, 40, 72, 16, False, False),     # one partial conv segment, d_inner not a multiple of 64
+    (2, 50, 16, 8, 64, False, True),       # the smallest d_inner, register form of the scan
 ]
 
 FP32_KEYS = ("conv_w", "D", "a_bias", "b_bias")
@@ -56,6 +61,7 @@ def run_case(Bt, L, dm, Di, N, residual, conv_state, seed):
 def test_mixer_matches_oracle(case):
     got, ref = run_case(*case, seed=77)
     assert np.isfinite(got).all()
+    assert np.abs(ref["y"]).max() > 0.1 and np.abs(ref["out"]).max() > 0.1  # a non-trivial case
     assert_close("out", got, ref["out"], TOL["bf16"])
 
 
