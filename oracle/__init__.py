@@ -166,6 +166,10 @@ def block_bwd(u, z, w, a, b, B, C, D, x0, dy, dx_final=None, conv_state=None):
     return out
 
 
+def _round(x):
+    return round_bf16(x)
+
+
 def round_bf16(x):
     """Values rounded to bfloat16 the way a device computing in fp32 stores them:
     first to the nearest fp32, then to the nearest bfloat16 (ties to the even
@@ -181,7 +185,7 @@ def round_bf16(x):
 
 
 def mixer_fwd(xn, W_u, W_z, conv_w, W_a, a_bias, W_b, b_bias, W_B, W_C, D, W_out, res=None,
-              conv_state=None):
+              conv_state=None, store_bf16=True):
     """The mixer layer of the block flowchart (reproduction README, "Background
     and main changes") around block_fwd, in fp64 with bf16 storage of the
     intermediates: returns a dict with u, z, h, a, b, B, C, y and out.
@@ -191,8 +195,10 @@ def mixer_fwd(xn, W_u, W_z, conv_w, W_a, a_bias, W_b, b_bias, W_B, W_C, D, W_out
         out = y W_out + res
     Every intermediate is stored as bf16 (round_bf16) before its next use; the
     projections read the stored h, the scan recomputes h from u (block_fwd).
-    The matrix products are numpy matmuls in fp64."""
+    The matrix products are numpy matmuls in fp64.  store_bf16=False skips the
+    storage rounding (the smooth layer that finite differences can check)."""
     f = lambda t: None if t is None else np.asarray(t, dtype=np.float64)
+    round_bf16 = _round if store_bf16 else (lambda t: np.asarray(t, dtype=np.float64))
     xn, W_u, W_z, W_a, W_b, W_B, W_C, W_out = map(f, (xn, W_u, W_z, W_a, W_b, W_B, W_C, W_out))
     u = round_bf16(xn @ W_u)
     z = round_bf16(xn @ W_z)
@@ -208,3 +214,68 @@ def mixer_fwd(xn, W_u, W_z, conv_w, W_a, a_bias, W_b, b_bias, W_B, W_C, D, W_out
     if res is not None:
         o = o + f(res)
     return dict(u=u, z=z, h=h, a=a, b=b, B=B, C=C, y=y, out=round_bf16(o))
+
+
+def _conv_silu_bwd(u, w, conv_state, dh):
+    """Reverse mode of h = SiLU(conv(u)) (conv as conv_silu): returns
+    (du, dw, dconv_state) for upstream dh, with SiLU'(p) = s (1 + p (1 - s))."""
+    Bt, L, Di = u.shape
+    K = w.shape[1]
+    pre, _ = conv_silu(u, w, conv_state)
+    s = 1.0 / (1.0 + np.exp(-pre))
+    dpre = dh * s * (1.0 + pre * (1.0 - s))
+    ext = np.concatenate([np.zeros((Bt, K - 1, Di)) if conv_state is None
+                          else np.asarray(conv_state, dtype=np.float64), u], axis=1)
+    du_ext = np.zeros_like(ext)
+    dw = np.zeros((Di, K))
+    for k in range(K):   # pre_n = sum_k w[:, k] ext[n + k]
+        du_ext[:, k:k + L, :] += dpre * w[:, k]
+        dw[:, k] = np.einsum("btc,btc->c", dpre, ext[:, k:k + L, :])
+    return du_ext[:, K - 1:, :], dw, du_ext[:, :K - 1, :]
+
+
+def mixer_bwd(xn, W_u, W_z, conv_w, W_a, a_bias, W_b, b_bias, W_B, W_C, D, W_out, d_out,
+              res=None, conv_state=None, store_bf16=True):
+    """Reverse mode of mixer_fwd for upstream gradient d_out = dLoss/dout.
+
+    The stored bf16 intermediates pass gradients unchanged (rounding is taken
+    as the identity); with store_bf16 the upstream gradients that the device
+    stores in bf16 (dy, and the block backward's du, dz, da, db, dB, dC) are
+    rounded the same way.  Returns a dict with dxn, dres, dW_u, dW_z, dconv_w,
+    dconv_state, dW_a, da_bias, dW_b, db_bias, dW_B, dW_C, dD, dW_out."""
+    f = lambda t: None if t is None else np.asarray(t, dtype=np.float64)
+    rnd = _round if store_bf16 else (lambda t: np.asarray(t, dtype=np.float64))
+    fw = mixer_fwd(xn, W_u, W_z, conv_w, W_a, a_bias, W_b, b_bias, W_B, W_C, D, W_out, res,
+                   conv_state, store_bf16)
+    xn, W_u, W_z, W_a, W_b, W_B, W_C, W_out, g = map(f, (xn, W_u, W_z, W_a, W_b, W_B, W_C,
+                                                        W_out, d_out))
+    w, cs = f(conv_w), f(conv_state)
+    out = {"dres": g.copy() if res is not None else None}
+    # out = y W_out + res
+    dy = rnd(g @ W_out.T)
+    out["dW_out"] = np.einsum("btk,btm->km", fw["y"], g)
+    # y = block_fwd(u, z, conv_w, a, b, B, C, D)
+    gb = block_bwd(fw["u"], fw["z"], w, fw["a"], fw["b"], fw["B"], fw["C"], D, None, dy,
+                   conv_state=cs)
+    da, db, dB, dC = (rnd(gb[k]) for k in ("da", "db", "dB", "dC"))
+    du_blk, dz = rnd(gb["du"]), rnd(gb["dz"])
+    out["dD"] = gb["dD"]
+    # a = h W_a + a_bias, b = h W_b + b_bias, B = h W_B, C = h W_C (h: the stored one)
+    h = fw["h"]
+    dh = da @ W_a.T + db @ W_b.T + dB @ W_B.T + dC @ W_C.T
+    out["dW_a"] = np.einsum("btk,btn->kn", h, da)
+    out["dW_b"] = np.einsum("btk,btn->kn", h, db)
+    out["dW_B"] = np.einsum("btk,btn->kn", h, dB)
+    out["dW_C"] = np.einsum("btk,btn->kn", h, dC)
+    out["da_bias"] = da.sum(axis=(0, 1))
+    out["db_bias"] = db.sum(axis=(0, 1))
+    # h = SiLU(conv(u)) on the projection path; the scan's own path is in gb
+    du_p, dw_p, dcs_p = _conv_silu_bwd(fw["u"], w, cs, dh)
+    du = rnd(du_blk + du_p)
+    out["dconv_w"] = gb["dw"] + dw_p
+    out["dconv_state"] = gb["dconv_state"] + dcs_p
+    # u = xn W_u, z = xn W_z
+    out["dxn"] = du @ W_u.T + dz @ W_z.T
+    out["dW_u"] = np.einsum("btk,btn->kn", xn, du)
+    out["dW_z"] = np.einsum("btk,btn->kn", xn, dz)
+    return out

@@ -485,3 +485,36 @@ def test_mixer_scan_part_is_the_block_forward():
     # gate statistics follow the scan workloads' (a around 5, b around -2, unit spread)
     assert abs(r["a"].mean() - 5.0) < 0.3 and 0.6 < r["a"].std() < 1.5
     assert abs(r["b"].mean() + 2.0) < 0.3 and 0.6 < r["b"].std() < 1.5
+
+
+def test_mixer_backward_matches_finite_differences():
+    """Every gradient of the (unrounded) mixer layer against a central
+    difference of the loss sum(d_out * out) along a random direction: a dropped
+    path (the projections' share of du or dconv_w), a transposed product or a
+    missing bias gradient fails here."""
+    d = {k: v.astype(np.float64) for k, v in
+         inputs.draw_mixer(2, 9, 8, 8, 16, seed=4, conv_state=True).items()}
+    rng = np.random.default_rng(8)
+    g = rng.standard_normal((2, 9, 8))
+    names = ("xn", "W_u", "W_z", "conv_w", "W_a", "a_bias", "W_b", "b_bias", "W_B", "W_C", "D",
+             "W_out")
+
+    def loss(p):
+        o = oracle.mixer_fwd(*(p[k] for k in names), res=p["res"], conv_state=p["conv_state"],
+                             store_bf16=False)
+        return float((g * o["out"]).sum())
+
+    grads = oracle.mixer_bwd(*(d[k] for k in names), g, res=d["res"],
+                             conv_state=d["conv_state"], store_bf16=False)
+    gname = {"xn": "dxn", "W_u": "dW_u", "W_z": "dW_z", "conv_w": "dconv_w", "W_a": "dW_a",
+             "a_bias": "da_bias", "W_b": "dW_b", "b_bias": "db_bias", "W_B": "dW_B",
+             "W_C": "dW_C", "D": "dD", "W_out": "dW_out", "res": "dres",
+             "conv_state": "dconv_state"}
+    for k, gk in gname.items():
+        v = rng.standard_normal(d[k].shape)
+        eps = 1e-6 * max(1.0, np.abs(d[k]).max())
+        p1 = dict(d); p1[k] = d[k] + eps * v
+        p2 = dict(d); p2[k] = d[k] - eps * v
+        fd = (loss(p1) - loss(p2)) / (2 * eps)
+        an = float((grads[gk] * v).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (k, fd, an)
