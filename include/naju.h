@@ -253,6 +253,37 @@ naju_status_t naju_mixer_fwd(const naju_dims_t *dims, int64_t d_model, const voi
                              const void *W_out, void *out, void *ws, size_t ws_bytes,
                              void *stream);
 
+/*
+ * Mixer layer backward: the reverse mode of naju_mixer_fwd for the upstream
+ * gradient d_out = dLoss/dout.  The call recomputes the layer's forward
+ * intermediates (u, z, h, a, b, B, C, y and the scan checkpoints) in its
+ * workspace, then runs the output projection's, the block scan's (the
+ * naju_block_bwd kernels), the gate / B / C projections', the projection
+ * path's conv + SiLU and the input projections' reverse modes.  The stored
+ * bf16 intermediates pass gradients unchanged (rounding taken as the
+ * identity); dy and the block backward's gradients are kept in bf16, the
+ * projections' sums in fp32.  The residual's gradient is d_out itself.
+ *   inputs        as naju_mixer_fwd (no res), and
+ *   d_out         [Bt][L][d_model] bf16
+ * outputs (written, fp32 unless noted):
+ *   dxn [Bt][L][d_model];  dW_u, dW_z [d_model][d_inner];  dconv_w [d_inner][4];
+ *   dconv_state [Bt][3][d_inner] bf16 or NULL (needs conv_state);
+ *   dW_a, dW_b [d_inner][d_inner];  da_bias, db_bias [d_inner];
+ *   dW_B, dW_C [d_inner][d_state];  dD [d_inner];  dW_out [d_inner][d_model]
+ *   ws            naju_mixer_bwd_workspace_bytes() bytes, as for the forward
+ * Output buffers must be 16-byte aligned (dD 4-byte).
+ */
+size_t naju_mixer_bwd_workspace_bytes(const naju_dims_t *dims, int64_t d_model);
+naju_status_t naju_mixer_bwd(const naju_dims_t *dims, int64_t d_model, const void *xn,
+                             const void *W_u, const void *W_z, const float *conv_w,
+                             const void *conv_state, const void *W_a, const float *a_bias,
+                             const void *W_b, const float *b_bias, const void *W_B,
+                             const void *W_C, const float *D, const void *W_out,
+                             const void *d_out, float *dxn, float *dW_u, float *dW_z,
+                             float *dconv_w, void *dconv_state, float *dW_a, float *da_bias,
+                             float *dW_b, float *db_bias, float *dW_B, float *dW_C, float *dD,
+                             float *dW_out, void *ws, size_t ws_bytes, void *stream);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char *naju_last_error(void);
 

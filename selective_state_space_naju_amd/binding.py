@@ -27,7 +27,8 @@ D_CONV = 4
 EXPORTS = ("naju_workspace_bytes", "naju_ckpt_bytes", "naju_workspace_init",
            "naju_workspace_check", "naju_scan_fwd", "naju_scan_bwd", "naju_block_fwd",
            "naju_block_bwd", "naju_scan_step", "naju_block_step", "naju_mixer_workspace_bytes",
-           "naju_mixer_fwd", "naju_last_error", "naju_version")
+           "naju_mixer_fwd", "naju_mixer_bwd_workspace_bytes", "naju_mixer_bwd", "naju_last_error",
+           "naju_version")
 
 
 class NajuError(RuntimeError):
@@ -84,6 +85,10 @@ def lib() -> ctypes.CDLL:
         L.naju_mixer_workspace_bytes.restype = sz
         L.naju_mixer_fwd.argtypes = [dp, ctypes.c_int64] + [vp] * 16 + [sz, vp]
         L.naju_mixer_fwd.restype = st
+        L.naju_mixer_bwd_workspace_bytes.argtypes = [dp, ctypes.c_int64]
+        L.naju_mixer_bwd_workspace_bytes.restype = sz
+        L.naju_mixer_bwd.argtypes = [dp, ctypes.c_int64] + [vp] * 28 + [sz, vp]
+        L.naju_mixer_bwd.restype = st
         L.naju_last_error.argtypes = []
         L.naju_last_error.restype = ctypes.c_char_p
         L.naju_version.argtypes = []
@@ -379,3 +384,48 @@ def mixer_fwd(xn, W_u, W_z, conv_w, W_a, a_bias, W_b, b_bias, W_B, W_C, D, W_out
                                _p(b_bias), _p(W_B), _p(W_C), _p(D), _p(W_out), _p(out), ws.ptr,
                                ws.nbytes, stream_handle(dev)))
     return out
+
+
+def mixer_bwd(xn, W_u, W_z, conv_w, W_a, a_bias, W_b, b_bias, W_B, W_C, D, W_out, d_out,
+              conv_state=None, *, ws=None):
+    """Gradients of naju_mixer_fwd for upstream d_out (the residual's is d_out):
+    dict(dxn, dW_u, dW_z, dconv_w, dconv_state, dW_a, da_bias, dW_b, db_bias, dW_B, dW_C,
+    dD, dW_out), fp32 except dconv_state (bf16, only with conv_state)."""
+    Bt, L, dm = xn.shape
+    Di = W_u.shape[1]
+    N = W_B.shape[1]
+    dt, dev = xn.dtype, xn.device
+    if dt != torch.bfloat16:
+        raise TypeError("the mixer layer takes bfloat16 activations and weights")
+    _req(d_out, "d_out", (Bt, L, dm), dt, dev)
+    for nm, t, shp in (("xn", xn, (Bt, L, dm)), ("W_u", W_u, (dm, Di)), ("W_z", W_z, (dm, Di)),
+                       ("W_a", W_a, (Di, Di)), ("W_b", W_b, (Di, Di)), ("W_B", W_B, (Di, N)),
+                       ("W_C", W_C, (Di, N)), ("W_out", W_out, (Di, dm))):
+        _req(t, nm, shp, dt, dev)
+    for nm, t, shp in (("conv_w", conv_w, (Di, D_CONV)), ("a_bias", a_bias, (Di,)),
+                       ("b_bias", b_bias, (Di,)), ("D", D, (Di,))):
+        _req(t, nm, shp, torch.float32, dev)
+    _opt(conv_state, "conv_state", (Bt, D_CONV - 1, Di), dt, dev)
+    dims = make_dims(Bt, L, Di, N, BF16)
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)  # noqa: E731
+    g = dict(dxn=f32(Bt, L, dm), dW_u=f32(dm, Di), dW_z=f32(dm, Di), dconv_w=f32(Di, D_CONV),
+             dW_a=f32(Di, Di), da_bias=f32(Di), dW_b=f32(Di, Di), db_bias=f32(Di),
+             dW_B=f32(Di, N), dW_C=f32(Di, N), dD=f32(Di), dW_out=f32(Di, dm))
+    g["dconv_state"] = (torch.empty((Bt, D_CONV - 1, Di), dtype=dt, device=dev)
+                        if conv_state is not None else None)
+    if ws is None:
+        d = torch.device(dev)
+        key = (d.index, torch.cuda.current_stream(d).cuda_stream, "mixer_bwd", Bt, L, dm, Di, N)
+        ws = _ws_cache.get(key)
+        if ws is None:
+            ws = Workspace(int(lib().naju_mixer_bwd_workspace_bytes(ctypes.byref(dims), dm)), d)
+            _ws_cache[key] = ws
+    check(lib().naju_mixer_bwd(ctypes.byref(dims), dm, _p(xn), _p(W_u), _p(W_z), _p(conv_w),
+                               _p(conv_state), _p(W_a), _p(a_bias), _p(W_b), _p(b_bias),
+                               _p(W_B), _p(W_C), _p(D), _p(W_out), _p(d_out), _p(g["dxn"]),
+                               _p(g["dW_u"]), _p(g["dW_z"]), _p(g["dconv_w"]),
+                               _p(g["dconv_state"]), _p(g["dW_a"]), _p(g["da_bias"]),
+                               _p(g["dW_b"]), _p(g["db_bias"]), _p(g["dW_B"]), _p(g["dW_C"]),
+                               _p(g["dD"]), _p(g["dW_out"]), ws.ptr, ws.nbytes,
+                               stream_handle(dev)))
+    return g

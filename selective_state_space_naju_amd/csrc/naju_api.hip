@@ -324,8 +324,8 @@ static naju_status_t mixer_common(const naju_dims_t *d, int64_t dm, const void *
                                   const float *conv_w, const void *conv_state, const void *W_a,
                                   const float *a_bias, const void *W_b, const float *b_bias,
                                   const void *W_B, const void *W_C, const float *D,
-                                  const void *W_out, void *out, void *ws, size_t ws_bytes,
-                                  void *stream)
+                                  const void *W_out, void *out, const MixerGrads *grads,
+                                  void *ws, size_t ws_bytes, void *stream)
 {
     TRY(check_dims(d, true));
     if (d->io != NAJU_BF16) return fail(NAJU_EUNSUPPORTED, "the mixer is built for bf16 io only");
@@ -353,12 +353,31 @@ static naju_status_t mixer_common(const naju_dims_t *d, int64_t dm, const void *
     TRY(need(W_C, "W_C", 16));
     TRY(need(D, "D", 4));
     TRY(need(W_out, "W_out", 16));
-    TRY(need(out, "out", 16));
-    const size_t need_b = mixer_ws_bytes(d->batch, d->seqlen, d->d_inner, d->d_state);
+    const size_t need_b = grads ? mixer_bwd_ws_bytes(d->batch, d->seqlen, d->d_inner, d->d_state)
+                                : mixer_ws_bytes(d->batch, d->seqlen, d->d_inner, d->d_state);
     if (!ws) return fail(NAJU_EWORKSPACE, "workspace is NULL (needs %zu bytes)", need_b);
     if (((uintptr_t)ws) % 256) return fail(NAJU_EINVAL, "workspace is not 256-byte aligned");
     if (ws_bytes < need_b)
         return fail(NAJU_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need_b);
+    if (grads) {
+        const MixerGrads &q = *grads;
+        TRY(need(q.d_out, "d_out", 16));
+        TRY(need(q.dxn, "dxn", 16));
+        TRY(need(q.dW_u, "dW_u", 16));
+        TRY(need(q.dW_z, "dW_z", 16));
+        TRY(need(q.dconv_w, "dconv_w", 16));
+        TRY(opt(q.dconv_state, "dconv_state", 16));
+        TRY(need(q.dW_a, "dW_a", 16));
+        TRY(need(q.da_bias, "da_bias", 16));
+        TRY(need(q.dW_b, "dW_b", 16));
+        TRY(need(q.db_bias, "db_bias", 16));
+        TRY(need(q.dW_B, "dW_B", 16));
+        TRY(need(q.dW_C, "dW_C", 16));
+        TRY(need(q.dD, "dD", 4));
+        TRY(need(q.dW_out, "dW_out", 16));
+    } else {
+        TRY(need(out, "out", 16));
+    }
     MixerArgs g{};
     g.Bt = d->batch;
     g.L = d->seqlen;
@@ -382,7 +401,8 @@ static naju_status_t mixer_common(const naju_dims_t *d, int64_t dm, const void *
     g.W_out = W_out;
     g.out = out;
     g.ws = ws;
-    const char *e = mixer_fwd(g, (hipStream_t)stream);
+    const char *e = grads ? mixer_bwd(g, *grads, (hipStream_t)stream)
+                          : mixer_fwd(g, (hipStream_t)stream);
     if (e) return fail(NAJU_EHIP, "mixer: %s", e);
     return NAJU_OK;
 }
@@ -522,7 +542,42 @@ naju_status_t naju_mixer_fwd(const naju_dims_t *dims, int64_t d_model, const voi
                              void *stream)
 {
     return mixer_common(dims, d_model, xn, res, W_u, W_z, conv_w, conv_state, W_a, a_bias, W_b,
-                        b_bias, W_B, W_C, D, W_out, out, ws, ws_bytes, stream);
+                        b_bias, W_B, W_C, D, W_out, out, nullptr, ws, ws_bytes, stream);
+}
+
+size_t naju_mixer_bwd_workspace_bytes(const naju_dims_t *dims, int64_t d_model)
+{
+    if (check_dims(dims, true) != NAJU_OK || d_model <= 0) return 0;
+    return mixer_bwd_ws_bytes(dims->batch, dims->seqlen, dims->d_inner, dims->d_state);
+}
+
+naju_status_t naju_mixer_bwd(const naju_dims_t *dims, int64_t d_model, const void *xn,
+                             const void *W_u, const void *W_z, const float *conv_w,
+                             const void *conv_state, const void *W_a, const float *a_bias,
+                             const void *W_b, const float *b_bias, const void *W_B,
+                             const void *W_C, const float *D, const void *W_out,
+                             const void *d_out, float *dxn, float *dW_u, float *dW_z,
+                             float *dconv_w, void *dconv_state, float *dW_a, float *da_bias,
+                             float *dW_b, float *db_bias, float *dW_B, float *dW_C, float *dD,
+                             float *dW_out, void *ws, size_t ws_bytes, void *stream)
+{
+    MixerGrads q{};
+    q.d_out = d_out;
+    q.dxn = dxn;
+    q.dW_u = dW_u;
+    q.dW_z = dW_z;
+    q.dconv_w = dconv_w;
+    q.dconv_state = dconv_state;
+    q.dW_a = dW_a;
+    q.da_bias = da_bias;
+    q.dW_b = dW_b;
+    q.db_bias = db_bias;
+    q.dW_B = dW_B;
+    q.dW_C = dW_C;
+    q.dD = dD;
+    q.dW_out = dW_out;
+    return mixer_common(dims, d_model, xn, nullptr, W_u, W_z, conv_w, conv_state, W_a, a_bias,
+                        W_b, b_bias, W_B, W_C, D, W_out, nullptr, &q, ws, ws_bytes, stream);
 }
 
 naju_status_t naju_scan_bwd(const naju_dims_t *dims, const void *h, const void *a,

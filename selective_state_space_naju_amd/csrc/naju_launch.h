@@ -227,6 +227,19 @@ struct MixerArgs {
     void *ws;                        // mixer_plan layout
 };
 size_t mixer_ws_bytes(int64_t Bt, int64_t L, int64_t Di, int64_t N);
+size_t mixer_bwd_ws_bytes(int64_t Bt, int64_t L, int64_t Di, int64_t N);
+struct MixerGrads {
+    const void *d_out;               // [Bt][L][dm] bf16
+    float *dxn;                      // [Bt][L][dm]
+    float *dW_u, *dW_z;              // [dm][Di]
+    float *dconv_w;                  // [Di][4]
+    void *dconv_state;               // [Bt][3][Di] bf16 or null
+    float *dW_a, *da_bias, *dW_b, *db_bias;
+    float *dW_B, *dW_C;              // [Di][N]
+    float *dD;                       // [Di]
+    float *dW_out;                   // [Di][dm]
+};
+const char *mixer_bwd(const MixerArgs &g, const MixerGrads &d, hipStream_t stream);
 // enqueues the layer; returns nullptr, or a message on failure
 const char *mixer_fwd(const MixerArgs &g, hipStream_t stream);
 

@@ -108,30 +108,42 @@ __global__ __launch_bounds__(64) void conv_silu_kernel(const int64_t L, const in
 }
 
 // ------------------------------------------------------------ GEMMs
-// Row-major D[T][n] = A[T][k] W[k][n] (+ bias[n]) (+ C[T][n]) is, in the
-// column-major terms of hipBLASLt, D^T (n x T) = W^T (n x k) A^T (k x T): W is
-// the first operand with leading dimension n, A the second with leading
-// dimension k, and the bias runs along D^T's rows.  Plans (layouts, epilogue,
-// the heuristic's algorithm) are cached per device and shape.
+// hipBLASLt is column-major: D (m x n) = op(X) (m x k) op(Y) (k x n)
+// (+ bias[m]) (+ C, beta 1), with C of D's type.  The row-major products of
+// the layer map onto it as follows (T tokens; W stored [in][out]):
+//   D[T][n] = A[T][k] W[k][n]    -> D^T = W^T A^T : X = W (n x k, ld n), Y = A (k x T, ld k)
+//   D[T][n] = A[T][k] W[n][k]^T  -> D^T = W A^T   : X = W^T stored (k x n, ld k), op T
+//   G[k][n] = A[T][k]^T E[T][n]  -> G^T = E^T A   : X = E (n x T, ld n), Y = A^T stored, op T
+// Plans (layouts, epilogue, the heuristic's first algorithm) are cached per
+// device and shape.
 struct GemmPlan {
     hipblasLtMatmulDesc_t md = nullptr;
-    hipblasLtMatrixLayout_t lw = nullptr, la = nullptr, ld = nullptr;
+    hipblasLtMatrixLayout_t lx = nullptr, ly = nullptr, ld = nullptr;
     hipblasLtMatmulAlgo_t algo{};
     size_t ws = 0;
     bool ok = false;
 };
 
+struct GemmShape {
+    int64_t m, n, k, ldx, ldy, ldd;
+    bool tx, ty;
+    hipDataType td;  // type of D (and C): HIP_R_16BF or HIP_R_32F
+    bool bias, beta;
+};
+
 static std::mutex g_lt_mu;
 static std::map<int, hipblasLtHandle_t> g_lt;
-static std::map<std::tuple<int, int64_t, int64_t, int64_t, int>, GemmPlan> g_plans;
+static std::map<std::tuple<int, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int>,
+                GemmPlan>
+    g_plans;
 
 constexpr size_t kGemmWs = (size_t)32 << 20;  // hipBLASLt workspace inside ws
 
-// Enqueues one projection.  Returns a message on failure (nullptr on success).
-static const char *gemm(hipStream_t st, int64_t T, int64_t n, int64_t k, const void *A,
-                        const void *W, const float *bias, const void *C, void *D, void *gws)
+// Enqueues one product.  Returns a message on failure (nullptr on success).
+static const char *gemm_cm(hipStream_t st, const GemmShape &g, const void *X, const void *Y,
+                           const float *bias, const void *C, void *D, void *gws)
 {
-    if (T == 0 || n == 0) return nullptr;
+    if (g.m == 0 || g.n == 0) return nullptr;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return "hipGetDevice failed";
     std::lock_guard<std::mutex> lk(g_lt_mu);
@@ -140,22 +152,26 @@ static const char *gemm(hipStream_t st, int64_t T, int64_t n, int64_t k, const v
         hd = nullptr;
         return "hipblasLtCreate failed";
     }
-    const int flags = (bias ? 1 : 0) | (C ? 2 : 0);
-    GemmPlan &p = g_plans[std::make_tuple(dev, T, n, k, flags)];
+    const int flags = (g.bias ? 1 : 0) | (g.beta ? 2 : 0) | (g.tx ? 4 : 0) | (g.ty ? 8 : 0) |
+                      (g.td == HIP_R_32F ? 16 : 0);
+    GemmPlan &p = g_plans[std::make_tuple(dev, g.m, g.n, g.k, g.ldx, g.ldy, g.ldd, flags)];
     if (!p.ok) {
+        const uint64_t xr = g.tx ? g.k : g.m, xc = g.tx ? g.m : g.k;
+        const uint64_t yr = g.ty ? g.n : g.k, yc = g.ty ? g.k : g.n;
         if (hipblasLtMatmulDescCreate(&p.md, HIPBLAS_COMPUTE_32F, HIP_R_32F) !=
                 HIPBLAS_STATUS_SUCCESS ||
-            hipblasLtMatrixLayoutCreate(&p.lw, HIP_R_16BF, (uint64_t)n, (uint64_t)k, n) !=
+            hipblasLtMatrixLayoutCreate(&p.lx, HIP_R_16BF, xr, xc, g.ldx) !=
                 HIPBLAS_STATUS_SUCCESS ||
-            hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, (uint64_t)k, (uint64_t)T, k) !=
+            hipblasLtMatrixLayoutCreate(&p.ly, HIP_R_16BF, yr, yc, g.ldy) !=
                 HIPBLAS_STATUS_SUCCESS ||
-            hipblasLtMatrixLayoutCreate(&p.ld, HIP_R_16BF, (uint64_t)n, (uint64_t)T, n) !=
+            hipblasLtMatrixLayoutCreate(&p.ld, g.td, (uint64_t)g.m, (uint64_t)g.n, g.ldd) !=
                 HIPBLAS_STATUS_SUCCESS)
             return "hipBLASLt descriptor creation failed";
-        const hipblasOperation_t opn = HIPBLAS_OP_N;
-        hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_TRANSA, &opn, sizeof(opn));
-        hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_TRANSB, &opn, sizeof(opn));
-        if (bias) {
+        const hipblasOperation_t opx = g.tx ? HIPBLAS_OP_T : HIPBLAS_OP_N;
+        const hipblasOperation_t opy = g.ty ? HIPBLAS_OP_T : HIPBLAS_OP_N;
+        hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_TRANSA, &opx, sizeof(opx));
+        hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_TRANSB, &opy, sizeof(opy));
+        if (g.bias) {
             const hipblasLtEpilogue_t epi = HIPBLASLT_EPILOGUE_BIAS;
             const hipDataType bt = HIP_R_32F;
             hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_EPILOGUE, &epi,
@@ -174,28 +190,52 @@ static const char *gemm(hipStream_t st, int64_t T, int64_t n, int64_t k, const v
             hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
                                                   &wsmax, sizeof(wsmax)) ==
                 HIPBLAS_STATUS_SUCCESS &&
-            hipblasLtMatmulAlgoGetHeuristic(hd, p.md, p.lw, p.la, p.ld, p.ld, pref, 1, res,
+            hipblasLtMatmulAlgoGetHeuristic(hd, p.md, p.lx, p.ly, p.ld, p.ld, pref, 1, res,
                                             &got) == HIPBLAS_STATUS_SUCCESS &&
             got > 0;
         if (pref) hipblasLtMatmulPreferenceDestroy(pref);
-        if (!found) return "hipBLASLt found no algorithm for a projection";
+        if (!found) return "hipBLASLt found no algorithm for a product";
         // (the heuristic's first choice: timing its other candidates on the
         // 8 x 2048-token layer made single projections up to 6 % faster, but the
         // block scan after them as much slower, and the whole layer no faster;
         // it would also synchronise the stream on a shape's first call)
-        const int best = 0;
-        p.algo = res[best].algo;
-        p.ws = res[best].workspaceSize;
+        p.algo = res[0].algo;
+        p.ws = res[0].workspaceSize;
         p.ok = true;
     }
-    if (bias)
+    if (g.bias)
         hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_BIAS_POINTER, &bias,
                                         sizeof(bias));
     const float one = 1.f, zero = 0.f;
-    if (hipblasLtMatmul(hd, p.md, &one, W, p.lw, A, p.la, C ? &one : &zero, C ? C : D, p.ld, D,
-                        p.ld, &p.algo, gws, p.ws, st) != HIPBLAS_STATUS_SUCCESS)
+    if (hipblasLtMatmul(hd, p.md, &one, X, p.lx, Y, p.ly, g.beta ? &one : &zero,
+                        g.beta ? C : D, p.ld, D, p.ld, &p.algo, gws, p.ws, st) !=
+        HIPBLAS_STATUS_SUCCESS)
         return "hipblasLtMatmul failed";
     return nullptr;
+}
+
+// D[T][n] = A[T][k] W[k][n] (+ bias[n]) (+ C[T][n]); bf16 D
+static const char *gemm(hipStream_t st, int64_t T, int64_t n, int64_t k, const void *A,
+                        const void *W, const float *bias, const void *C, void *D, void *gws)
+{
+    const GemmShape g{n, T, k, n, k, n, false, false, HIP_R_16BF, bias != nullptr, C != nullptr};
+    return gemm_cm(st, g, W, A, bias, C, D, gws);
+}
+
+// D[T][n] = A[T][k] W[n][k]^T (+ D when acc); D fp32 or bf16
+static const char *gemm_nt(hipStream_t st, int64_t T, int64_t n, int64_t k, const void *A,
+                           const void *W, bool acc, void *D, hipDataType td, void *gws)
+{
+    const GemmShape g{n, T, k, k, k, n, true, false, td, false, acc};
+    return gemm_cm(st, g, W, A, nullptr, D, D, gws);
+}
+
+// G[k][n] (fp32) = A[T][k]^T E[T][n]: the weight gradient of D = A W
+static const char *gemm_wgrad(hipStream_t st, int64_t T, int64_t n, int64_t k, const void *A,
+                              const void *E, float *G, void *gws)
+{
+    const GemmShape g{n, k, T, n, k, n, false, true, HIP_R_32F, false, false};
+    return gemm_cm(st, g, E, A, nullptr, nullptr, G, gws);
 }
 
 // ------------------------------------------------------------ layout of ws
@@ -252,9 +292,221 @@ hipError_t launch_conv_silu(int64_t Bt, int64_t L, int64_t Di, const void *u, co
     return hipGetLastError();
 }
 
+static const char *mixer_forward_pass(const MixerArgs &g, const MixerPlan &m, float *ckpt,
+                                      hipStream_t st);
+
 const char *mixer_fwd(const MixerArgs &g, hipStream_t st)
 {
     const MixerPlan m = mixer_plan(g.Bt, g.L, g.Di, g.N);
+    const char *e;
+    if ((e = mixer_forward_pass(g, m, nullptr, st))) return e;
+    const int64_t T = g.Bt * g.L;
+    return gemm(st, T, g.dm, g.Di, (char *)g.ws + m.off_y, g.W_out, nullptr, g.res, g.out,
+                (char *)g.ws + m.off_g);
+}
+
+// ------------------------------------------------------------ backward
+// conv + SiLU backward of the projection path: dpre = dh SiLU'(pre) with
+// SiLU'(p) = s (1 + p (1 - s)); du = du_scan + conv^T(dpre); per-segment
+// partial sums of dconv_w (reduced in a fixed order by mixer_dw_reduce_kernel);
+// the first segment also forms d(conv_state).  Thread = (batch row, 8 channels,
+// kSegB-token segment); the window of the last four dpre slides in registers.
+constexpr int kSegB = 32;
+
+__global__ __launch_bounds__(64) void conv_silu_bwd_kernel(
+    const int64_t L, const int64_t Di, const int nseg, const bf16 *__restrict__ u,
+    const float *__restrict__ w, const bf16 *__restrict__ cs, const float *__restrict__ dh,
+    const bf16 *__restrict__ du_scan, bf16 *__restrict__ du, float *__restrict__ dw_part,
+    const bf16 *__restrict__ dcs_scan, bf16 *__restrict__ dcs)
+{
+    const int64_t c0 = ((int64_t)blockIdx.x * 64 + threadIdx.x) * 8;
+    if (c0 >= Di) return;
+    const int64_t n0 = (int64_t)blockIdx.y * kSegB;
+    const int64_t bi = blockIdx.z;
+    const int64_t n1 = n0 + kSegB < L ? n0 + kSegB : L;
+    float wk[8][4];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float4 v = *(const float4 *)(w + (c0 + e) * 4);
+        wk[e][0] = v.x;
+        wk[e][1] = v.y;
+        wk[e][2] = v.z;
+        wk[e][3] = v.w;
+    }
+    auto ld_u = [&](int64_t m, float (&v)[8]) {  // u_m (conv_state before 0, zeros past L)
+        uint4 q = {0u, 0u, 0u, 0u};
+        if (m >= 0 && m < L)
+            q = *(const uint4 *)(u + (bi * L + m) * Di + c0);
+        else if (m < 0 && cs)
+            q = *(const uint4 *)(cs + (bi * 3 + (m + 3)) * Di + c0);
+        const uint32_t p[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = __uint_as_float(p[e] << 16);
+            v[2 * e + 1] = __uint_as_float(p[e] & 0xffff0000u);
+        }
+    };
+    float uw[4][8];  // u_{t-3} .. u_t
+    for (int r = 0; r < 3; ++r) ld_u(n0 - 3 + r, uw[r + 1]);
+    float dp[4][8];  // dpre_{t-3} .. dpre_t
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dp[r][c] = 0.f;
+    float dws[8][4];
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dws[c][k] = 0.f;
+    // dpre for tokens n0 .. n1 + 2 (zero past L); du_m is complete once dpre_{m+3} is known
+    for (int64_t t = n0; t < n1 + 3; ++t) {
+#pragma unroll
+        for (int r = 0; r < 3; ++r)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                uw[r][c] = uw[r + 1][c];
+                dp[r][c] = dp[r + 1][c];
+            }
+        ld_u(t, uw[3]);
+        float g[8];
+        if (t < L) {
+            const float4 g0 = *(const float4 *)(dh + (bi * L + t) * Di + c0);
+            const float4 g1 = *(const float4 *)(dh + (bi * L + t) * Di + c0 + 4);
+            g[0] = g0.x, g[1] = g0.y, g[2] = g0.z, g[3] = g0.w;
+            g[4] = g1.x, g[5] = g1.y, g[6] = g1.z, g[7] = g1.w;
+        } else {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) g[c] = 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float pre = wk[c][0] * uw[0][c] + wk[c][1] * uw[1][c] + wk[c][2] * uw[2][c] +
+                              wk[c][3] * uw[3][c];
+            const float sg = sigm(pre);
+            dp[3][c] = g[c] * sg * (1.f + pre * (1.f - sg));
+            if (t < n1) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) dws[c][k] += dp[3][c] * uw[k][c];
+            }
+        }
+        const int64_t m = t - 3;  // du_m = sum_k w_k dpre_{m+3-k}
+        if (m >= n0 && m < n1) {
+            const uint4 q = *(const uint4 *)(du_scan + (bi * L + m) * Di + c0);
+            const uint32_t p[4] = {q.x, q.y, q.z, q.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v2[2];
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int c = 2 * e + h2;
+                    const float base = __uint_as_float(h2 ? (p[e] & 0xffff0000u) : (p[e] << 16));
+                    v2[h2] = base + wk[c][0] * dp[3][c] + wk[c][1] * dp[2][c] +
+                             wk[c][2] * dp[1][c] + wk[c][3] * dp[0][c];
+                }
+                o[e] = (uint32_t)from_f<bf16>(v2[0]) | ((uint32_t)from_f<bf16>(v2[1]) << 16);
+            }
+            *(uint4 *)(du + (bi * L + m) * Di + c0) = uint4{o[0], o[1], o[2], o[3]};
+        }
+        // d(conv_state) row r (token r - 3): sum over k <= r of w_k dpre_{r-k}
+        if (n0 == 0 && dcs && t == 2) {
+            // dp[3] = dpre_2, dp[2] = dpre_1, dp[1] = dpre_0 (zero when L is shorter)
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                uint32_t o[4];
+                const uint4 q = dcs_scan ? *(const uint4 *)(dcs_scan + (bi * 3 + r) * Di + c0)
+                                         : uint4{0u, 0u, 0u, 0u};
+                const uint32_t p[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float v2[2];
+#pragma unroll
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int c = 2 * e + h2;
+                        float acc = __uint_as_float(h2 ? (p[e] & 0xffff0000u) : (p[e] << 16));
+                        // token r - 3 is tap k of token t' = r - 3 + 3 - k = r - k
+#pragma unroll
+                        for (int k = 0; k <= r; ++k) acc += wk[c][k] * dp[1 + r - k][c];
+                        v2[h2] = acc;
+                    }
+                    o[e] = (uint32_t)from_f<bf16>(v2[0]) | ((uint32_t)from_f<bf16>(v2[1]) << 16);
+                }
+                *(uint4 *)(dcs + (bi * 3 + r) * Di + c0) = uint4{o[0], o[1], o[2], o[3]};
+            }
+        }
+    }
+    float *pp = dw_part + ((bi * nseg + blockIdx.y) * Di + c0) * 4;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+        *(float4 *)(pp + c * 4) = float4{dws[c][0], dws[c][1], dws[c][2], dws[c][3]};
+}
+
+// dconv_w = dconv_w of the scan + the per-segment partials, summed in order
+__global__ void mixer_dw_reduce_kernel(const int64_t Di, const int64_t nparts,
+                                       const float *__restrict__ dw_scan,
+                                       const float *__restrict__ dw_part, float *__restrict__ dw)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (channel, tap)
+    if (i >= Di * 4) return;
+    float acc = dw_scan[i];
+    for (int64_t p = 0; p < nparts; ++p) acc += dw_part[p * Di * 4 + i];
+    dw[i] = acc;
+}
+
+__global__ void fill_bf16_kernel(bf16 *p, int64_t n, uint16_t v)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+struct MixerBwdPlan {
+    MixerPlan f;
+    size_t off_ck, off_dy, off_dub, off_dz, off_da, off_db, off_dB, off_dC, off_dwb, off_dcsb,
+        off_dh, off_du, off_ones, off_dwp, off_bws, bytes;
+    int nseg;
+};
+
+static MixerBwdPlan mixer_bwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N)
+{
+    MixerBwdPlan m{};
+    m.f = mixer_plan(Bt, L, Di, N);
+    const size_t act = up256((size_t)(Bt * L * Di) * 2), tok = up256((size_t)(Bt * L * N) * 2);
+    m.nseg = (int)((L + kSegB - 1) / kSegB);
+    size_t o = m.f.bytes;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += up256(bytes);
+        return at;
+    };
+    m.off_ck = take(ckpt_bytes(Bt, L, Di, N));
+    m.off_dy = take(act);
+    m.off_dub = take(act);
+    m.off_dz = take(act);
+    m.off_da = take(act);
+    m.off_db = take(act);
+    m.off_dB = take(tok);
+    m.off_dC = take(tok);
+    m.off_dwb = take((size_t)Di * 16);
+    m.off_dcsb = take((size_t)Bt * 3 * Di * 2);
+    m.off_dh = take((size_t)(Bt * L * Di) * 4);
+    m.off_du = take(act);
+    m.off_ones = take((size_t)(Bt * L) * 2);
+    m.off_dwp = take((size_t)Bt * m.nseg * Di * 16);
+    m.off_bws = take(bwd_plan(Bt, L, Di, N, true).bytes);
+    m.bytes = o;
+    return m;
+}
+
+size_t mixer_bwd_ws_bytes(int64_t Bt, int64_t L, int64_t Di, int64_t N)
+{
+    return mixer_bwd_plan(Bt, L, Di, N).bytes;
+}
+
+// forward part shared by both directions: u, z, h, a, b, B, C, y (+ checkpoints)
+static const char *mixer_forward_pass(const MixerArgs &g, const MixerPlan &m, float *ckpt,
+                                      hipStream_t st)
+{
     char *ws = (char *)g.ws;
     void *u = ws + m.off_u, *z = ws + m.off_z, *h = ws + m.off_h, *a = ws + m.off_a,
          *b = ws + m.off_b, *y = ws + m.off_y, *B = ws + m.off_B, *C = ws + m.off_C;
@@ -287,9 +539,97 @@ const char *mixer_fwd(const MixerArgs &g, hipStream_t st)
     f.conv_w = g.conv_w;
     f.conv_state = g.conv_state;
     f.y = y;
+    f.ckpt = ckpt;
     f.ws = ws + m.off_f;
     if (launch_fwd(f, st) != hipSuccess) return "block forward launch failed";
-    if ((e = gemm(st, T, g.dm, g.Di, y, g.W_out, nullptr, g.res, g.out, gws))) return e;
+    return nullptr;
+}
+
+const char *mixer_bwd(const MixerArgs &g, const MixerGrads &d, hipStream_t st)
+{
+    const MixerBwdPlan m = mixer_bwd_plan(g.Bt, g.L, g.Di, g.N);
+    char *ws = (char *)g.ws;
+    const MixerPlan &f = m.f;
+    void *u = ws + f.off_u, *z = ws + f.off_z, *h = ws + f.off_h, *a = ws + f.off_a,
+         *b = ws + f.off_b, *y = ws + f.off_y, *B = ws + f.off_B, *C = ws + f.off_C;
+    void *gws = ws + f.off_g;
+    float *ck = (float *)(ws + m.off_ck);
+    void *dy = ws + m.off_dy, *dub = ws + m.off_dub, *dz = ws + m.off_dz, *da = ws + m.off_da,
+         *db = ws + m.off_db, *dB = ws + m.off_dB, *dC = ws + m.off_dC;
+    float *dwb = (float *)(ws + m.off_dwb), *dh = (float *)(ws + m.off_dh);
+    float *dwp = (float *)(ws + m.off_dwp);
+    void *dcsb = ws + m.off_dcsb, *du = ws + m.off_du;
+    bf16 *ones = (bf16 *)(ws + m.off_ones);
+    const int64_t T = g.Bt * g.L;
+    const bool want_dcs = g.conv_state && d.dconv_state;
+    const char *e;
+    if ((e = mixer_forward_pass(g, f, ck, st))) return e;
+    // out = y W_out + res
+    if ((e = gemm_nt(st, T, g.Di, g.dm, d.d_out, g.W_out, false, dy, HIP_R_16BF, gws))) return e;
+    if ((e = gemm_wgrad(st, T, g.dm, g.Di, y, d.d_out, d.dW_out, gws))) return e;
+    // the block scan
+    BwdArgs k{};
+    k.io = NAJU_BF16;
+    k.N = (int)g.N;
+    k.block = true;
+    k.Bt = g.Bt;
+    k.L = g.L;
+    k.Di = g.Di;
+    k.scale = g.scale;
+    k.hu = u;
+    k.a = a;
+    k.b = b;
+    k.B = B;
+    k.C = C;
+    k.D = g.D;
+    k.z = z;
+    k.conv_w = g.conv_w;
+    k.conv_state = g.conv_state;
+    k.ckpt = ck;
+    k.dy = dy;
+    k.dhu = dub;
+    k.da = da;
+    k.db = db;
+    k.dB = dB;
+    k.dC = dC;
+    k.dz = dz;
+    k.dD = d.dD;
+    k.dconv_w = dwb;
+    k.dconv_state = want_dcs ? dcsb : nullptr;
+    k.ws = ws + m.off_bws;
+    if (launch_bwd(k, st) != hipSuccess) return "block backward launch failed";
+    // a = h W_a + a_bias, b = h W_b + b_bias, B = h W_B, C = h W_C
+    if ((e = gemm_nt(st, T, g.Di, g.Di, da, g.W_a, false, dh, HIP_R_32F, gws))) return e;
+    if ((e = gemm_nt(st, T, g.Di, g.Di, db, g.W_b, true, dh, HIP_R_32F, gws))) return e;
+    if ((e = gemm_nt(st, T, g.Di, g.N, dB, g.W_B, true, dh, HIP_R_32F, gws))) return e;
+    if ((e = gemm_nt(st, T, g.Di, g.N, dC, g.W_C, true, dh, HIP_R_32F, gws))) return e;
+    if ((e = gemm_wgrad(st, T, g.Di, g.Di, h, da, d.dW_a, gws))) return e;
+    if ((e = gemm_wgrad(st, T, g.Di, g.Di, h, db, d.dW_b, gws))) return e;
+    if ((e = gemm_wgrad(st, T, g.N, g.Di, h, dB, d.dW_B, gws))) return e;
+    if ((e = gemm_wgrad(st, T, g.N, g.Di, h, dC, d.dW_C, gws))) return e;
+    // bias gradients: column sums of da, db, as products with a vector of ones
+    hipLaunchKernelGGL(fill_bf16_kernel, dim3(256), dim3(256), 0, st, ones, T, (uint16_t)0x3F80);
+    if (hipGetLastError() != hipSuccess) return "fill launch failed";
+    if ((e = gemm_wgrad(st, T, g.Di, 1, ones, da, d.da_bias, gws))) return e;
+    if ((e = gemm_wgrad(st, T, g.Di, 1, ones, db, d.db_bias, gws))) return e;
+    // h = SiLU(conv(u)) on the projection path, plus the scan's own du
+    {
+        const dim3 grid((unsigned)((g.Di / 8 + 63) / 64), (unsigned)m.nseg, (unsigned)g.Bt);
+        hipLaunchKernelGGL(conv_silu_bwd_kernel, grid, dim3(64), 0, st, g.L, g.Di, m.nseg,
+                           (const bf16 *)u, g.conv_w, (const bf16 *)g.conv_state, dh,
+                           (const bf16 *)dub, (bf16 *)du, dwp,
+                           want_dcs ? (const bf16 *)dcsb : nullptr,
+                           want_dcs ? (bf16 *)d.dconv_state : nullptr);
+        if (hipGetLastError() != hipSuccess) return "conv backward launch failed";
+        hipLaunchKernelGGL(mixer_dw_reduce_kernel, dim3((unsigned)((g.Di * 4 + 255) / 256)),
+                           dim3(256), 0, st, g.Di, g.Bt * (int64_t)m.nseg, dwb, dwp, d.dconv_w);
+        if (hipGetLastError() != hipSuccess) return "dconv_w reduction launch failed";
+    }
+    // u = xn W_u, z = xn W_z
+    if ((e = gemm_nt(st, T, g.dm, g.Di, du, g.W_u, false, d.dxn, HIP_R_32F, gws))) return e;
+    if ((e = gemm_nt(st, T, g.dm, g.Di, dz, g.W_z, true, d.dxn, HIP_R_32F, gws))) return e;
+    if ((e = gemm_wgrad(st, T, g.Di, g.dm, g.xn, du, d.dW_u, gws))) return e;
+    if ((e = gemm_wgrad(st, T, g.Di, g.dm, g.xn, dz, d.dW_z, gws))) return e;
     return nullptr;
 }
 

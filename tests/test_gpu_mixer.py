@@ -77,3 +77,31 @@ def test_mixer_repeat_calls_are_identical():
     o1 = host(nb.mixer_fwd(*args, res=t["res"]))
     o2 = host(nb.mixer_fwd(*args, res=t["res"]))
     assert_close("repeat", o2, o1, 1e-2)
+
+
+BWD_CASES = [
+    # Bt, L, d_model, d_inner, d_state, conv_state
+    (2, 200, 64, 128, 16, False),
+    (1, 333, 96, 64, 64, True),
+    (2, 130, 32, 256, 16, True),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "b%d_l%d_dm%d_d%d_n%d" % c[:5])
+def test_mixer_backward_matches_oracle(case):
+    Bt, L, dm, Di, N, cs = case
+    print("mixer bwd case Bt=%d L=%d dm=%d Di=%d N=%d cs=%s" % case, flush=True)
+    d = inputs.draw_mixer(Bt, L, dm, Di, N, seed=91, residual=False, conv_state=cs)
+    g = inputs.bf16_round(np.random.default_rng(92).standard_normal((Bt, L, dm)).astype(np.float32))
+    t = {k: (f32_dev(v) if k in FP32_KEYS else to_dev(v, "bf16")) for k, v in d.items()}
+    got = nb.mixer_bwd(t["xn"], t["W_u"], t["W_z"], t["conv_w"], t["W_a"], t["a_bias"],
+                       t["W_b"], t["b_bias"], t["W_B"], t["W_C"], t["D"], t["W_out"],
+                       to_dev(g, "bf16"), conv_state=t.get("conv_state"))
+    torch.cuda.synchronize()
+    ref = oracle.mixer_bwd(d["xn"], d["W_u"], d["W_z"], d["conv_w"], d["W_a"], d["a_bias"],
+                           d["W_b"], d["b_bias"], d["W_B"], d["W_C"], d["D"], d["W_out"], g,
+                           conv_state=d.get("conv_state"))
+    names = ["dxn", "dW_u", "dW_z", "dconv_w", "dW_a", "da_bias", "dW_b", "db_bias", "dW_B",
+             "dW_C", "dD", "dW_out"] + (["dconv_state"] if cs else [])
+    for k in names:
+        assert_close(k, host(got[k]), ref[k], TOL["bf16"])
