@@ -441,24 +441,49 @@ __global__ __launch_bounds__(64) void conv_silu_bwd_kernel(
         *(float4 *)(pp + c * 4) = float4{dws[c][0], dws[c][1], dws[c][2], dws[c][3]};
 }
 
-// dconv_w = dconv_w of the scan + the per-segment partials, summed in order
-__global__ void mixer_dw_reduce_kernel(const int64_t Di, const int64_t nparts,
-                                       const float *__restrict__ dw_scan,
-                                       const float *__restrict__ dw_part, float *__restrict__ dw)
+// Column sums of a [rows][cols] array (fp32 partials or bf16 values) in a
+// fixed order: workgroup (column block of 64, row slice); its 4 waves take
+// interleaved rows of the slice, then combine in LDS in wave order.  With
+// rows_per == rows a single launch gives the final sums (plus `add`, if any).
+template <typename T>
+__global__ __launch_bounds__(256) void colsum_kernel(const int64_t rows, const int64_t cols,
+                                                     const int64_t rows_per,
+                                                     const T *__restrict__ x,
+                                                     const float *__restrict__ add,
+                                                     float *__restrict__ out)
 {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // (channel, tap)
-    if (i >= Di * 4) return;
-    float acc = dw_scan[i];
-    for (int64_t p = 0; p < nparts; ++p) acc += dw_part[p * Di * 4 + i];
-    dw[i] = acc;
+    __shared__ float part[4][64];
+    const int64_t c = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+    const int wv = threadIdx.x >> 6;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per;
+    const int64_t r1 = r0 + rows_per < rows ? r0 + rows_per : rows;
+    float acc = 0.f;
+    if (c < cols)
+        for (int64_t r = r0 + wv; r < r1; r += 4) acc += to_f(x[r * cols + c]);
+    part[wv][threadIdx.x & 63] = acc;
+    __syncthreads();
+    if (wv == 0 && c < cols) {
+        float t = part[0][threadIdx.x] + part[1][threadIdx.x] + part[2][threadIdx.x] +
+                  part[3][threadIdx.x];
+        if (add) t += add[c];
+        out[(int64_t)blockIdx.y * cols + c] = t;
+    }
 }
 
-__global__ void fill_bf16_kernel(bf16 *p, int64_t n, uint16_t v)
+// two fixed-order passes: [rows][cols] -> [slices][cols] -> out (+ add)
+template <typename T>
+static hipError_t colsum(const T *x, int64_t rows, int64_t cols, const float *add, float *tmp,
+                         int64_t slices, float *out, hipStream_t st)
 {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = v;
+    const int64_t per = (rows + slices - 1) / slices;
+    const unsigned cb = (unsigned)((cols + 63) / 64);
+    hipLaunchKernelGGL(colsum_kernel<T>, dim3(cb, (unsigned)slices), dim3(256), 0, st, rows,
+                       cols, per, x, (const float *)nullptr, tmp);
+    hipLaunchKernelGGL(colsum_kernel<float>, dim3(cb, 1), dim3(256), 0, st, slices, cols, slices,
+                       (const float *)tmp, add, out);
+    return hipGetLastError();
 }
+constexpr int64_t kSlices = 256;  // row slices of the first column-sum pass
 
 struct MixerBwdPlan {
     MixerPlan f;
@@ -491,7 +516,7 @@ static MixerBwdPlan mixer_bwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N)
     m.off_dcsb = take((size_t)Bt * 3 * Di * 2);
     m.off_dh = take((size_t)(Bt * L * Di) * 4);
     m.off_du = take(act);
-    m.off_ones = take((size_t)(Bt * L) * 2);
+    m.off_ones = take((size_t)kSlices * Di * 16);  // column-sum partials (up to Di * 4 columns)
     m.off_dwp = take((size_t)Bt * m.nseg * Di * 16);
     m.off_bws = take(bwd_plan(Bt, L, Di, N, true).bytes);
     m.bytes = o;
@@ -559,7 +584,7 @@ const char *mixer_bwd(const MixerArgs &g, const MixerGrads &d, hipStream_t st)
     float *dwb = (float *)(ws + m.off_dwb), *dh = (float *)(ws + m.off_dh);
     float *dwp = (float *)(ws + m.off_dwp);
     void *dcsb = ws + m.off_dcsb, *du = ws + m.off_du;
-    bf16 *ones = (bf16 *)(ws + m.off_ones);
+    float *csum = (float *)(ws + m.off_ones);
     const int64_t T = g.Bt * g.L;
     const bool want_dcs = g.conv_state && d.dconv_state;
     const char *e;
@@ -607,11 +632,10 @@ const char *mixer_bwd(const MixerArgs &g, const MixerGrads &d, hipStream_t st)
     if ((e = gemm_wgrad(st, T, g.Di, g.Di, h, db, d.dW_b, gws))) return e;
     if ((e = gemm_wgrad(st, T, g.N, g.Di, h, dB, d.dW_B, gws))) return e;
     if ((e = gemm_wgrad(st, T, g.N, g.Di, h, dC, d.dW_C, gws))) return e;
-    // bias gradients: column sums of da, db, as products with a vector of ones
-    hipLaunchKernelGGL(fill_bf16_kernel, dim3(256), dim3(256), 0, st, ones, T, (uint16_t)0x3F80);
-    if (hipGetLastError() != hipSuccess) return "fill launch failed";
-    if ((e = gemm_wgrad(st, T, g.Di, 1, ones, da, d.da_bias, gws))) return e;
-    if ((e = gemm_wgrad(st, T, g.Di, 1, ones, db, d.db_bias, gws))) return e;
+    // bias gradients: column sums of da and db (two fixed-order passes)
+    if (colsum((const bf16 *)da, T, g.Di, nullptr, csum, kSlices, d.da_bias, st) != hipSuccess ||
+        colsum((const bf16 *)db, T, g.Di, nullptr, csum, kSlices, d.db_bias, st) != hipSuccess)
+        return "bias gradient launch failed";
     // h = SiLU(conv(u)) on the projection path, plus the scan's own du
     {
         const dim3 grid((unsigned)((g.Di / 8 + 63) / 64), (unsigned)m.nseg, (unsigned)g.Bt);
@@ -621,9 +645,10 @@ const char *mixer_bwd(const MixerArgs &g, const MixerGrads &d, hipStream_t st)
                            want_dcs ? (const bf16 *)dcsb : nullptr,
                            want_dcs ? (bf16 *)d.dconv_state : nullptr);
         if (hipGetLastError() != hipSuccess) return "conv backward launch failed";
-        hipLaunchKernelGGL(mixer_dw_reduce_kernel, dim3((unsigned)((g.Di * 4 + 255) / 256)),
-                           dim3(256), 0, st, g.Di, g.Bt * (int64_t)m.nseg, dwb, dwp, d.dconv_w);
-        if (hipGetLastError() != hipSuccess) return "dconv_w reduction launch failed";
+        // dconv_w = the scan's + the segments' partials ([segments][Di * 4])
+        if (colsum((const float *)dwp, g.Bt * (int64_t)m.nseg, g.Di * 4, dwb, csum, kSlices,
+                   d.dconv_w, st) != hipSuccess)
+            return "dconv_w reduction launch failed";
     }
     // u = xn W_u, z = xn W_z
     if ((e = gemm_nt(st, T, g.dm, g.Di, du, g.W_u, false, d.dxn, HIP_R_32F, gws))) return e;
