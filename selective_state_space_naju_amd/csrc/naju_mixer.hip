@@ -483,7 +483,7 @@ static hipError_t colsum(const T *x, int64_t rows, int64_t cols, const float *ad
                        (const float *)tmp, add, out);
     return hipGetLastError();
 }
-constexpr int64_t kSlices = 256;  // row slices of the first column-sum pass
+constexpr int64_t kSlices = 64;  // row slices of the first column-sum pass
 
 struct MixerBwdPlan {
     MixerPlan f;
