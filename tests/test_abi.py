@@ -154,6 +154,32 @@ def test_validation_errors_mixer(lib):
     assert lib.naju_mixer_workspace_bytes(ctypes.byref(dims(d_state=48)), 64) == 0
 
 
+def test_validation_errors_mixer_bwd(lib):
+    # dims, d_model, 14 inputs (xn .. d_out), 13 gradients, ws, ws_bytes, stream
+    def call(d, dm=64, **over):
+        ins = dict(xn=FAKE, W_u=FAKE, W_z=FAKE, conv_w=FAKE, conv_state=None, W_a=FAKE,
+                   a_bias=FAKE, W_b=FAKE, b_bias=FAKE, W_B=FAKE, W_C=FAKE, D=FAKE, W_out=FAKE,
+                   d_out=FAKE)
+        outs = dict(dxn=FAKE, dW_u=FAKE, dW_z=FAKE, dconv_w=FAKE, dconv_state=None, dW_a=FAKE,
+                    da_bias=FAKE, dW_b=FAKE, db_bias=FAKE, dW_B=FAKE, dW_C=FAKE, dD=FAKE,
+                    dW_out=FAKE)
+        for k, v in over.items():
+            if k not in ("ws", "wsb"):
+                (ins if k in ins else outs)[k] = v
+        return lib.naju_mixer_bwd(ctypes.byref(d), dm, *ins.values(), *outs.values(),
+                                  over.get("ws", FAKE), over.get("wsb", 1 << 40), None)
+    d = dims(d_inner=128)
+    assert call(d, d_out=None) == nb.EINVAL
+    assert "d_out is NULL" in nb.last_error()
+    assert call(d, dW_a=None) == nb.EINVAL
+    assert "dW_a is NULL" in nb.last_error()
+    assert call(d, dxn=FAKE + 4) == nb.EINVAL
+    assert call(dims(d_inner=128, io=nb.F32)) == nb.EUNSUPPORTED
+    assert call(dims(d_inner=128, batch=0), xn=None) == nb.OK
+    fwd = lib.naju_mixer_workspace_bytes(ctypes.byref(d), 64)
+    assert lib.naju_mixer_bwd_workspace_bytes(ctypes.byref(d), 64) > fwd
+
+
 def test_workspace_and_ckpt_sizes(lib):
     d = dims(batch=8, seqlen=2048, d_inner=1536)
     for op in range(4):
