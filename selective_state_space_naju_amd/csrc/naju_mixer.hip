@@ -485,10 +485,37 @@ static hipError_t colsum(const T *x, int64_t rows, int64_t cols, const float *ad
 }
 constexpr int64_t kSlices = 64;  // row slices of the first column-sum pass
 
+// [X | Y] row by row: out[r][0:nx] = x[r], out[r][nx:nx+ny] = y[r] (bf16), or the
+// reverse split of fp32 rows (unpack) -- to run the two narrow B and C products
+// of the backward as one
+__global__ void pack2_kernel(const int64_t rows, const int nx, const bf16 *__restrict__ x,
+                             const bf16 *__restrict__ y, bf16 *__restrict__ out)
+{
+    const int w = 2 * nx;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows * w;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / w;
+        const int c = (int)(i - r * w);
+        out[i] = c < nx ? x[r * nx + c] : y[r * nx + c - nx];
+    }
+}
+
+__global__ void unpack2_kernel(const int64_t rows, const int nx, const float *__restrict__ in,
+                               float *__restrict__ x, float *__restrict__ y)
+{
+    const int w = 2 * nx;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows * w;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / w;
+        const int c = (int)(i - r * w);
+        (c < nx ? x[r * nx + c] : y[r * nx + c - nx]) = in[i];
+    }
+}
+
 struct MixerBwdPlan {
     MixerPlan f;
     size_t off_ck, off_dy, off_dub, off_dz, off_da, off_db, off_dB, off_dC, off_dwb, off_dcsb,
-        off_dh, off_du, off_ones, off_dwp, off_bws, bytes;
+        off_dh, off_du, off_ones, off_dwp, off_bws, off_dBC, off_WBC, off_gBC, bytes;
     int nseg;
 };
 
@@ -519,6 +546,9 @@ static MixerBwdPlan mixer_bwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N)
     m.off_ones = take((size_t)kSlices * Di * 16);  // column-sum partials (up to Di * 4 columns)
     m.off_dwp = take((size_t)Bt * m.nseg * Di * 16);
     m.off_bws = take(bwd_plan(Bt, L, Di, N, true).bytes);
+    m.off_dBC = take((size_t)(Bt * L) * 2 * N * 2);  // [dB | dC] bf16 [T][2N]
+    m.off_WBC = take((size_t)Di * 2 * N * 2);         // [W_B | W_C] bf16 [Di][2N]
+    m.off_gBC = take((size_t)Di * 2 * N * 4);         // [dW_B | dW_C] fp32 [Di][2N]
     m.bytes = o;
     return m;
 }
@@ -626,12 +656,22 @@ const char *mixer_bwd(const MixerArgs &g, const MixerGrads &d, hipStream_t st)
     // a = h W_a + a_bias, b = h W_b + b_bias, B = h W_B, C = h W_C
     if ((e = gemm_nt(st, T, g.Di, g.Di, da, g.W_a, false, dh, HIP_R_32F, gws))) return e;
     if ((e = gemm_nt(st, T, g.Di, g.Di, db, g.W_b, true, dh, HIP_R_32F, gws))) return e;
-    if ((e = gemm_nt(st, T, g.Di, g.N, dB, g.W_B, true, dh, HIP_R_32F, gws))) return e;
-    if ((e = gemm_nt(st, T, g.Di, g.N, dC, g.W_C, true, dh, HIP_R_32F, gws))) return e;
+    // the B and C terms as one product over [dB | dC] and [W_B | W_C] (each narrow
+    // product would otherwise read and write all of dh, or read all of h)
+    bf16 *dBC = (bf16 *)(ws + m.off_dBC), *WBC = (bf16 *)(ws + m.off_WBC);
+    float *gBC = (float *)(ws + m.off_gBC);
+    hipLaunchKernelGGL(pack2_kernel, dim3(1024), dim3(256), 0, st, T, (int)g.N,
+                       (const bf16 *)dB, (const bf16 *)dC, dBC);
+    hipLaunchKernelGGL(pack2_kernel, dim3(256), dim3(256), 0, st, g.Di, (int)g.N,
+                       (const bf16 *)g.W_B, (const bf16 *)g.W_C, WBC);
+    if (hipGetLastError() != hipSuccess) return "pack launch failed";
+    if ((e = gemm_nt(st, T, g.Di, 2 * g.N, dBC, WBC, true, dh, HIP_R_32F, gws))) return e;
     if ((e = gemm_wgrad(st, T, g.Di, g.Di, h, da, d.dW_a, gws))) return e;
     if ((e = gemm_wgrad(st, T, g.Di, g.Di, h, db, d.dW_b, gws))) return e;
-    if ((e = gemm_wgrad(st, T, g.N, g.Di, h, dB, d.dW_B, gws))) return e;
-    if ((e = gemm_wgrad(st, T, g.N, g.Di, h, dC, d.dW_C, gws))) return e;
+    if ((e = gemm_wgrad(st, T, 2 * g.N, g.Di, h, dBC, gBC, gws))) return e;
+    hipLaunchKernelGGL(unpack2_kernel, dim3(256), dim3(256), 0, st, g.Di, (int)g.N,
+                       (const float *)gBC, d.dW_B, d.dW_C);
+    if (hipGetLastError() != hipSuccess) return "unpack launch failed";
     // bias gradients: column sums of da and db (two fixed-order passes)
     if (colsum((const bf16 *)da, T, g.Di, nullptr, csum, kSlices, d.da_bias, st) != hipSuccess ||
         colsum((const bf16 *)db, T, g.Di, nullptr, csum, kSlices, d.db_bias, st) != hipSuccess)
