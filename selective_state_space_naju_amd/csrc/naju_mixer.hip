@@ -34,59 +34,56 @@
 namespace naju {
 
 // ------------------------------------------------------------ conv + SiLU
-// Thread = (batch row, 8 channels, 16-token segment), one wave per workgroup:
-// the segment's 16 rows (and the 3 rows before it) are loaded together, 16
-// bytes per thread and row, then the 4-tap window slides in registers; a
-// wave covers 64 x 16 consecutive bytes of a row.
-constexpr int kSeg = 16;
+// Thread = (batch row, 8 channels, 32-token segment): the 4-tap window slides
+// in registers, so each u row is read once (plus 3 halo rows per segment);
+// a wave covers 64 x 16 consecutive bytes of a row.
+constexpr int kSeg = 32;
 
-__global__ __launch_bounds__(64) void conv_silu_kernel(const int64_t L, const int64_t Di,
-                                                       const bf16 *__restrict__ u,
-                                                       const float *__restrict__ w,
-                                                       const bf16 *__restrict__ cs,
-                                                       bf16 *__restrict__ h)
+__global__ __launch_bounds__(256) void conv_silu_kernel(const int64_t L, const int64_t Di,
+                                                        const bf16 *__restrict__ u,
+                                                        const float *__restrict__ w,
+                                                        const bf16 *__restrict__ cs,
+                                                        bf16 *__restrict__ h)
 {
-    const int64_t c0 = ((int64_t)blockIdx.x * 64 + threadIdx.x) * 8;
+    const int64_t c0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
     if (c0 >= Di) return;
     const int64_t n0 = (int64_t)blockIdx.y * kSeg;
     const int64_t bi = blockIdx.z;
     const bf16 *ub = u + bi * L * Di + c0;
-    const int rows = (int)(L - n0 < kSeg ? L - n0 : kSeg);
-    // h rows of the segment through a buffer whose range ends with the last
-    // valid row: stores past the sequence end are dropped, no branch per row
-    const rsrc_t rh = make_rsrc(h + (bi * L + n0) * Di, (uint32_t)rows * (uint32_t)Di * 2);
-    // u at tokens n0-3 .. n0+kSeg-1, every load unconditional (rows past the end
-    // re-read the last row and are never stored; rows before the sequence come
-    // from conv_state, or are zero), so they are all in flight together
-    uint4 q[kSeg + 3];
-#pragma unroll
-    for (int r = 0; r < kSeg + 3; ++r) {
-        const int64_t m = n0 - 3 + r;
-        const bf16 *src;
-        if (m >= 0)
-            src = ub + (m < L ? m : L - 1) * Di;
-        else
-            src = cs ? cs + (bi * 3 + (m + 3)) * Di + c0 : ub;
-        q[r] = *(const uint4 *)src;
-    }
-#pragma unroll
-    for (int r = 0; r < 3; ++r)
-        if (n0 - 3 + r < 0 && !cs) q[r] = uint4{0u, 0u, 0u, 0u};
+    bf16 *hb = h + bi * L * Di + c0;
     float wk[8][4];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float4 v = *(const float4 *)(w + (c0 + e) * 4);
-        wk[e][0] = v.x;
-        wk[e][1] = v.y;
-        wk[e][2] = v.z;
-        wk[e][3] = v.w;
+        const float4 q = *(const float4 *)(w + (c0 + e) * 4);
+        wk[e][0] = q.x;
+        wk[e][1] = q.y;
+        wk[e][2] = q.z;
+        wk[e][3] = q.w;
     }
-    auto at = [&](int r, int c) -> float {  // channel c0 + c of row r
-        const uint32_t p = c < 2 ? q[r].x : c < 4 ? q[r].y : c < 6 ? q[r].z : q[r].w;
-        return __uint_as_float((c & 1) ? (p & 0xffff0000u) : (p << 16));
-    };
+    auto unpack = [](const uint4 &q, float (&v)[8]) {
+        const uint32_t p[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-    for (int t = 0; t < kSeg; ++t) {
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = __uint_as_float(p[e] << 16);
+            v[2 * e + 1] = __uint_as_float(p[e] & 0xffff0000u);
+        }
+    };
+    // window: u at tokens n-3, n-2, n-1 (before the sequence: conv_state or 0)
+    float win[3][8];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+        const int64_t m = n0 - 3 + r;
+        uint4 q = {0u, 0u, 0u, 0u};
+        if (m >= 0)
+            q = *(const uint4 *)(ub + m * Di);
+        else if (cs)
+            q = *(const uint4 *)(cs + (bi * 3 + (m + 3)) * Di + c0);
+        unpack(q, win[r]);
+    }
+    const int64_t n1 = n0 + kSeg < L ? n0 + kSeg : L;
+    for (int64_t n = n0; n < n1; ++n) {
+        float cur[8];
+        unpack(*(const uint4 *)(ub + n * Di), cur);
         uint32_t o[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -94,16 +91,19 @@ __global__ __launch_bounds__(64) void conv_silu_kernel(const int64_t L, const in
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const int c = e + k;
-                const float pre = wk[c][0] * at(t, c) + wk[c][1] * at(t + 1, c) +
-                                  wk[c][2] * at(t + 2, c) + wk[c][3] * at(t + 3, c);
+                const float pre = wk[c][0] * win[0][c] + wk[c][1] * win[1][c] +
+                                  wk[c][2] * win[2][c] + wk[c][3] * cur[c];
                 hv[k] = pre * sigm(pre);
             }
             o[e / 2] = (uint32_t)from_f<bf16>(hv[0]) | ((uint32_t)from_f<bf16>(hv[1]) << 16);
         }
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 ov = {o[0], o[1], o[2], o[3]};
-        __builtin_amdgcn_raw_buffer_store_b128(ov, rh, (uint32_t)c0 * 2,
-                                               (uint32_t)t * (uint32_t)Di * 2, 0);
+        *(uint4 *)(hb + n * Di) = uint4{o[0], o[1], o[2], o[3]};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            win[0][c] = win[1][c];
+            win[1][c] = win[2][c];
+            win[2][c] = cur[c];
+        }
     }
 }
 
@@ -285,9 +285,9 @@ hipError_t launch_conv_silu(int64_t Bt, int64_t L, int64_t Di, const void *u, co
                             const void *cs, void *h, hipStream_t st)
 {
     if (Bt == 0 || L == 0 || Di == 0) return hipSuccess;
-    const dim3 grid((unsigned)((Di / 8 + 63) / 64), (unsigned)((L + kSeg - 1) / kSeg),
+    const dim3 grid((unsigned)((Di / 8 + 255) / 256), (unsigned)((L + kSeg - 1) / kSeg),
                     (unsigned)Bt);
-    hipLaunchKernelGGL(conv_silu_kernel, grid, dim3(64), 0, st, L, Di, (const bf16 *)u, w,
+    hipLaunchKernelGGL(conv_silu_kernel, grid, dim3(256), 0, st, L, Di, (const bf16 *)u, w,
                        (const bf16 *)cs, (bf16 *)h);
     return hipGetLastError();
 }

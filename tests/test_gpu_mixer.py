@@ -37,6 +37,7 @@ CASES = [
     (1, 1, 32, 64, 16, False, True),       # one token: conv window entirely from conv_state
     (3, 17, 40, 72, 16, False, False),     # one partial conv segment, d_inner not a multiple of 64
     (2, 50, 16, 8, 64, False, True),       # the smallest d_inner, register form of the scan
+    (8, 2048, 64, 128, 16, False, False),  # the training batch shape (16384 tokens), narrow layer
 ]
 
 FP32_KEYS = ("conv_w", "D", "a_bias", "b_bias")
@@ -84,6 +85,7 @@ BWD_CASES = [
     (2, 200, 64, 128, 16, False),
     (1, 333, 96, 64, 64, True),
     (2, 130, 32, 256, 16, True),
+    (8, 2048, 64, 128, 16, False),  # the training batch shape (16384 tokens), narrow layer
 ]
 
 
