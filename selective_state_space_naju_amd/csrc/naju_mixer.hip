@@ -196,9 +196,9 @@ static const char *gemm_cm(hipStream_t st, const GemmShape &g, const void *X, co
         if (pref) hipblasLtMatmulPreferenceDestroy(pref);
         if (!found) return "hipBLASLt found no algorithm for a product";
         // (the heuristic's first choice: timing its other candidates on the
-        // 8 x 2048-token layer made single projections up to 6 % faster, but the
-        // block scan after them as much slower, and the whole layer no faster;
-        // it would also synchronise the stream on a shape's first call)
+        // 8 x 2048-token layer made single projections up to 6 % faster, but it
+        // synchronises the stream on a shape's first call, and the gain for the
+        // whole layer was not established)
         p.algo = res[0].algo;
         p.ws = res[0].workspaceSize;
         p.ok = true;
