@@ -105,6 +105,11 @@ def test_scan_bf16_l8192_n64_sampled_and_chained():
     # chain == single call over every channel
     assert_close("chain/single y", host(yc), host(y), TOL["bf16"])
     assert_close("chain/single x", host(x), host(xf), 1e-4)
+    # every output of a second call is bit for bit the first (this form has no
+    # look-back, so nothing may depend on timing: a lost or late store would show)
+    y2, xf2 = nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], D)
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y) and torch.equal(xf2, xf)
 
 
 def test_scan_bf16_l65536_sampled():
