@@ -352,10 +352,13 @@ def bench_mixer_workload(args, torch, nb, inputs):
     sets = [t["xn"], t["xn"].roll(1, 0).contiguous()]
     res = [t["res"], t["res"].roll(1, 0).contiguous()]
 
+    dims = nb.make_dims(Bt, L, Di, N, nb.BF16)
+    fws = nb.Workspace(int(nb.lib().naju_mixer_workspace_bytes(ctypes.byref(dims), dm)), dev)
+
     def call(i):
         nb.mixer_fwd(sets[i % 2], t["W_u"], t["W_z"], t["conv_w"], t["W_a"], t["a_bias"],
                      t["W_b"], t["b_bias"], t["W_B"], t["W_C"], t["D"], t["W_out"],
-                     res=res[i % 2])
+                     res=res[i % 2], ws=fws)
 
     def timed(fn, steps):
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -380,9 +383,11 @@ def bench_mixer_workload(args, torch, nb, inputs):
         nb.mixer_bwd(sets[i % 2], t["W_u"], t["W_z"], t["conv_w"], t["W_a"], t["a_bias"],
                      t["W_b"], t["b_bias"], t["W_B"], t["W_C"], t["D"], t["W_out"], g_out[i % 2])
 
-    def call_step(i):
+    def call_step(i):  # a training step: the backward reuses the forward's workspace
         call(i)
-        call_bwd(i)
+        nb.mixer_bwd(sets[i % 2], t["W_u"], t["W_z"], t["conv_w"], t["W_a"], t["a_bias"],
+                     t["W_b"], t["b_bias"], t["W_B"], t["W_C"], t["D"], t["W_out"], g_out[i % 2],
+                     fwd_ws=fws)
     for k in range(args.warmup):
         call_bwd(k)
     _, tbw = timed(call_bwd, args.steps)
@@ -417,8 +422,8 @@ def bench_mixer_workload(args, torch, nb, inputs):
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": Bt, "seq_len": L, "d_model": dm,
                    "d_inner": Di, "d_state": N, "io": "bf16",
-                   "step": "naju_mixer_fwd + naju_mixer_bwd (the backward recomputes the "
-                           "forward intermediates)"},
+                   "step": "naju_mixer_fwd + naju_mixer_bwd reusing the forward's workspace "
+                           "(parts.mixer_bwd: the backward alone, recomputing the forward)"},
         "roofline": {"kernel": "the call's hipBLASLt projections (bf16, fp32 accumulation); "
                                "time = mixer call minus the block forward alone",
                      "bound": "mfma", "achieved": round(ach_g, 1),

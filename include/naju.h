@@ -270,6 +270,10 @@ naju_status_t naju_mixer_fwd(const naju_dims_t *dims, int64_t d_model, const voi
  *   dconv_state [Bt][3][d_inner] bf16 or NULL (needs conv_state);
  *   dW_a, dW_b [d_inner][d_inner];  da_bias, db_bias [d_inner];
  *   dW_B, dW_C [d_inner][d_state];  dD [d_inner];  dW_out [d_inner][d_model]
+ *   fwd_ws        NULL (the forward intermediates are recomputed), or the workspace
+ *                 of the naju_mixer_fwd call on the same inputs, untouched since
+ *                 (it holds u, z, h, a, b, B, C, y and the scan's checkpoints, so
+ *                 the recomputation is skipped); fwd_ws_bytes its size
  *   ws            naju_mixer_bwd_workspace_bytes() bytes, as for the forward
  * Output buffers must be 16-byte aligned (dD 4-byte).
  */
@@ -282,7 +286,8 @@ naju_status_t naju_mixer_bwd(const naju_dims_t *dims, int64_t d_model, const voi
                              const void *d_out, float *dxn, float *dW_u, float *dW_z,
                              float *dconv_w, void *dconv_state, float *dW_a, float *da_bias,
                              float *dW_b, float *db_bias, float *dW_B, float *dW_C, float *dD,
-                             float *dW_out, void *ws, size_t ws_bytes, void *stream);
+                             float *dW_out, const void *fwd_ws, size_t fwd_ws_bytes, void *ws,
+                             size_t ws_bytes, void *stream);
 
 /* Thread-local description of the last non-OK status ("" if none). */
 const char *naju_last_error(void);

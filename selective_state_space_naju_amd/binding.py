@@ -87,7 +87,7 @@ def lib() -> ctypes.CDLL:
         L.naju_mixer_fwd.restype = st
         L.naju_mixer_bwd_workspace_bytes.argtypes = [dp, ctypes.c_int64]
         L.naju_mixer_bwd_workspace_bytes.restype = sz
-        L.naju_mixer_bwd.argtypes = [dp, ctypes.c_int64] + [vp] * 28 + [sz, vp]
+        L.naju_mixer_bwd.argtypes = [dp, ctypes.c_int64] + [vp] * 28 + [sz, vp, sz, vp]
         L.naju_mixer_bwd.restype = st
         L.naju_last_error.argtypes = []
         L.naju_last_error.restype = ctypes.c_char_p
@@ -387,8 +387,9 @@ def mixer_fwd(xn, W_u, W_z, conv_w, W_a, a_bias, W_b, b_bias, W_B, W_C, D, W_out
 
 
 def mixer_bwd(xn, W_u, W_z, conv_w, W_a, a_bias, W_b, b_bias, W_B, W_C, D, W_out, d_out,
-              conv_state=None, *, ws=None):
-    """Gradients of naju_mixer_fwd for upstream d_out (the residual's is d_out):
+              conv_state=None, *, fwd_ws=None, ws=None):
+    """Gradients of naju_mixer_fwd for upstream d_out (the residual's is d_out); fwd_ws:
+    the Workspace a mixer_fwd call on the same inputs used (its intermediates are reused):
     dict(dxn, dW_u, dW_z, dconv_w, dconv_state, dW_a, da_bias, dW_b, db_bias, dW_B, dW_C,
     dD, dW_out), fp32 except dconv_state (bf16, only with conv_state)."""
     Bt, L, dm = xn.shape
@@ -426,6 +427,8 @@ def mixer_bwd(xn, W_u, W_z, conv_w, W_a, a_bias, W_b, b_bias, W_B, W_C, D, W_out
                                _p(g["dW_u"]), _p(g["dW_z"]), _p(g["dconv_w"]),
                                _p(g["dconv_state"]), _p(g["dW_a"]), _p(g["da_bias"]),
                                _p(g["dW_b"]), _p(g["db_bias"]), _p(g["dW_B"]), _p(g["dW_C"]),
-                               _p(g["dD"]), _p(g["dW_out"]), ws.ptr, ws.nbytes,
+                               _p(g["dD"]), _p(g["dW_out"]),
+                               fwd_ws.ptr if fwd_ws is not None else None,
+                               fwd_ws.nbytes if fwd_ws is not None else 0, ws.ptr, ws.nbytes,
                                stream_handle(dev)))
     return g

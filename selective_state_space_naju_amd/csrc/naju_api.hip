@@ -559,10 +559,20 @@ naju_status_t naju_mixer_bwd(const naju_dims_t *dims, int64_t d_model, const voi
                              const void *d_out, float *dxn, float *dW_u, float *dW_z,
                              float *dconv_w, void *dconv_state, float *dW_a, float *da_bias,
                              float *dW_b, float *db_bias, float *dW_B, float *dW_C, float *dD,
-                             float *dW_out, void *ws, size_t ws_bytes, void *stream)
+                             float *dW_out, const void *fwd_ws, size_t fwd_ws_bytes, void *ws,
+                             size_t ws_bytes, void *stream)
 {
+    if (fwd_ws) {
+        if (check_dims(dims, true) != NAJU_OK) return check_dims(dims, true);
+        const size_t nf = mixer_ws_bytes(dims->batch, dims->seqlen, dims->d_inner, dims->d_state);
+        if (((uintptr_t)fwd_ws) % 256) return fail(NAJU_EINVAL, "fwd_ws is not 256-byte aligned");
+        if (fwd_ws_bytes < nf)
+            return fail(NAJU_EWORKSPACE, "fwd_ws has %zu bytes, a forward workspace needs %zu",
+                        fwd_ws_bytes, nf);
+    }
     MixerGrads q{};
     q.d_out = d_out;
+    q.saved = fwd_ws;
     q.dxn = dxn;
     q.dW_u = dW_u;
     q.dW_z = dW_z;

@@ -230,6 +230,7 @@ size_t mixer_ws_bytes(int64_t Bt, int64_t L, int64_t Di, int64_t N);
 size_t mixer_bwd_ws_bytes(int64_t Bt, int64_t L, int64_t Di, int64_t N);
 struct MixerGrads {
     const void *d_out;               // [Bt][L][dm] bf16
+    const void *saved;               // workspace of a naju_mixer_fwd call, or null
     float *dxn;                      // [Bt][L][dm]
     float *dW_u, *dW_z;              // [dm][Di]
     float *dconv_w;                  // [Di][4]

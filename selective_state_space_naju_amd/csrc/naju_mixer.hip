@@ -242,7 +242,7 @@ static const char *gemm_wgrad(hipStream_t st, int64_t T, int64_t n, int64_t k, c
 // u, z, h, a, b, y [T][Di] bf16; B, C [T][N] bf16; the GEMM workspace; the
 // block forward's own workspace -- each 256-byte aligned.
 struct MixerPlan {
-    size_t off_u, off_z, off_h, off_a, off_b, off_y, off_B, off_C, off_g, off_f, bytes;
+    size_t off_u, off_z, off_h, off_a, off_b, off_y, off_B, off_C, off_g, off_f, off_ck, bytes;
 };
 
 static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -272,6 +272,8 @@ static MixerPlan mixer_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N)
     o += kGemmWs;
     m.off_f = o;
     o += up256(fwd_ws_bytes(Bt, L, Di, N));
+    m.off_ck = o;  // the scan's checkpoints, kept for a backward that reuses this workspace
+    o += up256(ckpt_bytes(Bt, L, Di, N));
     m.bytes = o;
     return m;
 }
@@ -299,7 +301,7 @@ const char *mixer_fwd(const MixerArgs &g, hipStream_t st)
 {
     const MixerPlan m = mixer_plan(g.Bt, g.L, g.Di, g.N);
     const char *e;
-    if ((e = mixer_forward_pass(g, m, nullptr, st))) return e;
+    if ((e = mixer_forward_pass(g, m, (float *)((char *)g.ws + m.off_ck), st))) return e;
     const int64_t T = g.Bt * g.L;
     return gemm(st, T, g.dm, g.Di, (char *)g.ws + m.off_y, g.W_out, nullptr, g.res, g.out,
                 (char *)g.ws + m.off_g);
@@ -531,7 +533,6 @@ static MixerBwdPlan mixer_bwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N)
         o += up256(bytes);
         return at;
     };
-    m.off_ck = take(ckpt_bytes(Bt, L, Di, N));
     m.off_dy = take(act);
     m.off_dub = take(act);
     m.off_dz = take(act);
@@ -605,10 +606,13 @@ const char *mixer_bwd(const MixerArgs &g, const MixerGrads &d, hipStream_t st)
     const MixerBwdPlan m = mixer_bwd_plan(g.Bt, g.L, g.Di, g.N);
     char *ws = (char *)g.ws;
     const MixerPlan &f = m.f;
-    void *u = ws + f.off_u, *z = ws + f.off_z, *h = ws + f.off_h, *a = ws + f.off_a,
-         *b = ws + f.off_b, *y = ws + f.off_y, *B = ws + f.off_B, *C = ws + f.off_C;
+    // the forward's intermediates: those a naju_mixer_fwd call left in its own
+    // workspace (same inputs), else recomputed into this one
+    char *fw = d.saved ? (char *)d.saved : ws;
+    void *u = fw + f.off_u, *z = fw + f.off_z, *h = fw + f.off_h, *a = fw + f.off_a,
+         *b = fw + f.off_b, *y = fw + f.off_y, *B = fw + f.off_B, *C = fw + f.off_C;
     void *gws = ws + f.off_g;
-    float *ck = (float *)(ws + m.off_ck);
+    float *ck = (float *)(fw + f.off_ck);
     void *dy = ws + m.off_dy, *dub = ws + m.off_dub, *dz = ws + m.off_dz, *da = ws + m.off_da,
          *db = ws + m.off_db, *dB = ws + m.off_dB, *dC = ws + m.off_dC;
     float *dwb = (float *)(ws + m.off_dwb), *dh = (float *)(ws + m.off_dh);
@@ -618,7 +622,7 @@ const char *mixer_bwd(const MixerArgs &g, const MixerGrads &d, hipStream_t st)
     const int64_t T = g.Bt * g.L;
     const bool want_dcs = g.conv_state && d.dconv_state;
     const char *e;
-    if ((e = mixer_forward_pass(g, f, ck, st))) return e;
+    if (!d.saved && (e = mixer_forward_pass(g, f, ck, st))) return e;
     // out = y W_out + res
     if ((e = gemm_nt(st, T, g.Di, g.dm, d.d_out, g.W_out, false, dy, HIP_R_16BF, gws))) return e;
     if ((e = gemm_wgrad(st, T, g.dm, g.Di, y, d.d_out, d.dW_out, gws))) return e;

@@ -164,9 +164,10 @@ def test_validation_errors_mixer_bwd(lib):
                     da_bias=FAKE, dW_b=FAKE, db_bias=FAKE, dW_B=FAKE, dW_C=FAKE, dD=FAKE,
                     dW_out=FAKE)
         for k, v in over.items():
-            if k not in ("ws", "wsb"):
+            if k not in ("ws", "wsb", "fws", "fwsb"):
                 (ins if k in ins else outs)[k] = v
         return lib.naju_mixer_bwd(ctypes.byref(d), dm, *ins.values(), *outs.values(),
+                                  over.get("fws", None), over.get("fwsb", 0),
                                   over.get("ws", FAKE), over.get("wsb", 1 << 40), None)
     d = dims(d_inner=128)
     assert call(d, d_out=None) == nb.EINVAL
@@ -176,6 +177,8 @@ def test_validation_errors_mixer_bwd(lib):
     assert call(d, dxn=FAKE + 4) == nb.EINVAL
     assert call(dims(d_inner=128, io=nb.F32)) == nb.EUNSUPPORTED
     assert call(dims(d_inner=128, batch=0), xn=None) == nb.OK
+    assert call(d, fws=FAKE, fwsb=16) == nb.EWORKSPACE  # a forward workspace too small
+    assert call(d, fws=FAKE + 8, fwsb=1 << 40) == nb.EINVAL
     fwd = lib.naju_mixer_workspace_bytes(ctypes.byref(d), 64)
     assert lib.naju_mixer_bwd_workspace_bytes(ctypes.byref(d), 64) > fwd
 

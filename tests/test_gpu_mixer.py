@@ -7,6 +7,8 @@ and weights.  Tolerance: normwise relative error <= 2e-2 on the bf16 output,
 as for the other bf16 entry points (the device's fp32 accumulation can flip
 a bf16 rounding of an intermediate, which then propagates).
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -106,4 +108,31 @@ def test_mixer_backward_matches_oracle(case):
     names = ["dxn", "dW_u", "dW_z", "dconv_w", "dW_a", "da_bias", "dW_b", "db_bias", "dW_B",
              "dW_C", "dD", "dW_out"] + (["dconv_state"] if cs else [])
     for k in names:
+        assert_close(k, host(got[k]), ref[k], TOL["bf16"])
+
+
+@pytest.mark.parametrize("case", [(2, 200, 64, 128, 16, True), (8, 2048, 64, 128, 16, False)],
+                         ids=lambda c: "b%d_l%d_dm%d_d%d_n%d" % c[:5])
+def test_mixer_backward_reusing_forward_workspace(case):
+    """The backward given the forward call's workspace (no recomputation) matches
+    the oracle like the recomputing one."""
+    Bt, L, dm, Di, N, cs = case
+    print("mixer bwd (saved forward) case Bt=%d L=%d dm=%d Di=%d N=%d cs=%s" % case, flush=True)
+    d = inputs.draw_mixer(Bt, L, dm, Di, N, seed=93, residual=False, conv_state=cs)
+    g = inputs.bf16_round(np.random.default_rng(94).standard_normal((Bt, L, dm)).astype(np.float32))
+    t = {k: (f32_dev(v) if k in FP32_KEYS else to_dev(v, "bf16")) for k, v in d.items()}
+    W = (t["W_u"], t["W_z"], t["conv_w"], t["W_a"], t["a_bias"], t["W_b"], t["b_bias"], t["W_B"],
+         t["W_C"], t["D"], t["W_out"])
+    dims = nb.make_dims(Bt, L, Di, N, nb.BF16)
+    fws = nb.Workspace(int(nb.lib().naju_mixer_workspace_bytes(ctypes.byref(dims), dm)),
+                       t["xn"].device)
+    nb.mixer_fwd(t["xn"], *W, conv_state=t.get("conv_state"), ws=fws)
+    got = nb.mixer_bwd(t["xn"], *W, to_dev(g, "bf16"), conv_state=t.get("conv_state"),
+                       fwd_ws=fws)
+    torch.cuda.synchronize()
+    ref = oracle.mixer_bwd(d["xn"], d["W_u"], d["W_z"], d["conv_w"], d["W_a"], d["a_bias"],
+                           d["W_b"], d["b_bias"], d["W_B"], d["W_C"], d["D"], d["W_out"], g,
+                           conv_state=d.get("conv_state"))
+    for k in ["dxn", "dW_u", "dW_z", "dconv_w", "dW_a", "da_bias", "dW_b", "db_bias", "dW_B",
+              "dW_C", "dD", "dW_out"] + (["dconv_state"] if cs else []):
         assert_close(k, host(got[k]), ref[k], TOL["bf16"])
