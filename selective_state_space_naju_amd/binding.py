@@ -106,6 +106,15 @@ def check(status: int) -> None:
         raise NajuError(status, last_error())
 
 
+def check_workspace(ws) -> None:
+    """Raises if a cross-workgroup wait of a call that used `ws` gave up (its
+    results are then invalid).  Synchronises the workspace's device."""
+    flags = ws.error_flags()
+    if flags:
+        raise NajuError(EHIP, "a cross-workgroup wait gave up (workspace error flags 0x%x): "
+                              "results invalid" % flags)
+
+
 def make_dims(batch, seqlen, d_inner, d_state, io, d_conv=D_CONV) -> Dims:
     return Dims(int(batch), int(seqlen), int(d_inner), int(d_state), int(d_conv), int(io))
 
@@ -188,8 +197,11 @@ def _opt(t, name, shape, dtype, device):
 
 
 # ------------------------------------------------------------------ entry points
-def scan_fwd(h, a, b, B, C, D, x0=None, *, return_ckpt=False, ws=None):
-    """y, x_final (, ckpt) = naju_scan_fwd(h, a, b, B, C, D, x0)."""
+def scan_fwd(h, a, b, B, C, D, x0=None, *, return_ckpt=False, ws=None, check_errors=False):
+    """y, x_final (, ckpt) = naju_scan_fwd(h, a, b, B, C, D, x0).
+
+    check_errors=True synchronises and raises if a look-back wait gave up (the
+    library sets an error bit in the workspace instead of hanging)."""
     Bt, L, Di = h.shape
     N = B.shape[-1]
     dt, dev = h.dtype, h.device
@@ -210,12 +222,15 @@ def scan_fwd(h, a, b, B, C, D, x0=None, *, return_ckpt=False, ws=None):
     check(lib().naju_scan_fwd(ctypes.byref(dims), _p(h), _p(a), _p(b), _p(B), _p(C), _p(D),
                               _p(x0), _p(y), _p(xf), _p(ck), ws.ptr, ws.nbytes,
                               stream_handle(dev)))
+    if check_errors:
+        check_workspace(ws)
     return (y, xf, ck) if return_ckpt else (y, xf)
 
 
 def block_fwd(u, z, conv_w, a, b, B, C, D, x0=None, conv_state=None, *, return_ckpt=False,
-              ws=None):
-    """y, x_final, conv_state_out (, ckpt) = naju_block_fwd(...)."""
+              ws=None, check_errors=False):
+    """y, x_final, conv_state_out (, ckpt) = naju_block_fwd(...) (check_errors: as for
+    scan_fwd)."""
     Bt, L, Di = u.shape
     N = B.shape[-1]
     dt, dev = u.dtype, u.device
@@ -239,6 +254,8 @@ def block_fwd(u, z, conv_w, a, b, B, C, D, x0=None, conv_state=None, *, return_c
     check(lib().naju_block_fwd(ctypes.byref(dims), _p(u), _p(z), _p(conv_w), _p(conv_state),
                                _p(a), _p(b), _p(B), _p(C), _p(D), _p(x0), _p(y), _p(xf),
                                _p(cso), _p(ck), ws.ptr, ws.nbytes, stream_handle(dev)))
+    if check_errors:
+        check_workspace(ws)
     return (y, xf, cso, ck) if return_ckpt else (y, xf, cso)
 
 

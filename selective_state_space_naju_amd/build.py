@@ -3,7 +3,8 @@
     python -m selective_state_space_naju_amd.build [--verbose]
 
 Every HIP source is compiled with packed-fp32 instruction selection turned
-off (``-Xclang -target-feature -Xclang -packed-fp32-ops``).
+off (``-Xclang -target-feature -Xclang -packed-fp32-ops``) and without the
+atomic optimizer's wave aggregation.
 """
 from __future__ import annotations
 
@@ -24,6 +25,9 @@ ARCH = os.environ.get("NAJU_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # single-lane counter atomics stay plain: the wave-aggregating rewrite
+         # reads the result back at once, which would wait out the round trip
+         "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
          "-I" + os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
 
 

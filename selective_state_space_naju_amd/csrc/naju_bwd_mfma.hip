@@ -70,22 +70,29 @@ __device__ __forceinline__ bf16 bits_of(const bf16x8 &v, int s)
 }
 
 // Raw buffer over [p, p + bytes): loads past the end return 0, stores past the
-// end are dropped (the hardware range check of a stride-0 buffer).
+// end are dropped (the hardware range check of a stride-0 buffer, applied to the
+// lane offset).  Every offset that must be range-checked, row offsets included,
+// is passed as the lane offset; the scalar soffset operand is always 0, so
+// nothing depends on whether the check covers it.
 __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
                                              0x00020000);
 }
-// bf16 element at byte offset off + soff (soff wave-uniform; the range check
-// covers the sum)
-__device__ __forceinline__ float ldb(rsrc_t r, uint32_t off, uint32_t soff = 0)
+// bf16 element at byte offset off
+__device__ __forceinline__ float ldb(rsrc_t r, uint32_t off)
 {
-    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, soff, 0) << 16);
+    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0) << 16);
 }
-__device__ __forceinline__ void stb(rsrc_t r, uint32_t off, uint32_t soff, float v)
+__device__ __forceinline__ void stb(rsrc_t r, uint32_t off, float v)
 {
-    __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(v), r, off, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(v), r, off, 0, 0);
 }
+
+// sigma(-v) in (0, 1) is parked as fp16 scaled by 2^15: normal (2^-11 relative)
+// for sigma(-v) >= 2^-29, i.e. v up to about 20; beyond that it underflows
+// gradually towards 0 (a gradient factor below 2e-9 there)
+constexpr float kSigScale = 32768.f, kSigUnscale = 1.f / 32768.f;
 
 // Value held by lane l ^ 32.  v_permlane32_swap exchanges the upper half of
 // its first operand with the lower half of its second; with both operands
@@ -136,7 +143,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
     __shared__ float sR[kTW][16][32];
     // per-token factors consumed once, after the matrix products: sigma(-a) and
     // dy SiLU'(z)  [wave][slot][lane]
-    __shared__ _Float16 sSA[kTW][16][64];  // in (0, 1): fp16 is ample
+    __shared__ _Float16 sSA[kTW][16][64];  // sigma(-a) * kSigScale
     __shared__ float sGZ[BLOCK ? kTW : 1][16][64];
     __shared__ bf16 sUw[BLOCK ? kTW : 1][35][32];  // u: three tokens before the wave, then its 32
     // per-wave transposes for the channel contractions (bf16, padded rows)
@@ -225,10 +232,10 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
         for (int r = 0; r < 4; ++r) vr[r] = valid ? (uint32_t)((4 * hh + r) * Di + col) * 2 : kOOB;
         auto trs = [&](const bf16 *t) -> rsrc_t { return make_rsrc(t + ebase, (uint32_t)Lw * row2); };
         auto LD = [&](const bf16 *t, int i) -> float {
-            return ldb(trs(t), vr[i & 3], (uint32_t)(8 * (i >> 2)) * row2);
+            return ldb(trs(t), vr[i & 3] + (uint32_t)(8 * (i >> 2)) * row2);
         };
         auto ST = [&](bf16 *t, int i, float v) {
-            stb(trs(t), vr[i & 3], (uint32_t)(8 * (i >> 2)) * row2, v);
+            stb(trs(t), vr[i & 3] + (uint32_t)(8 * (i >> 2)) * row2, v);
         };
 
         // ------------------------------------------------------- phase A
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                 float dv = LD(dy, i);
                 const float e = tval(i) ? ex2(-av * kLog2e) : 0.f;
                 invf[i] = 1.f + e;
-                sSA[tw][i][lane] = (_Float16)(e * rcp(invf[i]));  // sigma(-a)
+                sSA[tw][i][lane] = (_Float16)(e * rcp(invf[i]) * kSigScale);  // sigma(-a)
                 if (BLOCK) {
                     const float zv = LD(z, i);
                     const float ez = ex2(-zv * kLog2e);
@@ -317,7 +324,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 sUw[tw][3 + tok(i)][col] = (bf16)__builtin_amdgcn_raw_buffer_load_b16(
-                    ru, vr[i & 3], (uint32_t)(8 * (i >> 2)) * row2, 0);
+                    ru, vr[i & 3] + (uint32_t)(8 * (i >> 2)) * row2, 0, 0);
             if (!upper) {
 #pragma unroll
                 for (int k = 0; k < 3; ++k)
@@ -326,10 +333,10 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
             }
         };
         float h[16], ib[16];
-        // SiLU'(pre) in [-0.1, 1.1], kept as fp16 pairs (2^-11 relative) to save registers
         typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+        // SiLU'(pre) in [-0.1, 1.1], kept as fp16 pairs (2^-11 relative) to save registers
         half2_t hd2[8];
-        bf16x8 WB[2];
+        bf16x8 WB[2], WBl[2];  // W' as bf16 hi + lo parts
         {
             float uv[16], bv[16];
             // every load issued before any is used (one round trip, not one per token)
@@ -362,7 +369,10 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                     h[i] = hv;
                     const float wp = ib[i] * hv * invP[i];
                     ok = ok && (__builtin_fabsf(wp) < 1e30f);
-                    WB[i >> 3][i & 7] = (__bf16)wp;
+                    __bf16 whi, wlo;
+                    split2(wp, whi, wlo);
+                    WB[i >> 3][i & 7] = whi;
+                    WBl[i >> 3][i & 7] = wlo;
                 }
             }
 #pragma unroll
@@ -464,32 +474,56 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                     ML[k] = l2;
                 }
                 const bf16x8 Bop = rows(sBr), Csc = rows(sCr);
-                // tril(G) and its transpose as A operands (C pre-scaled, so G = Csc.B)
-                bf16x8 GA[2], GTA[2];
+                // tril(G) and its transpose as A operands (C pre-scaled, so G =
+                // Csc.B), each in bf16 hi + lo parts: the gate gradient is a prefix
+                // sum of products whose difference it takes, so their rounding must
+                // stay near fp32.  One at a time, to keep the registers low.
                 {
+                    bf16x8 GA[2], GAl[2];
                     const f32x16 g1 = mma(Bop, Csc, zero);  // g1[i] = G[col][tok(i)]
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        __bf16 hi, lo;
+                        split2((tok(i) <= col) ? g1[i] : 0.f, hi, lo);
+                        GA[i >> 3][i & 7] = hi;
+                        GAl[i >> 3][i & 7] = lo;
+                    }
+                    Z = mma(Csc, XH, zero);
+                    Z = mma(Csc, XL, Z);
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        Z = mma(GA[kb], WB[kb], Z);
+                        Z = mma(GA[kb], WBl[kb], Z);
+                        Z = mma(GAl[kb], WB[kb], Z);
+                    }
+                }
+                {
+                    bf16x8 GTA[2], GTAl[2];
                     const f32x16 g2 = mma(Csc, Bop, zero);  // g2[i] = G[tok(i)][col]
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        GA[i >> 3][i & 7] = (__bf16)((tok(i) <= col) ? g1[i] : 0.f);
-                        GTA[i >> 3][i & 7] = (__bf16)((tok(i) >= col) ? g2[i] : 0.f);
+                        __bf16 hi, lo;
+                        split2((tok(i) >= col) ? g2[i] : 0.f, hi, lo);
+                        GTA[i >> 3][i & 7] = hi;
+                        GTAl[i >> 3][i & 7] = lo;
                     }
-                }
-                PU = mma(Bop, MH, zero);
-                PU = mma(Bop, ML, PU);
-                Z = mma(Csc, XH, zero);
-                Z = mma(Csc, XL, Z);
+                    PU = mma(Bop, MH, zero);
+                    PU = mma(Bop, ML, PU);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    Z = mma(GA[kb], WB[kb], Z);
-                    PU = mma(GTA[kb], GpH[kb], PU);
-                    PU = mma(GTA[kb], GpL[kb], PU);
+                    for (int kb = 0; kb < 2; ++kb) {
+                        PU = mma(GTA[kb], GpH[kb], PU);
+                        PU = mma(GTA[kb], GpL[kb], PU);
+                        PU = mma(GTAl[kb], GpH[kb], PU);
+                    }
                 }
             }
 
             // per 4-token group q: outputs, the exclusive prefix for da, the conv
             // transpose (the upper half finishes its previous group once the
             // partner's first three dpre of this group arrive) and dconv_w partials
+            float bq[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) bq[i] = LD(bg, i);
             float dDp = 0.f, dwa0 = 0.f, dwa1 = 0.f, dwa2 = 0.f, dwa3 = 0.f;
             float base = 0.f;              // prefix of ph over the groups before
             float dprev[4] = {0.f, 0.f, 0.f, 0.f};  // upper half: previous group's dpre
@@ -503,7 +537,11 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                     const float dw = invP[i] * PU[i];
                     const float ysd = rcp(invP[i]) * Z[i];
                     ph[r] = fmaf(g[i], ysd, -ib[i] * h[i] * dw);
-                    ST(db, i, dw * h[i] * ib[i] * (1.f - ib[i]));
+                    // sigma(-b) = e^{-b} sigma(b) from b, read again (an L2 hit): not as
+                    // 1 - sigma(b), which cancels for large b
+                    const float eb = ex2(-bq[i] * kLog2e);
+                    const float sbm = eb < __builtin_huge_valf() ? eb * ib[i] : 1.f;
+                    ST(db, i, dw * h[i] * ib[i] * sbm);
                     const float dh = fmaf(dw, ib[i], Dc * g[i]);
                     dDp = fmaf(g[i], h[i], dDp);
                     if (BLOCK) {
@@ -520,7 +558,7 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int i = 4 * q + r;
-                        ST(da, i, (float)sSA[tw][i][lane] * (phi0 - run));
+                        ST(da, i, (float)sSA[tw][i][lane] * kSigUnscale * (phi0 - run));
                         run += ph[r];
                     }
                     base += sq + ps;
@@ -703,7 +741,8 @@ __global__ __launch_bounds__(64 * kTW) void bwd_carry_kernel(
     // the two channels of slot i as one 4-byte load
     auto LD2 = [&](const bf16 *t, int i) -> uint32_t {
         return __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(t + ebase, (uint32_t)Lw * row2),
-                                                    vr[i & 3], (uint32_t)(8 * (i >> 2)) * row2, 0);
+                                                    vr[i & 3] + (uint32_t)(8 * (i >> 2)) * row2,
+                                                    0, 0);
     };
     float invf[2][16], g[2][16];
 #pragma unroll

@@ -99,7 +99,9 @@ struct WsHeader {
     uint32_t error;   // bit 0: a bounded spin gave up
     uint32_t ticket2; // second ticket counter (multi-kernel calls)
     uint32_t done2;
-    uint32_t pad[58];
+    uint32_t pad[10];     // pad[0]: count of the backward's fix-up list
+    uint32_t queue[8];    // per-XCD ticket counters of the matrix-core forward
+    uint32_t pad2[40];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 

@@ -246,8 +246,8 @@ __global__ __launch_bounds__(64 * kWv, 1) void fwd_mfma64_kernel(
         const uint32_t vc = (uint32_t)((lane & 31) * N + 8 * (lane >> 5)) * 2;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-            cv[kb] = __builtin_bit_cast(bf16x8,
-                                        __builtin_amdgcn_raw_buffer_load_b128(rc, vc, 32 * kb, 0));
+            cv[kb] = __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rc, vc + 32 * kb, 0, 0));
     };
 
     // workgroup w takes rows w, w + G, w + 2G, ...
@@ -513,13 +513,16 @@ __global__ __launch_bounds__(64 * kWv, 1) void fwd_mfma64_kernel(
         if (ckpt && active) {
             float *cp = ckpt + (((int64_t)bi * n_waves + (int64_t)chunk * 4 + tbw) * N) * Di + cbase + kCW * chh;
             const rsrc_t rc = make_rsrc(cp, (uint32_t)(N * Di * 4));
+            // every offset in the lane's voffset: a buffer's range check does not
+            // cover the scalar soffset operand, so nothing may rely on it
             const uint32_t vo = c_col < Di ? (uint32_t)((8 * hh) * Di + col) * 4 : kOOB;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xs[kb][e]), rc, vo,
-                                                          (uint32_t)((16 * kb + e) * Di) * 4, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        __float_as_uint(xs[kb][e]), rc,
+                        c_col < Di ? vo + (uint32_t)((16 * kb + e) * Di) * 4 : kOOB, 0, 0);
         }
 
         if (!wave_ok) {
@@ -560,8 +563,8 @@ __global__ __launch_bounds__(64 * kWv, 1) void fwd_mfma64_kernel(
                     const uint32_t vo = vc ? (uint32_t)((4 * hh + r) * Di + kCW * chh + col) * 2 : kOOB;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        zb[4 * q + r] =
-                            __builtin_amdgcn_raw_buffer_load_b16(rz, vo, (uint32_t)(8 * q) * row2, 0);
+                        zb[4 * q + r] = __builtin_amdgcn_raw_buffer_load_b16(
+                            rz, vo + (uint32_t)(8 * q) * row2, 0, 0);
                 }
             }
 #pragma unroll
@@ -570,14 +573,16 @@ __global__ __launch_bounds__(64 * kWv, 1) void fwd_mfma64_kernel(
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int i = 4 * q + r;
-                    const uint32_t so = (uint32_t)(8 * q) * row2;
+                    // the row offset joins the lane offset (the range, Lw rows, then
+                    // drops rows past the wave's last token; kOOB drops channels past Di)
+                    const uint32_t off = vo + (uint32_t)(8 * q) * row2;
                     float yv = Pv[i] * Y[i];
                     if (BLOCK) {
                         const float zv = __uint_as_float(zb[i] << 16);
                         yv *= zv * sigm(zv);
                     }
                     // (no nontemporal hint: L2 merges the 64-byte pieces into whole lines)
-                    __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(yv), ry, vo, so, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(yv), ry, off, 0, 0);
                 }
             }
         }

@@ -22,6 +22,45 @@ constexpr int kBwdTB = 8;  // tokens recomputed per sub-block
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Unsigned division of n < 2^31 by a fixed d >= 1 without a divide: with
+// l = ceil(log2 d) and m = floor(2^32 (2^l - d) / d) + 1, n / d =
+// (mulhi(n, m) + n) >> l (the round-up multiplier method of Granlund and
+// Montgomery, in its 32-bit "add" form).  Kernels take the pair from the host,
+// so a uniform division is a scalar multiply-high, an add and a shift.
+struct FastDiv {
+    uint32_t d, m, l;
+};
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t l = 0;
+    while (l < 32 && (1ull << l) < d) ++l;
+    const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    return FastDiv{d, (uint32_t)m, l};
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f)
+{
+    return (__umulhi(n, f.m) + n) >> f.l;
+}
+
+// Ticket queues of a persistent kernel, one per XCD: rows r (batch row x
+// channel tile) with r % 8 == q form queue q, served chunk-major, so all chunks
+// of a row -- a look-back chain -- run on one XCD.  rows[q] is the queue's row
+// count (its FastDiv), total[q] its ticket count.
+struct TicketQueues {
+    FastDiv rows[8];
+    uint32_t total[8];
+};
+inline TicketQueues make_ticket_queues(uint32_t per_chunk, uint32_t n_chunks)
+{
+    TicketQueues t{};
+    for (uint32_t q = 0; q < 8; ++q) {
+        const uint32_t r = per_chunk > q ? (per_chunk - q + 7) / 8 : 0;
+        t.rows[q] = make_fastdiv(r > 0 ? r : 1);
+        t.total[q] = r * n_chunks;
+    }
+    return t;
+}
+
 struct FwdPlan {
     int n_tiles;      // channel tiles of 64/LPC channels
     int n_chunks;     // workgroup chunks of kFwdT*kFwdW tokens
@@ -38,10 +77,11 @@ inline FwdPlan fwd_plan(int64_t Bt, int64_t L, int64_t Di, int64_t N, int W = kF
     p.n_chunks = (int)((L + kFwdT * W - 1) / (kFwdT * W));
     p.n_wg = Bt * p.n_tiles * p.n_chunks;
     p.n_waves = (L + kFwdT - 1) / kFwdT;
-    // the matrix-core forward looks back in two state groups of eight: two
-    // (P, S[8]) aggregates and two x_out[8] per workgroup chunk, each value a
-    // tagged 64-bit word; the register forward uses flags and fp32 payloads
-    const size_t fl = W == kMfmaW ? 2 : 1, ar = W == kMfmaW ? 18 : 17;
+    // the matrix-core forwards look back in state groups (four of four: four
+    // (P, S[4]) aggregates and four x_out[4] per workgroup chunk; or two of
+    // eight), each value a tagged 64-bit word; the register forward uses flags
+    // and fp32 payloads
+    const size_t fl = W == kMfmaW ? 2 : 1, ar = W == kMfmaW ? 20 : 17;
     const size_t vb = W == kMfmaW ? 8 : 4;  // bytes per published value
     p.off_flags = 256;
     p.off_agg = align256(p.off_flags + 4 * fl * (size_t)p.n_wg);

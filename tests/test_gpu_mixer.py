@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import TOL, assert_close, f32_dev, host, to_dev
+from gpu_helpers import TOL, assert_agree, assert_close, f32_dev, host, to_dev
 from selective_state_space_naju_amd import binding as nb
 from selective_state_space_naju_amd import inputs
 
@@ -40,6 +40,7 @@ CASES = [
     (3, 17, 40, 72, 16, False, False),     # one partial conv segment, d_inner not a multiple of 64
     (2, 50, 16, 8, 64, False, True),       # the smallest d_inner, register form of the scan
     (8, 2048, 64, 128, 16, False, False),  # the training batch shape (16384 tokens), narrow layer
+    (2, 256, 768, 1536, 16, True, True),   # the benchmarked layer width, fewer tokens
 ]
 
 FP32_KEYS = ("conv_w", "D", "a_bias", "b_bias")
@@ -79,7 +80,10 @@ def test_mixer_repeat_calls_are_identical():
             t["b_bias"], t["W_B"], t["W_C"], t["D"], t["W_out"])
     o1 = host(nb.mixer_fwd(*args, res=t["res"]))
     o2 = host(nb.mixer_fwd(*args, res=t["res"]))
-    assert_close("repeat", o2, o1, 1e-2)
+    # the GEMMs repeat exactly; a look-back that folds a predecessor's aggregate
+    # instead of taking its inclusive state changes only the fp32 rounding of the
+    # block forward, so an output moves by at most a bf16 rounding flip or two
+    assert_agree("repeat", o2, o1, ulps=2.0)
 
 
 BWD_CASES = [
@@ -88,6 +92,13 @@ BWD_CASES = [
     (1, 333, 96, 64, 64, True),
     (2, 130, 32, 256, 16, True),
     (8, 2048, 64, 128, 16, False),  # the training batch shape (16384 tokens), narrow layer
+    # the benchmarked layer width, fewer tokens: within the normwise bound (3.3e-3 of
+    # 2e-2), but dW_u exceeds the elementwise bound by 1.2x at one element -- the
+    # block backward's dB / dC carry single-bf16 operands in their channel products
+    # (relative L2 error 3e-3, twice the bf16 rounding floor), which the layer's dh
+    # = dB W_B^T + dC W_C^T spreads over every channel of a token
+    pytest.param((2, 256, 768, 1536, 16, True), marks=pytest.mark.xfail(
+        strict=True, reason="dB/dC precision of the block backward (single-bf16 operands)")),
 ]
 
 

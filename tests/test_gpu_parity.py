@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import TOL, assert_close, dev, f32_dev, host, to_dev
+from gpu_helpers import TOL, assert_agree, assert_close, dev, f32_dev, host, to_dev
 from selective_state_space_naju_amd import binding as nb
 from selective_state_space_naju_amd import inputs
 
@@ -220,9 +220,13 @@ def test_repeat_runs_agree_and_workspace_clean():
             for _ in range(3)]
     torch.cuda.synchronize()
     assert ws.error_flags() == 0
+    # Repeats may fold a look-back predecessor's aggregate where another run found
+    # its inclusive state, which only changes the fp32 rounding: x_final agrees to
+    # 1e-6 of its size, and a bf16 output at most by a rounding flip (1 ulp).
+    y0, x0f = host(outs[0][0]), host(outs[0][1])
     for y, xf in outs[1:]:
-        assert (y.float() - outs[0][0].float()).abs().max().item() <= 1e-2 * outs[0][0].float().abs().max().item()
-        assert torch.allclose(xf, outs[0][1], rtol=1e-5, atol=1e-5)
+        assert_agree("y(repeat)", host(y), y0)
+        assert np.abs(host(xf) - x0f).max() <= 1e-6 * np.abs(x0f).max()
 
 
 @pytest.mark.parametrize("block", [False, True], ids=["scan", "block"])
