@@ -289,6 +289,26 @@ naju_status_t naju_mixer_bwd(const naju_dims_t *dims, int64_t d_model, const voi
                              float *dW_out, const void *fwd_ws, size_t fwd_ws_bytes, void *ws,
                              size_t ws_bytes, void *stream);
 
+/*
+ * Scan forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, outputs and results as
+ * naju_scan_fwd; it allocates nothing, neither itself nor through a library.
+ * Its scratch is a 64 MiB device array inside the library, one per GPU, zero
+ * at load and held until the process ends; shapes whose forward workspace
+ * (naju_workspace_bytes(NAJU_OP_SCAN_FWD, dims)) exceeds it return
+ * NAJU_EWORKSPACE before anything is enqueued.  Every call on a GPU shares that
+ * GPU's scratch: calls that overlap on one GPU (different streams, or host
+ * threads) race and must not be issued.
+ *   flags  device uint32 or NULL: receives the call's error word (0: every
+ *          cross-workgroup wait completed; nonzero: one gave up and the
+ *          results are invalid), which the call then clears in the scratch
+ */
+naju_status_t naju_scan_fwd_noalloc(const naju_dims_t *dims, const void *h, const void *a,
+                                    const void *b, const void *B, const void *C, const float *D,
+                                    const float *x0, void *y, float *x_final, float *ckpt,
+                                    uint32_t *flags, void *stream);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char *naju_last_error(void);
 

@@ -27,8 +27,8 @@ D_CONV = 4
 EXPORTS = ("naju_workspace_bytes", "naju_ckpt_bytes", "naju_workspace_init",
            "naju_workspace_check", "naju_scan_fwd", "naju_scan_bwd", "naju_block_fwd",
            "naju_block_bwd", "naju_scan_step", "naju_block_step", "naju_mixer_workspace_bytes",
-           "naju_mixer_fwd", "naju_mixer_bwd_workspace_bytes", "naju_mixer_bwd", "naju_last_error",
-           "naju_version")
+           "naju_mixer_fwd", "naju_mixer_bwd_workspace_bytes", "naju_mixer_bwd",
+           "naju_scan_fwd_noalloc", "naju_last_error", "naju_version")
 
 
 class NajuError(RuntimeError):
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.naju_mixer_bwd_workspace_bytes.restype = sz
         L.naju_mixer_bwd.argtypes = [dp, ctypes.c_int64] + [vp] * 28 + [sz, vp, sz, vp]
         L.naju_mixer_bwd.restype = st
+        L.naju_scan_fwd_noalloc.argtypes = [dp] + [vp] * 12
+        L.naju_scan_fwd_noalloc.restype = st
         L.naju_last_error.argtypes = []
         L.naju_last_error.restype = ctypes.c_char_p
         L.naju_version.argtypes = []

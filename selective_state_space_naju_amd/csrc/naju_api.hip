@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/naju.h"
 #include "naju_device.h"
 #include "naju_launch.h"
@@ -407,11 +409,73 @@ static naju_status_t mixer_common(const naju_dims_t *d, int64_t dm, const void *
     return NAJU_OK;
 }
 
+// ---------------------------------------------- allocation-free scan forward
+// A device-resident scratch array serves as the workspace of
+// naju_scan_fwd_noalloc: zero at load (so, like a zero-filled caller workspace,
+// it needs no initialisation), epoch-tagged words and self-resetting counters
+// keep it reusable across calls of any shape.  Each GPU holds its own copy of
+// the array, at its own address, until the process ends.  In host code the
+// array's name is not a device address: the kernels take the address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+// the error word read back (and cleared) after a call, for the caller
+__global__ void scratch_flags_kernel(WsHeader *hdr, uint32_t *flags)
+{
+    *flags = hdr->error;
+    hdr->error = 0u;
+}
+
+static naju_status_t scratch_address(void **out)
+{
+    static std::mutex mu;
+    static void *addr[64] = {};
+    int dev = 0;
+    TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+    if (dev < 0 || dev >= 64) return fail(NAJU_EUNSUPPORTED, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        // (once per device, with that device current)
+        TRY(hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress"));
+        if (!p) return fail(NAJU_EHIP, "hipGetSymbolAddress returned NULL");
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return NAJU_OK;
+}
+
 }  // namespace naju
 
 using namespace naju;
 
 extern "C" {
+
+naju_status_t naju_scan_fwd_noalloc(const naju_dims_t *dims, const void *h, const void *a,
+                                    const void *b, const void *B, const void *C, const float *D,
+                                    const float *x0, void *y, float *x_final, float *ckpt,
+                                    uint32_t *flags, void *stream)
+{
+    TRY(check_dims(dims, false));
+    const size_t need_b = ws_bytes_for(NAJU_OP_SCAN_FWD, dims);
+    if (need_b > kScratchBytes)
+        return fail(NAJU_EWORKSPACE,
+                    "naju_scan_fwd_noalloc: this shape needs %zu bytes of scratch, more than "
+                    "the library's %zu; use naju_scan_fwd with a workspace",
+                    need_b, kScratchBytes);
+    TRY(opt(flags, "flags", 4));
+    void *ws = nullptr;
+    TRY(scratch_address(&ws));
+    TRY(fwd_common(false, dims, h, nullptr, nullptr, nullptr, a, b, B, C, D, x0, y, x_final,
+                   nullptr, ckpt, ws, kScratchBytes, stream));
+    if (flags) {
+        hipLaunchKernelGGL(scratch_flags_kernel, dim3(1), dim3(1), 0, (hipStream_t)stream,
+                           (WsHeader *)ws, flags);
+        TRY(hip_status(hipGetLastError(), "scratch flags launch"));
+    }
+    return NAJU_OK;
+}
 
 size_t naju_workspace_bytes(naju_op_t op, const naju_dims_t *dims)
 {

@@ -199,3 +199,16 @@ def test_binding_requires_library_file(monkeypatch, tmp_path):
     monkeypatch.setattr(nb, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         nb.lib()
+
+
+def test_validation_errors_scan_fwd_noalloc(lib):
+    """Rejected before anything is enqueued: bad dims, and a shape whose forward
+    workspace exceeds the library's scratch (no GPU is touched)."""
+    bad = nb.make_dims(1, 16, 64, 17, nb.BF16)
+    st = lib.naju_scan_fwd_noalloc(ctypes.byref(bad), *([ctypes.c_void_p(256)] * 10), None, None)
+    assert st != nb.OK
+    big = nb.make_dims(64, 65536, 4096, 16, nb.BF16)
+    assert nb.workspace_bytes(nb.OP_SCAN_FWD, big) > (64 << 20)
+    st = lib.naju_scan_fwd_noalloc(ctypes.byref(big), *([ctypes.c_void_p(256)] * 10), None, None)
+    assert st == nb.EWORKSPACE
+    assert b"scratch" in lib.naju_last_error()
