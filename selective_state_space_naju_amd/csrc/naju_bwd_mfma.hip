@@ -72,8 +72,9 @@ __device__ __forceinline__ bf16 bits_of(const bf16x8 &v, int s)
 // Raw buffer over [p, p + bytes): loads past the end return 0, stores past the
 // end are dropped (the hardware range check of a stride-0 buffer, applied to the
 // lane offset).  Every offset that must be range-checked, row offsets included,
-// is passed as the lane offset; the scalar soffset operand is always 0, so
-// nothing depends on whether the check covers it.
+// is passed as the lane offset; a nonzero scalar soffset carries only offsets
+// that stay in range for every lane that is not already out of range by its
+// lane offset alone, so nothing depends on whether the check covers it.
 __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
@@ -117,7 +118,10 @@ __device__ __forceinline__ void pair_of(uint32_t b, uint32_t &p, int &h)
 }  // namespace
 
 template <bool BLOCK>
-__global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
+#ifndef NAJU_BWD_MINB
+#define NAJU_BWD_MINB 2
+#endif
+__global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
     const int64_t Bt, const int64_t L, const int64_t Di, const int n_tiles, const int n_sub,
     const int n_super, const int n_chunks, const int64_t n_waves, const float scale,
     const bf16 *__restrict__ hu, const bf16 *__restrict__ a, const bf16 *__restrict__ bg,
@@ -192,7 +196,11 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
     }
 
     f32x16 dBC = {};  // dB (columns 0..15) | dC / scale (columns 16..31) of this wave's tokens
-    for (int st = 0; st < n_sub && tile_of(st) < n_tiles; ++st) {
+    // The tile's work in two forms (the same barriers in the same order): FULL
+    // for a wave of 32 valid tokens, and the ragged form for the last wave of a
+    // sequence (see the element access below).
+    auto tile_body = [&](const int st, auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
         // lane-derived values are re-derived every tile: kept out of loop-invariant
         // code motion, which would pin dozens of them (masks, offsets) in registers
         // across the whole loop
@@ -223,19 +231,37 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
         const bool valid = c < Di;
         const int64_t ebase = (tokbase + (active ? n0 : 0)) * Di + (int64_t)tile * 32;
         // Element access of every [Bt][L][Di] tensor: slot i = 4q + r is token
-        // 8q + 4h + r.  One buffer per tensor, ending at the wave's last valid
-        // token; the lane offset of row 4h + r plus the wave-uniform offset of
-        // group q's first row.
+        // 8q + 4h + r, at lane offset vr[r] (row 4h + r) plus group q's row offset.
+        // A full wave passes the group offset as the wave-uniform soffset: every
+        // row is in range, and the lanes of channels past Di carry kOOB, past the
+        // range with or without it.  The ragged wave uses one buffer per tensor
+        // and group, starting at the group's first row and ending at the wave's
+        // last valid token, so the range check sees the whole offset.
         const uint32_t row2 = (uint32_t)Di * 2;
         uint32_t vr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) vr[r] = valid ? (uint32_t)((4 * hh + r) * Di + col) * 2 : kOOB;
         auto trs = [&](const bf16 *t) -> rsrc_t { return make_rsrc(t + ebase, (uint32_t)Lw * row2); };
+        auto trq = [&](const bf16 *t, int q) -> rsrc_t {
+            const int left = Lw - 8 * q;  // valid rows from the group's first
+            return make_rsrc(t + ebase + (int64_t)(8 * q) * Di, left > 0 ? (uint32_t)left * row2 : 0u);
+        };
+        auto LD16 = [&](const bf16 *t, int i) -> uint16_t {
+            if constexpr (FULL)
+                return __builtin_amdgcn_raw_buffer_load_b16(trs(t), vr[i & 3],
+                                                            (uint32_t)(8 * (i >> 2)) * row2, 0);
+            else
+                return __builtin_amdgcn_raw_buffer_load_b16(trq(t, i >> 2), vr[i & 3], 0, 0);
+        };
         auto LD = [&](const bf16 *t, int i) -> float {
-            return ldb(trs(t), vr[i & 3] + (uint32_t)(8 * (i >> 2)) * row2);
+            return __uint_as_float((uint32_t)LD16(t, i) << 16);
         };
         auto ST = [&](bf16 *t, int i, float v) {
-            stb(trs(t), vr[i & 3] + (uint32_t)(8 * (i >> 2)) * row2, v);
+            if constexpr (FULL)
+                __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(v), trs(t), vr[i & 3],
+                                                      (uint32_t)(8 * (i >> 2)) * row2, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(v), trq(t, i >> 2), vr[i & 3], 0, 0);
         };
 
         // ------------------------------------------------------- phase A
@@ -320,11 +346,8 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                                                : (const void *)a,
                                         pbytes);
             const uint32_t po = valid ? (uint32_t)col * 2 : kOOB;
-            const rsrc_t ru = trs(hu);
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                sUw[tw][3 + tok(i)][col] = (bf16)__builtin_amdgcn_raw_buffer_load_b16(
-                    ru, vr[i & 3] + (uint32_t)(8 * (i >> 2)) * row2, 0, 0);
+            for (int i = 0; i < 16; ++i) sUw[tw][3 + tok(i)][col] = (bf16)LD16(hu, i);
             if (!upper) {
 #pragma unroll
                 for (int k = 0; k < 3; ++k)
@@ -332,13 +355,18 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                         rp, po + (uint32_t)(k * Di) * 2, 0, 0);
             }
         };
-        float h[16], ib[16];
-        typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-        // SiLU'(pre) in [-0.1, 1.1], kept as fp16 pairs (2^-11 relative) to save registers
-        half2_t hd2[8];
-        bf16x8 WB[2], WBl[2];  // W' as bf16 hi + lo parts
+        // h = SiLU(pre) of the block and its derivative, from the u window in LDS
+        auto silu_at = [&](int q, int r, float &hd) -> float {
+            const float pre = cw0 * win(q, r) + cw1 * win(q, r + 1) + cw2 * win(q, r + 2) +
+                              cw3 * win(q, r + 3);
+            const float sp = rcp(1.f + ex2(-pre * kLog2e));
+            hd = sp * fmaf(pre, 1.f - sp, 1.f);  // SiLU'(pre); 1 - sp enters only as pre (1 - sp)
+            return pre * sp;
+        };
+        float h[16], hdk[BLOCK ? 16 : 1];  // h and (block) SiLU'(pre)
+        bf16x8 WB[2], WBl[2];     // W' as bf16 hi + lo parts
         {
-            float uv[16], bv[16];
+            float uv[16], bv[16], ib[16];
             // every load issued before any is used (one round trip, not one per token)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -354,18 +382,10 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                 for (int r = 0; r < 4; ++r) {
                     const int i = 4 * q + r;
                     float hv;
-                    if (BLOCK) {
-                        const float pre = cw0 * win(q, r) + cw1 * win(q, r + 1) +
-                                          cw2 * win(q, r + 2) + cw3 * win(q, r + 3);
-                        const float ep_ = ex2(-pre * kLog2e);
-                        const float sp = rcp(1.f + ep_);
-                        const float sm = 1.f - sp;  // sigma(-pre), used as pre sigma(-pre)
-                        hv = pre * sp;
-                        hd2[i >> 1][i & 1] = (_Float16)(sp * fmaf(pre, sm, 1.f));  // SiLU'(pre)
-                    } else {
+                    if constexpr (BLOCK)
+                        hv = silu_at(q, r, hdk[i]);
+                    else
                         hv = uv[i];
-                        hd2[i >> 1][i & 1] = (_Float16)0.f;
-                    }
                     h[i] = hv;
                     const float wp = ib[i] * hv * invP[i];
                     ok = ok && (__builtin_fabsf(wp) < 1e30f);
@@ -536,17 +556,20 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
                     const int i = 4 * q + r;
                     const float dw = invP[i] * PU[i];
                     const float ysd = rcp(invP[i]) * Z[i];
-                    ph[r] = fmaf(g[i], ysd, -ib[i] * h[i] * dw);
-                    // sigma(-b) = e^{-b} sigma(b) from b, read again (an L2 hit): not as
-                    // 1 - sigma(b), which cancels for large b
+                    // sigma(b) and sigma(-b) = e^{-b} sigma(b) from b, read again (an L2
+                    // hit; sigma(b) comes out as in the first phase, and sigma(-b) is not
+                    // taken as 1 - sigma(b), which cancels for large b)
                     const float eb = ex2(-bq[i] * kLog2e);
-                    const float sbm = eb < __builtin_huge_valf() ? eb * ib[i] : 1.f;
-                    ST(db, i, dw * h[i] * ib[i] * sbm);
-                    const float dh = fmaf(dw, ib[i], Dc * g[i]);
-                    dDp = fmaf(g[i], h[i], dDp);
+                    const float ibv = rcp(1.f + eb);
+                    const float sbm = eb < __builtin_huge_valf() ? eb * ibv : 1.f;
+                    const float hv = h[i];
+                    ph[r] = fmaf(g[i], ysd, -ibv * hv * dw);
+                    ST(db, i, dw * hv * ibv * sbm);
+                    const float dh = fmaf(dw, ibv, Dc * g[i]);
+                    dDp = fmaf(g[i], hv, dDp);
                     if (BLOCK) {
-                        ST(dz, i, sGZ[tw][i][lane] * fmaf(Dc, h[i], ysd));
-                        dp[r] = dh * (float)hd2[i >> 1][i & 1];
+                        ST(dz, i, sGZ[tw][i][lane] * fmaf(Dc, hv, ysd));
+                        dp[r] = dh * hdk[i];
                     } else {
                         ST(dhu, i, dh);
                     }
@@ -673,6 +696,12 @@ __global__ __launch_bounds__(64 * kTW, 2) void bwd_mfma_kernel(
             }
         }
         __syncthreads();  // sQ, sR, sMu are rewritten by the next tile
+    };
+    for (int st = 0; st < n_sub && tile_of(st) < n_tiles; ++st) {
+        if (Lw == T)
+            tile_body(st, std::true_type{});
+        else
+            tile_body(st, std::false_type{});
     }
 
     // ------------------------- dB/dC partial of this super-tile, per token
