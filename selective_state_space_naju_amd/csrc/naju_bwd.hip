@@ -467,8 +467,15 @@ __device__ __forceinline__ void bc_reduce_block(int blk, const int64_t rows, con
     const int64_t row = i / N2;
     const int s = (int)(i % N2);
     const float *p = part + row * (int64_t)n_tiles * N2 + s;
+    // eight partials in flight at a time, added in tile order (missing ones add 0)
     float acc = 0.f;
-    for (int t = 0; t < n_tiles; ++t) acc += p[(int64_t)t * N2];
+    for (int t0 = 0; t0 < n_tiles; t0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = t0 + k < n_tiles ? p[(int64_t)(t0 + k) * N2] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc += v[k];
+    }
     const int N = N2 / 2;
     if (s < N)
         dB[row * N + s] = from_f<IO>(acc);
