@@ -15,8 +15,9 @@ stream; median, mean, p10 and p90 over at least 50 launches):
   shape, and the one-token decode step at its batch and width;
 * every other workload of the hot path: the fp32 1 x 256 x 192 scan, the
   4 x 8192 x 4096 d_state-64 scan (one call, and the same sequence as 4 chained
-  calls of 2048 tokens carrying the state), the 1 x 65536 x 2048 long scan, and
-  the mixer layer around the scan (8 x 2048, d_model 768, d_inner 1536);
+  calls of 2048 tokens carrying the state), the 1 x 65536 x 2048 long scan, the
+  step's scan shape with forgetful gates (every chunk on the register fallback),
+  and the mixer layer around the scan (8 x 2048, d_model 768, d_inner 1536);
 * the CPU oracle (the cpu_baseline leg) on a bounded sample of each workload,
   on the host's cores and, for the fp32 1 x 256 x 192 scan, on one thread.
 
@@ -48,7 +49,7 @@ WORKLOAD = "train_bf16_b8_l2048_d1536_n16"
 MIXER = "mixer_bf16_b8_l2048_dm768_d1536_n16"
 # the other workloads of the hot path, timed as parts of the default run
 SCAN_PARTS = ("scan_f32_b1_l256_d192_n16", "scan_bf16_b4_l8192_d4096_n64",
-              "scan_bf16_b1_l65536_d2048_n16")
+              "scan_bf16_b1_l65536_d2048_n16", "scan_bf16_b8_l2048_d1536_n16_forget")
 NSETS = 3
 MIN_LAUNCHES = 50
 

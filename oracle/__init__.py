@@ -4,10 +4,13 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product path never does, and this
 package imports nothing from the product package.
 
-The arithmetic lives in ``naju_oracle.c`` (plain C, fp64, sequential time
-loops); this module only builds it with gcc, marshals numpy arrays and
-returns numpy arrays.  Definitions followed (reproduction README of arXiv
-2607.21000, "Core equations" and the block flowchart):
+The scan and block arithmetic lives in ``naju_oracle.c`` (plain C, fp64,
+sequential time loops); this module builds it with gcc and marshals numpy
+arrays.  It also holds the mixer layer's oracle (``mixer_fwd`` /
+``mixer_bwd``): the block flowchart's projections around the C block scan,
+written as fp64 numpy matrix products, and the conv+SiLU reverse mode they
+need.  Definitions followed (reproduction README of arXiv 2607.21000, "Core
+equations" and the block flowchart):
 
     x_n  = sigma(a_n) x_{n-1} + sigma(b_n) h_n B_n^T
     ys_n = x_n C_n / sqrt(N) + D h_n

@@ -7,7 +7,7 @@
  * (the HIP library and its Python binding) never calls it and shares no
  * code, header, table or helper with it.
  *
- * What it computes (sources are the Naju pages; see oracle/README.md):
+ * What it computes (sources: the Naju pages, cited by title and section):
  *
  *   Recurrence ("Core equations", reproduction README of arXiv 2607.21000):
  *       x_n = f_n (.) x_{n-1} + i_n (.) (h_n B_n^T),  f_n = sigma(a_n),

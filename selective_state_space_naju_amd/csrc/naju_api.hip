@@ -142,18 +142,17 @@ static naju_status_t check_ws(naju_op_t op, const naju_dims_t *d, const void *ws
     return NAJU_OK;
 }
 
-static naju_status_t fwd_common(bool block, const naju_dims_t *d, const void *hu, const void *z,
-                                const float *conv_w, const void *conv_state, const void *a,
-                                const void *b, const void *B, const void *C, const float *D,
-                                const float *x0, void *y, float *x_final, void *conv_state_out,
-                                float *ckpt, void *ws, size_t ws_bytes, void *stream)
+// The forward's argument checks other than the workspace's.
+static naju_status_t fwd_check(bool block, const naju_dims_t *d, const void *hu, const void *z,
+                               const float *conv_w, const void *conv_state, const void *a,
+                               const void *b, const void *B, const void *C, const float *D,
+                               const float *x0, const void *y, const float *x_final,
+                               const void *conv_state_out, const float *ckpt)
 {
     TRY(check_dims(d, block));
-    const naju_op_t op = block ? NAJU_OP_BLOCK_FWD : NAJU_OP_SCAN_FWD;
     const size_t e = d->io == NAJU_F32 ? 4 : 2;
     if (empty(d)) return NAJU_OK;
-    const bool has_tok = d->seqlen > 0;
-    if (has_tok) {
+    if (d->seqlen > 0) {
         TRY(need(hu, block ? "u" : "h", e));
         TRY(need(a, "a", e));
         TRY(need(b, "b", e));
@@ -165,7 +164,6 @@ static naju_status_t fwd_common(bool block, const naju_dims_t *d, const void *hu
             TRY(need(z, "z", e));
             TRY(need(conv_w, "conv_w", 4));
         }
-        TRY(check_ws(op, d, ws, ws_bytes));
     }
     TRY(opt(x0, "x0", 4));
     TRY(opt(x_final, "x_final", 4));
@@ -174,6 +172,20 @@ static naju_status_t fwd_common(bool block, const naju_dims_t *d, const void *hu
         TRY(opt(conv_state, "conv_state", e));
         TRY(opt(conv_state_out, "conv_state_out", e));
     }
+    return NAJU_OK;
+}
+
+static naju_status_t fwd_common(bool block, const naju_dims_t *d, const void *hu, const void *z,
+                                const float *conv_w, const void *conv_state, const void *a,
+                                const void *b, const void *B, const void *C, const float *D,
+                                const float *x0, void *y, float *x_final, void *conv_state_out,
+                                float *ckpt, void *ws, size_t ws_bytes, void *stream)
+{
+    TRY(fwd_check(block, d, hu, z, conv_w, conv_state, a, b, B, C, D, x0, y, x_final,
+                  conv_state_out, ckpt));
+    if (empty(d)) return NAJU_OK;
+    const bool has_tok = d->seqlen > 0;
+    if (has_tok) TRY(check_ws(block ? NAJU_OP_BLOCK_FWD : NAJU_OP_SCAN_FWD, d, ws, ws_bytes));
     hipStream_t st = (hipStream_t)stream;
     if (!has_tok)
         return hip_status(launch_empty_seq(d->io, d->batch, d->d_inner, d->d_state, x0, x_final,
@@ -465,6 +477,9 @@ naju_status_t naju_scan_fwd_noalloc(const naju_dims_t *dims, const void *h, cons
                     "the library's %zu; use naju_scan_fwd with a workspace",
                     need_b, kScratchBytes);
     TRY(opt(flags, "flags", 4));
+    // every argument is checked before the device is queried
+    TRY(fwd_check(false, dims, h, nullptr, nullptr, nullptr, a, b, B, C, D, x0, y, x_final,
+                  nullptr, ckpt));
     void *ws = nullptr;
     TRY(scratch_address(&ws));
     TRY(fwd_common(false, dims, h, nullptr, nullptr, nullptr, a, b, B, C, D, x0, y, x_final,

@@ -86,6 +86,11 @@ WORKLOADS = {
                                               16, a_mu=7.0, seed=1003),
     "train_bf16_b8_l2048_d1536_n16": Workload("train_bf16_b8_l2048_d1536_n16", 8, 2048, 1536,
                                               16, seed=1004, block=True, backward=True),
+    # forgetful gates (forget pre-activation around -2, f ~ 0.12): the product of
+    # 1/f over 32 tokens is far past 2^64, so every chunk leaves the rescaled
+    # matrix-core form and takes the register recurrence
+    "scan_bf16_b8_l2048_d1536_n16_forget": Workload("scan_bf16_b8_l2048_d1536_n16_forget", 8,
+                                                    2048, 1536, 16, a_mu=-2.0, seed=1006),
 }
 
 
