@@ -190,7 +190,7 @@ def scan_workload_parts(name, torch, nb, inputs, warmup, launches, keep_sample=N
         traffic = measured_traffic("hbm_traffic_fwd_mfma64_%s.md" % name, FWD64_SRC)
     elif N == 16 and e == 2:
         kernel = "naju::fwd_chunk_kernel<false> (naju_scan_fwd)"
-        traffic = measured_traffic("hbm_traffic_fwd_mfma_%s.md" % name, FWD_SRC)
+        traffic = measured_traffic("hbm_traffic_fwd_chunk_%s.md" % name, FWD_SRC)
     else:
         kernel = "naju_scan_fwd, fp32 register recurrence (d_state %d)" % N
         traffic = None
@@ -498,7 +498,7 @@ def main():
                                             % Bt)
 
     rf_scan = (roofline_hbm(parts["scan_fwd"], "naju::fwd_chunk_kernel<false> (naju_scan_fwd)",
-                            measured_traffic("hbm_traffic_fwd_mfma_scan_bf16_b8_l2048_d1536_n16.md",
+                            measured_traffic("hbm_traffic_fwd_chunk_scan_bf16_b8_l2048_d1536_n16.md",
                                              FWD_SRC))
                if "scan_fwd" in parts else None)
     # dominant part of the timed step
@@ -511,7 +511,9 @@ def main():
                               measured_traffic("hbm_traffic_block_bwd_train_bf16_b8_l2048_d1536_n16.md",
                                                BWD_SRC))
         else:
-            rf = roofline_hbm(parts["block_fwd"], "naju::fwd_chunk_kernel<true> (naju_block_fwd)")
+            rf = roofline_hbm(parts["block_fwd"], "naju::fwd_chunk_kernel<true> (naju_block_fwd)",
+                              measured_traffic("hbm_traffic_fwd_chunk_block_train_bf16_b8_l2048_d1536_n16.md",
+                                               FWD_SRC))
     # the training step's input set stays on the host for the CPU leg; the device
     # buffers are freed before the other workloads
     del sets, base, outs, ws_f, ws_b, ws_s
