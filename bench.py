@@ -507,7 +507,7 @@ def main():
         if parts["block_bwd"]["ms_mean"] >= parts["block_fwd"]["ms_mean"]:
             rf = roofline_hbm(parts["block_bwd"],
                               "naju_block_bwd call: bwd_carry + bwd_carry_scan + bwd_mfma<true> "
-                              "(gradients) + bwd_fix + 4 reduction kernels",
+                              "(gradients) + bwd_fix + finish + dd_reduce2",
                               measured_traffic("hbm_traffic_block_bwd_train_bf16_b8_l2048_d1536_n16.md",
                                                BWD_SRC))
         else:
