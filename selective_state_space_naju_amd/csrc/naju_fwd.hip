@@ -56,6 +56,12 @@ __global__ __launch_bounds__(64 * W) void fwd_kernel(
     constexpr int kCh = 64 / LPC;
     constexpr int kStg = STG ? (4 * T * kCh + 2 * T * N) : 8;
     __shared__ __attribute__((aligned(16))) IO sStg[STG ? W : 1][kStg];
+    // SBC (d_state 16 without STG): each wave's B and C rows, [tok][N] each, staged
+    // once, so that the sequential token loop reads them from LDS instead of making
+    // one round trip to memory per token
+    constexpr bool SBC = !STG && N == 16;
+    constexpr int kBC = SBC ? 2 * T * N : 1;
+    __shared__ __attribute__((aligned(16))) IO sBCs[SBC ? W : 1][kBC];
     __shared__ uint32_t s_ticket, s_epoch;
     __shared__ float sP[W][64];
     __shared__ float sS[W][16][64];
@@ -103,6 +109,31 @@ __global__ __launch_bounds__(64 * W) void fwd_kernel(
             dma16b(rC, vb, (uint32_t)(8 * k * N * 2), stg + 4 * T * kCh + T * N + 8 * k * N);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    if constexpr (SBC) {
+        // 16 bytes per lane and instruction through a buffer whose range ends with the
+        // wave's last valid token (rows past it read 0)
+        static_assert(T * N * sizeof(IO) % 1024 == 0, "staging layout");
+        constexpr int kPer = T * N * (int)sizeof(IO) / 1024;
+        const int rows = n0 < L ? (int)(L - n0 < T ? L - n0 : T) : 0;
+        const int64_t tb = ((int64_t)bi * L + (n0 < L ? n0 : 0)) * N;
+        const uint32_t bytes = (uint32_t)rows * N * (uint32_t)sizeof(IO);
+        const rsrc_t rB = make_rsrc(Bm + tb, bytes), rC = make_rsrc(Cm + tb, bytes);
+        uint4 vb[kPer], vc[kPer];
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            vb[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rB, (uint32_t)(16 * lane + 1024 * k), 0, 0));
+            vc[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  rC, (uint32_t)(16 * lane + 1024 * k), 0, 0));
+        }
+        uint4 *dst = (uint4 *)&sBCs[wv][0];
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            dst[lane + 64 * k] = vb[k];
+            dst[T * N * (int)sizeof(IO) / 16 + lane + 64 * k] = vc[k];
+        }
+        __syncthreads();
     }
     const int cl = lane / LPC;  // this lane's channel inside the tile
 
@@ -178,10 +209,12 @@ __global__ __launch_bounds__(64 * W) void fwd_kernel(
             }
             const float f = sigm(av);
             const float wr = sigm(bv) * hv;
-            const IO *Bn = STG ? stg + 4 * T * kCh + j * N + sg * 16
-                               : Bm + ((int64_t)bi * L + n) * N + sg * 16;
-            const IO *Cn = STG ? stg + 4 * T * kCh + T * N + j * N + sg * 16
-                               : Cm + ((int64_t)bi * L + n) * N + sg * 16;
+            const IO *Bn = STG   ? stg + 4 * T * kCh + j * N + sg * 16
+                           : SBC ? &sBCs[wv][j * N]
+                                 : Bm + ((int64_t)bi * L + n) * N + sg * 16;
+            const IO *Cn = STG   ? stg + 4 * T * kCh + T * N + j * N + sg * 16
+                           : SBC ? &sBCs[wv][T * N + j * N]
+                                 : Cm + ((int64_t)bi * L + n) * N + sg * 16;
             float acc = 0.f;
 #pragma unroll
             for (int s = 0; s < 16; ++s) {
@@ -309,8 +342,9 @@ __global__ __launch_bounds__(64 * W) void fwd_kernel(
         for (int j = 0; j < T; ++j) {
             const int64_t n = n0 + j;
             if (n < L) {
-                const IO *Cn = STG ? stg + 4 * T * kCh + T * N + j * N + sg * 16
-                                   : Cm + ((int64_t)bi * L + n) * N + sg * 16;
+                const IO *Cn = STG   ? stg + 4 * T * kCh + T * N + j * N + sg * 16
+                               : SBC ? &sBCs[wv][T * N + j * N]
+                                     : Cm + ((int64_t)bi * L + n) * N + sg * 16;
                 float dot = 0.f;
 #pragma unroll
                 for (int s = 0; s < 16; ++s) dot = fmaf(xin[s], to_f(Cn[s]), dot);
