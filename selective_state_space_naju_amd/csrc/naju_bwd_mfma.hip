@@ -265,6 +265,46 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
         };
 
         // ------------------------------------------------------- phase A
+        // Every global load of the phase is issued first, so that the phase waits for
+        // one round trip: a, dy, z, b, h|u (the block's u rows, and the three rows
+        // before the wave, go to LDS below), D and the conv taps.
+        uint16_t ra[16], rdy[16], rz[BLOCK ? 16 : 1], rb[16], ru[16], rpv[3];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            ra[i] = LD16(a, i);
+            rdy[i] = LD16(dy, i);
+            if (BLOCK) rz[i] = LD16(z, i);
+            rb[i] = LD16(bg, i);
+            ru[i] = LD16(hu, i);
+        }
+        if (BLOCK) {
+            // u at the three tokens before the wave: the previous rows of u, or the
+            // carried conv state before the sequence start
+            const bool first = n0 == 0;
+            const bf16 *pbase = first ? conv_state : hu;
+            const int64_t poff = first ? (int64_t)bi * 3 * Di : (tokbase + n0 - 3) * Di;
+            const uint32_t pbytes = ((first && !conv_state) || !active) ? 0u : 3u * (uint32_t)Di * 2;
+            const rsrc_t rp = make_rsrc(pbytes ? (const void *)(pbase + poff + tile * 32)
+                                               : (const void *)a,
+                                        pbytes);
+            const uint32_t po = valid ? (uint32_t)col * 2 : kOOB;
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                rpv[k] = __builtin_amdgcn_raw_buffer_load_b16(rp, po + (uint32_t)(k * Di) * 2, 0, 0);
+        }
+        // inputs of w = sigma(b) h
+        float cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f, Dc = 0.f;
+        if (valid) {
+            Dc = D[c];
+            if (BLOCK) {
+                cw0 = conv_w[c * 4 + 0];
+                cw1 = conv_w[c * 4 + 1];
+                cw2 = conv_w[c * 4 + 2];
+                cw3 = conv_w[c * 4 + 3];
+            }
+        }
+        auto bf = [](uint16_t v) -> float { return __uint_as_float((uint32_t)v << 16); };
+
         // gates and readout gradients; the wave's reverse carry (P_last, R)
         float invP[16], g[16];
         bf16x8 GpH[2], GpL[2];
@@ -273,13 +313,13 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
             float invf[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float av = LD(a, i);
-                float dv = LD(dy, i);
+                const float av = bf(ra[i]);
+                float dv = bf(rdy[i]);
                 const float e = tval(i) ? ex2(-av * kLog2e) : 0.f;
                 invf[i] = 1.f + e;
                 sSA[tw][i][lane] = (_Float16)(e * rcp(invf[i]) * kSigScale);  // sigma(-a)
                 if (BLOCK) {
-                    const float zv = LD(z, i);
+                    const float zv = bf(rz[i]);
                     const float ez = ex2(-zv * kLog2e);
                     const float sz = rcp(1.f + ez);
                     const float szm = 1.f - sz;  // sigma(-z): only z sigma(-z) is used, absolute error suffices
@@ -320,39 +360,16 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                 GpL[i >> 3][i & 7] = lo;
             }
         }
-        // inputs of w = sigma(b) h
-        float cw0 = 0.f, cw1 = 0.f, cw2 = 0.f, cw3 = 0.f, Dc = 0.f;
-        if (valid) {
-            Dc = D[c];
-            if (BLOCK) {
-                cw0 = conv_w[c * 4 + 0];
-                cw1 = conv_w[c * 4 + 1];
-                cw2 = conv_w[c * 4 + 2];
-                cw3 = conv_w[c * 4 + 3];
-            }
-        }
         // the u window: the wave's 32 tokens and the three before, staged in LDS
         // (row 3 + t is token n0 + t); window u_{n-3..n} of slot 4q+r is rows
         // 8q + 4h + r .. 8q + 4h + r + 3
         auto win = [&](int q, int k) -> float { return to_f(sUw[tw][8 * q + 4 * hh + k][col]); };
         auto fill_window = [&]() {
-            // u at the three tokens before the wave: the previous rows of u, or the
-            // carried conv state before the sequence start
-            const bool first = n0 == 0;
-            const bf16 *pbase = first ? conv_state : hu;
-            const int64_t poff = first ? (int64_t)bi * 3 * Di : (tokbase + n0 - 3) * Di;
-            const uint32_t pbytes = ((first && !conv_state) || !active) ? 0u : 3u * (uint32_t)Di * 2;
-            const rsrc_t rp = make_rsrc(pbytes ? (const void *)(pbase + poff + tile * 32)
-                                               : (const void *)a,
-                                        pbytes);
-            const uint32_t po = valid ? (uint32_t)col * 2 : kOOB;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sUw[tw][3 + tok(i)][col] = (bf16)LD16(hu, i);
+            for (int i = 0; i < 16; ++i) sUw[tw][3 + tok(i)][col] = (bf16)ru[i];
             if (!upper) {
 #pragma unroll
-                for (int k = 0; k < 3; ++k)
-                    sUw[tw][k][col] = (bf16)__builtin_amdgcn_raw_buffer_load_b16(
-                        rp, po + (uint32_t)(k * Di) * 2, 0, 0);
+                for (int k = 0; k < 3; ++k) sUw[tw][k][col] = (bf16)rpv[k];
             }
         };
         // h = SiLU(pre) of the block and its derivative, from the u window in LDS
@@ -366,15 +383,9 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
         float h[16], hdk[BLOCK ? 16 : 1];  // h and (block) SiLU'(pre)
         bf16x8 WB[2], WBl[2];     // W' as bf16 hi + lo parts
         {
-            float uv[16], bv[16], ib[16];
-            // every load issued before any is used (one round trip, not one per token)
+            float ib[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (!BLOCK) uv[i] = LD(hu, i);
-                bv[i] = LD(bg, i);
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) ib[i] = rcp(1.f + ex2(-bv[i] * kLog2e));
+            for (int i = 0; i < 16; ++i) ib[i] = rcp(1.f + ex2(-bf(rb[i]) * kLog2e));
             if (BLOCK) fill_window();
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -385,7 +396,7 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                     if constexpr (BLOCK)
                         hv = silu_at(q, r, hdk[i]);
                     else
-                        hv = uv[i];
+                        hv = bf(ru[i]);
                     h[i] = hv;
                     const float wp = ib[i] * hv * invP[i];
                     ok = ok && (__builtin_fabsf(wp) < 1e30f);
