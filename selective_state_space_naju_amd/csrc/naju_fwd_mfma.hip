@@ -9,9 +9,10 @@
 // sequential loop is an affine scan; it is computed here as one:
 //
 //   * inside a wave's 32-token chunk, with the chunk-local running product
-//     P_n = prod_{j<=n} f_j and the rescaled writes W'_k = w_k / P_k,
-//         x_n = P_n (x_in + sum_{k<=n} W'_k B_k)
-//         y_n = P_n ( sum_{k<=n} G[n,k] W'_k + C_n x_in / sqrt(N) ) + D h_n
+//     P_n = prod_{j<=n} f_j, a pivot p (token 16) and the rescaled writes
+//     W'_k = w_k P_p / P_k,
+//         x_n = (P_n / P_p) (P_p x_in + sum_{k<=n} W'_k B_k)
+//         y_n = (P_n / P_p) ( sum_{k<=n} G[n,k] W'_k + C_n P_p x_in / sqrt(N) ) + D h_n
 //     with G = tril(C B^T) / sqrt(N) shared by every channel: G @ W', the
 //     chunk's state increment B^T W' and C @ x_in run on the matrix cores
 //     (v_mfma_f32_32x32x16_bf16, operands split into bf16 hi + lo parts so the
@@ -43,10 +44,12 @@
 // the tiles (HBM -> LDS, 16 bytes per lane, no registers involved); waves 0
 // and 1 run the look-back, so their polls never queue behind a copy.
 //
-// Safety: the factorisation needs 1/P over a chunk to stay in range (the Muir
-// page warns that unpivoted chunked decay factorisations overflow).  A wave
-// whose chunk has prod(1/f) > 2^64 or a non-finite or extreme input computes
-// that chunk with the plain register recurrence instead (exact for any input).
+// Safety: the factorisation needs the decay ratios to stay in range (the Muir
+// page warns that unpivoted chunked decay factorisations overflow, and pivots
+// at a chunk point): with the pivot in the middle, P_p / P_k and P_n / P_p each
+// span at most 16 tokens.  A wave whose half-chunk has prod(1/f) > 2^96 or a
+// non-finite or extreme input computes that chunk with the plain register
+// recurrence instead (exact for any input).
 #include <type_traits>
 
 #include "naju_device.h"
@@ -417,10 +420,12 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
         }
 
         // ------------------------------------------------------ gates, W', P
-        // e_a = e^{-a}, e_b = e^{-b}; invP_n = prod_{k<=n} (1 + e_a) = 1/P_n over
-        // the wave's 32 tokens.  One reciprocal r = 1 / (invP (1 + e_b)) gives
-        // sigma(b) = r invP and P = r (1 + e_b).  Tokens past the end of the
-        // sequence (only in the last wave of a row) get f = 1 and w = 0.
+        // e_a = e^{-a}, e_b = e^{-b}; invP_n = prod (1 + e_a) = P_p / P_n, the decay
+        // between token n and the pivot p (the wave's token 16), so that neither it
+        // nor its inverse spans more than 16 tokens.  One reciprocal
+        // r = 1 / (invP (1 + e_b)) gives sigma(b) = r invP and P_n / P_p = r (1 + e_b).
+        // Tokens past the end of the sequence (only in the last wave of a row) get
+        // f = 1 and w = 0.
         uint32_t rw[3][8];  // EARLY: h, a, b of column tile 1, tokens (2p, 2p + 1)
         if constexpr (EARLY) {
             const int chn = 2 * col + 1;
@@ -445,7 +450,8 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
         float Pv[2][16];  // P (block: P SiLU(z)), the factor of the token's output
         f32x16 Y[2];      // D h / P, then + G W', then + C x_in
         bf16x8 Whi[2][2], Wlo[2][2];
-        float Ptot[2];
+        float Ptot[2];  // P over tokens 16..31, the second half (the aggregate's scale)
+        float rQv[2];   // P over tokens 0..15: P at the pivot
         bool ok = true;
         auto gates = [&](auto tail_c) {
             constexpr bool TL = decltype(tail_c)::value;
@@ -469,15 +475,28 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
                     }
                     tot[q] = run;
                 }
-                float E[4], acc = 1.f;
+                // The decay is pivoted at token 16 (the chunk's middle): with Q the
+                // product over tokens 0..15, invP'_k = invP_k / Q, so W' = w P_p / P_k and
+                // the outputs' factor P_n / P_p stay within a 16-token product either side.
+                float E[4], acc = 1.f, Q = 1.f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
+                    if (q == 2) {  // restart the running product at the pivot
+                        Q = acc;
+                        acc = 1.f;
+                    }
                     const float pt = xhalf(tot[q], upper);  // partner group (q, 1-h)
                     // token order of the groups: (0,0) (0,1) (1,0) (1,1) ...
                     E[q] = upper ? acc * pt : acc;
                     acc *= tot[q] * pt;
                 }
-                ok = ok && (acc <= 18446744073709551616.f);  // 2^64; false for NaN
+                // 2^96 bounds for both halves (W' then stays below 2^96 |h| and the
+                // G @ W' sums far below fp32's range); false for NaN
+                ok = ok && (Q <= 0x1p96f) && (acc <= 0x1p96f);
+                const float rQ = rcp(Q);
+                E[0] *= rQ;  // tokens before the pivot: P_p / P_k <= 1
+                E[1] *= rQ;
+                rQv[j] = rQ;
                 Ptot[j] = rcp(acc);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
@@ -555,8 +574,9 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
                     sacc = mfma(Bsv[kb], Wlo[j][kb], sacc);
                 }
 #pragma unroll
+                // S = P_T sum_k B_k w_k / P_k = (P_T / P_p) B^T W'; the wave's P_T = Q^-1 Ptot
                 for (int i = 0; i < 8; ++i) sS[wv][tok(i)][2 * col + j] = sacc[i] * Ptot[j];
-                if (!upper) sP[wv][2 * col + j] = Ptot[j];
+                if (!upper) sP[wv][2 * col + j] = Ptot[j] * rQv[j];
             }
             f32x16 g = {};
             g = mfma(Bop, Csc, g);  // g[i] = C_{col} . B_{tok(i)} / sqrt(N) = G[col][tok(i)]
@@ -771,8 +791,12 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
             if (y) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
+                    // P_n C x = (P_n / P_p) C (P_p x): the state enters scaled by P_p
+                    float xp[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) xp[k] = xs[j][k] * rQv[j];
                     bf16x8 xh, xl;
-                    split8(xs[j], xh, xl);
+                    split8(xp, xh, xl);
                     Y[j] = mfma(Csc, xh, Y[j]);
                     Y[j] = mfma(Csc, xl, Y[j]);
                 }

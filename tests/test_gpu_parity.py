@@ -289,6 +289,44 @@ def test_bf16_fallback_chunks(block, N):
 
 
 @pytest.mark.parametrize("block", [False, True], ids=["scan", "block"])
+def test_bf16_strongly_forgetting_gates(block):
+    """Forget pre-activations around -3.5 (f ~ 0.03): a 32-token chunk's decay spans
+    about 2^160, which only the pivoted factorisation (each half-chunk's product of
+    1/f bounded) keeps on the matrix cores; the few half-chunks past the bound take
+    the register recurrence.  Forward and backward against the oracle."""
+    Bt, L, Di, N = 2, 500, 128, 16
+    d = inputs.draw(Bt, L, Di, N, io="bf16", seed=29, a_mu=-3.5, x0=True, backward=True,
+                    dx_final=True, block=block, conv_state=block)
+    print("strongly forgetting", block, flush=True)
+    D, x0, dxf = f32_dev(d["D"]), f32_dev(d["x0"]), f32_dev(d["dx_final"])
+    if block:
+        t = {k: to_dev(d[k], "bf16") for k in ("u", "z", "a", "b", "B", "C", "dy", "conv_state")}
+        w = f32_dev(d["conv_w"])
+        y, xf, _, ck = nb.block_fwd(t["u"], t["z"], w, t["a"], t["b"], t["B"], t["C"], D, x0,
+                                    t["conv_state"], return_ckpt=True)
+        g = nb.block_bwd(t["u"], t["z"], w, t["a"], t["b"], t["B"], t["C"], D, t["dy"], x0, dxf,
+                         t["conv_state"], ck)
+        ys, xs, _ = oracle.block_fwd(d["u"], d["z"], d["conv_w"], d["a"], d["b"], d["B"], d["C"],
+                                     d["D"], d["x0"], d["conv_state"])
+        ref = oracle.block_bwd(d["u"], d["z"], d["conv_w"], d["a"], d["b"], d["B"], d["C"], d["D"],
+                               d["x0"], d["dy"], d["dx_final"], d["conv_state"])
+        ref["dconv_w"] = ref["dw"]
+        names = ("du", "dz", "da", "db", "dB", "dC", "dD", "dx0", "dconv_w", "dconv_state")
+    else:
+        t = {k: to_dev(d[k], "bf16") for k in ("h", "a", "b", "B", "C", "dy")}
+        y, xf, ck = nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], D, x0, return_ckpt=True)
+        g = nb.scan_bwd(t["h"], t["a"], t["b"], t["B"], t["C"], D, t["dy"], x0, dxf, ckpt=ck)
+        ys, xs = oracle.scan_fwd(d["h"], d["a"], d["b"], d["B"], d["C"], d["D"], d["x0"])
+        ref = oracle.scan_bwd(d["h"], d["a"], d["b"], d["B"], d["C"], d["D"], d["x0"], d["dy"],
+                              d["dx_final"])
+        names = ("dh", "da", "db", "dB", "dC", "dD", "dx0")
+    torch.cuda.synchronize()
+    assert_close("y", host(y), ys, TOL["bf16"])
+    assert_close("x_final", host(xf), xs, TOL["bf16"])
+    _grad_checks(names, g, ref, "bf16")
+
+
+@pytest.mark.parametrize("block", [False, True], ids=["scan", "block"])
 def test_bf16_bwd_fallback_chunks(block):
     """Backward on the matrix-core path with chunks it must hand to the plain reverse
     recurrence (f = 0 resets, very wide forget gates), mixed with ordinary chunks."""
