@@ -21,17 +21,25 @@
 // w_n B_n), so da_n = sigma(-a_n) Phi_n is an exclusive prefix sum over the
 // chunk.  Every contraction runs on v_mfma_f32_32x32x16_bf16 with the forward's
 // lane order (lane l owns column l%32 and the 16 chunk tokens {8q + 4h + r},
-// h = l/32); carried quantities (x_in, Mu, Gp) use bf16 hi + lo operand pairs.
+// h = l/32), every operand as a bf16 hi + lo pair (three products per pair).
+//
+// The products take the decay pivoted at the wave's token 16, as the forward
+// does: with p = 15 they use W'' = w P_p / P_k, Gp'' = g P_n / P_p,
+// X = P_p x_in and Mu'' = (P_last / P_p) mu_in, which give the same Z P, dw,
+// H, dB and dC (each P_p cancels per channel) while every scale factor spans
+// at most one 16-token half of the wave.  The rescaled form holds while each
+// half's product of 1/f stays below 2^96 (forget pre-activations down to about
+// -4 on average).
 //
 // A workgroup owns 128 tokens (four token-waves) of a super-tile of n_sub
 // 32-channel tiles, visited in turn; its dB/dC partial over those channels is
 // accumulated in the matrix registers and written once.  Activations are read
 // and written through buffer resources whose range ends at the last valid
-// token, so ragged tails need no branches.  A wave whose chunk has
-// prod(1/f) > 2^64 or a non-finite value cannot use the rescaled form: it
-// still publishes its exact reverse carry, records itself with its entering
-// adjoint, and a follow-up kernel recomputes its gradients with the plain
-// reverse recurrence.
+// token, so ragged tails need no branches.  A wave with a half past the bound,
+// or a non-finite value, cannot use the rescaled form: it still publishes its
+// exact reverse carry (from the plain running product, which underflows
+// instead of overflowing), records itself with its entering adjoint, and a
+// follow-up kernel recomputes its gradients with the plain reverse recurrence.
 #include "naju_device.h"
 #include "naju_launch.h"
 
@@ -58,16 +66,6 @@ __device__ __forceinline__ void split2(float v, __bf16 &hi, __bf16 &lo)
 }
 
 __device__ __forceinline__ __bf16 asbf(bf16 v) { return __builtin_bit_cast(__bf16, v); }
-
-// Bit pattern of element s of a bf16x8.  Goes through the whole vector: a
-// bit_cast of a single __bf16 vector element to an integer is mis-lowered by
-// this compiler (every element reads as element 0).
-__device__ __forceinline__ bf16 bits_of(const bf16x8 &v, int s)
-{
-    const uint4 q = __builtin_bit_cast(uint4, v);
-    const uint32_t w = (s >> 1) == 0 ? q.x : (s >> 1) == 1 ? q.y : (s >> 1) == 2 ? q.z : q.w;
-    return (bf16)(w >> (16 * (s & 1)));
-}
 
 // Raw buffer over [p, p + bytes): loads past the end return 0, stores past the
 // end are dropped (the hardware range check of a stride-0 buffer, applied to the
@@ -150,11 +148,6 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
     __shared__ _Float16 sSA[kTW][16][64];  // sigma(-a) * kSigScale
     __shared__ float sGZ[BLOCK ? kTW : 1][16][64];
     __shared__ bf16 sUw[BLOCK ? kTW : 1][35][32];  // u: three tokens before the wave, then its 32
-    // per-wave transposes for the channel contractions (bf16, padded rows)
-    __shared__ __attribute__((aligned(16))) bf16 sGT[kTW][32][40];  // Gp  [token][channel]
-    __shared__ __attribute__((aligned(16))) bf16 sWT[kTW][32][40];  // W'  [token][channel]
-    __shared__ __attribute__((aligned(16))) bf16 sXT[kTW][16][40];  // x_in [state][channel]
-    __shared__ __attribute__((aligned(16))) bf16 sMT[kTW][16][40];  // Mu   [state][channel]
     __shared__ __attribute__((aligned(16))) bf16 sBr[kTW * 32][16];  // B rows of the 128 tokens
     __shared__ __attribute__((aligned(16))) bf16 sCr[kTW * 32][16];  // C rows / sqrt(N)
 
@@ -305,10 +298,15 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
         }
         auto bf = [](uint16_t v) -> float { return __uint_as_float((uint32_t)v << 16); };
 
-        // gates and readout gradients; the wave's reverse carry (P_last, R)
+        // gates and readout gradients; the wave's reverse carry (P_last, R).  The
+        // decay is pivoted at the wave's token 16, as in the forward: invP holds
+        // P_p / P_k, Gp = g P_n / P_p, W' = w P_p / P_k, and the products take
+        // X = P_p x_in and Mu = (P_last / P_p) mu_in, so that every scale factor spans
+        // at most 16 tokens.
         float invP[16], g[16];
         bf16x8 GpH[2], GpL[2];
         bool ok = true;
+        float rQ, plp;  // P_p, and P_last / P_p of the lane's channel
         {
             float invf[16];
 #pragma unroll
@@ -339,21 +337,28 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                 }
                 tot[q] = run;
             }
-            float E[4], acc = 1.f;
+            float E[4], acc = 1.f, Q = 1.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                if (q == 2) {  // restart the running product at the pivot
+                    Q = acc;
+                    acc = 1.f;
+                }
                 const float pt = xhalf(tot[q], upper);  // partner group (q, 1-h)
                 // token order of the groups: (0,0) (0,1) (1,0) (1,1) ...
                 E[q] = upper ? acc * pt : acc;
                 acc *= tot[q] * pt;
             }
-            ok = acc <= 18446744073709551616.f;  // 2^64; false for NaN
+            ok = (Q <= 0x1p96f) && (acc <= 0x1p96f);  // both halves; false for NaN
+            rQ = rcp(Q);
+            E[0] *= rQ;
+            E[1] *= rQ;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 invP[i] = E[i >> 2] * cum[i];
                 const float P = rcp(invP[i]);
                 const float gp = g[i] * P;
-                ok = ok && (__builtin_fabsf(gp) < 1e30f);
+                ok = ok && (__builtin_fabsf(gp) < 0x1p110f);
                 __bf16 hi, lo;
                 split2(gp, hi, lo);
                 GpH[i >> 3][i & 7] = hi;
@@ -399,15 +404,13 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                         hv = bf(ru[i]);
                     h[i] = hv;
                     const float wp = ib[i] * hv * invP[i];
-                    ok = ok && (__builtin_fabsf(wp) < 1e30f);
+                    ok = ok && (__builtin_fabsf(wp) < 0x1p110f);
                     __bf16 whi, wlo;
                     split2(wp, whi, wlo);
                     WB[i >> 3][i & 7] = whi;
                     WBl[i >> 3][i & 7] = wlo;
                 }
             }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sWT[tw][tok(i)][col] = bits_of(WB[i >> 3], i & 7);
         }
         const bool wave_ok = __all(ok);
         // x_in (forward checkpoint): states 8h..8h+7 of channel col; and the
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
 #pragma unroll
             for (int k = 0; k < 8; ++k) mu0[k] = muin[me * (16 * 32) + (8 * hh + k) * 32 + col];
         }
-        {
+        if (wave_ok) {
             f32x16 r = {};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -431,10 +434,58 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                 r = mma(Cv, GpL[kb], r);
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) sR[tw][tok(i)][col] = r[i];
-            if (upper) sQ[tw][col] = rcp(invP[15]);  // P at the wave's last token
+            for (int i = 0; i < 8; ++i) sR[tw][tok(i)][col] = r[i] * rQ;  // R = P_p C^T Gp
+            // P_last / P_p from the token-31 lane (the upper half), and the true P_last
+            const float pl_own = rcp(invP[15]);
+            const float pl_other = xhalf(pl_own, upper);
+            plp = upper ? pl_own : pl_other;
+            if (upper) sQ[tw][col] = pl_own * rQ;
+        } else {
+            // A wave outside the rescaled form still owes the earlier waves its exact
+            // carry.  The pivoted factors can overflow here (a half-chunk's product of
+            // 1/f past the float range, or f = 0), so the carry is formed from the
+            // plain running product P_n = prod_{j<=n} f_j, which underflows to 0
+            // instead.  a is read again (an L2 hit) rather than kept live.
+            float cum[16], tot[4];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sGT[tw][tok(i)][col] = bits_of(GpH[i >> 3], i & 7);
+            for (int q = 0; q < 4; ++q) {
+                float run = 1.f;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * q + r;
+                    run *= tval(i) ? 1.f + ex2(-LD(a, i) * kLog2e) : 1.f;
+                    cum[i] = run;
+                }
+                tot[q] = run;
+            }
+            float acc = 1.f;
+            bf16x8 PH[2], PL[2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float pt = xhalf(tot[q], upper);
+                const float Eq = upper ? acc * pt : acc;
+                acc *= tot[q] * pt;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * q + r;
+                    cum[i] *= Eq;  // 1 / P at token tok(i)
+                    __bf16 hi, lo;
+                    split2(g[i] * rcp(cum[i]), hi, lo);
+                    PH[i >> 3][i & 7] = hi;
+                    PL[i >> 3][i & 7] = lo;
+                }
+            }
+            f32x16 r = {};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 Cv = trans(sCr, kb, col < N);
+                r = mma(Cv, PH[kb], r);
+                r = mma(Cv, PL[kb], r);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sR[tw][tok(i)][col] = r[i];
+            if (upper) sQ[tw][col] = rcp(cum[15]);
+            plp = 0.f;
         }
         __syncthreads();
 
@@ -461,10 +512,11 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
             float t = 0.f;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                Mu[k] = pl * mu[k];
-                t = fmaf(Mu[k] + sR[tw][8 * hh + k][col], xin[k], t);
-                sXT[tw][8 * hh + k][col] = from_f<bf16>(xin[k]);
-                sMT[tw][8 * hh + k][col] = from_f<bf16>(Mu[k]);
+                // Phi_0 = mu_out . x_in with the true Mu = P_last mu_in and R; the
+                // products take the pivoted Mu and X
+                t = fmaf(fmaf(pl, mu[k], sR[tw][8 * hh + k][col]), xin[k], t);
+                Mu[k] = plp * mu[k];
+                xin[k] *= rQ;
             }
             phi0 = t + xhalf(t, upper);
         }
@@ -491,19 +543,20 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
             }
         } else if (active) {
             const f32x16 zero = {};
+            bf16x8 XH, XL, MH, ML;  // x_in and Mu (states 8h..8h+7) as A operands
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                __bf16 h1, l1, h2, l2;
+                split2(xin[k], h1, l1);
+                split2(Mu[k], h2, l2);
+                XH[k] = h1;
+                XL[k] = l1;
+                MH[k] = h2;
+                ML[k] = l2;
+            }
+
             f32x16 Z, PU;  // PU = G^T_{m>=n} Gp + B.Mu, so dw = PU / P
             {
-                bf16x8 XH, XL, MH, ML;
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    __bf16 h1, l1, h2, l2;
-                    split2(xin[k], h1, l1);
-                    split2(Mu[k], h2, l2);
-                    XH[k] = h1;
-                    XL[k] = l1;
-                    MH[k] = h2;
-                    ML[k] = l2;
-                }
                 const bf16x8 Bop = rows(sBr), Csc = rows(sCr);
                 // tril(G) and its transpose as A operands (C pre-scaled, so G =
                 // Csc.B), each in bf16 hi + lo parts: the gate gradient is a prefix
@@ -659,54 +712,116 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                     *(float4 *)(dw_part + (((int64_t)bi * n_waves + wrow) * Di + c) * 4) =
                         make_float4(dwa0, dwa1, dwa2, dwa3);
             }
-
-            // channel contractions: H = Gp W'^T; columns 0..15 of dBC gather
-            // tril(H)^T C + W' Mu (C pre-scaled), columns 16..31 Gp X_in + tril(H) B
-            __builtin_amdgcn_wave_barrier();
+            // Channel contractions: H = Gp W'^T; columns 0..15 of dBC gather
+            // tril(H)^T C + W' Mu (C pre-scaled), columns 16..31 Gp X_in + tril(H) B.
+            // Every operand and H itself enter as bf16 hi + lo parts: H sums products
+            // over the channels of values whose rounding does not cancel, so a single
+            // bf16 part would leave dB and dC about 1% of their own scale off.
+            // The channel-major operands come from the register layout through a
+            // product with a 0/1 selection matrix on the matrix cores (each output is
+            // one input times 1, so exact): afterwards lane (col, h) holds, for token
+            // (or state) col, the channels tok(i) of the tile in K order.  Gp, W', x_in
+            // and Mu all come out in that one channel order, which is all that a
+            // contraction over channels needs.
             {
-                bf16x8 GpT[2], WpT[2], XM[2];
+                // selection over tokens: element s of block kb in lane (col, h) stands
+                // for token 16 kb + 8 (s >> 2) + 4 h + (s & 3), i.e. tok(8 kb + s)
+                auto sel_tok = [&](int kb) -> bf16x8 {
+                    bf16x8 v;
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    GpT[kb] = __builtin_bit_cast(bf16x8,
-                                                 *(const uint4 *)&sGT[tw][col][16 * kb + 8 * hh]);
-                    WpT[kb] = __builtin_bit_cast(bf16x8,
-                                                 *(const uint4 *)&sWT[tw][col][16 * kb + 8 * hh]);
-                    // state col & 15 over channels: Mu for dB (columns < 16), x_in for dC
-                    const uint4 mq = *(const uint4 *)&sMT[tw][col & 15][16 * kb + 8 * hh];
-                    const uint4 xq = *(const uint4 *)&sXT[tw][col & 15][16 * kb + 8 * hh];
-                    XM[kb] = __builtin_bit_cast(bf16x8, col < N ? mq : xq);
-                }
-                f32x16 HA = zero, HTA = zero;
+                    for (int s = 0; s < 8; ++s) v[s] = (__bf16)(tok(8 * kb + s) == col ? 1.f : 0.f);
+                    return v;
+                };
+                const bf16x8 S0 = sel_tok(0), S1 = sel_tok(1);
+                // transpose of a 32 x 32 operand pair held with rows by lane and
+                // columns by slot: afterwards rows by slot, columns by lane (exact)
+                auto chan_major = [&](const bf16x8 (&v)[2], bf16x8 (&out)[2]) {
+                    f32x16 t = mma(v[0], S0, zero);
+                    t = mma(v[1], S1, t);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    HA = mma(WpT[kb], GpT[kb], HA);    // HA[i]  = H[col][tok(i)]
-                    HTA = mma(GpT[kb], WpT[kb], HTA);  // HTA[i] = H[tok(i)][col]
-                }
-                bf16x8 HAb[2], HTAb[2];
+                    for (int i = 0; i < 16; ++i) out[i >> 3][i & 7] = (__bf16)t[i];
+                };
+                bf16x8 GTh[2], GTl[2], WTh[2], WTl[2];
+                chan_major(GpH, GTh);
+                chan_major(GpL, GTl);
+                chan_major(WB, WTh);
+                chan_major(WBl, WTl);
+                // Mu (state col, columns 0..15) and x_in (state col - 16, columns
+                // 16..31) over the same channels: states 8h + s select column 8h + s
+                // of the first half or of the second
+                bf16x8 XMh[2], XMl[2];
+                {
+                    bf16x8 sm, sx;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    HAb[i >> 3][i & 7] = (__bf16)(tok(i) <= col ? HA[i] : 0.f);
-                    HTAb[i >> 3][i & 7] = (__bf16)(tok(i) >= col ? HTA[i] : 0.f);
+                    for (int s = 0; s < 8; ++s) {
+                        sm[s] = (__bf16)(8 * hh + s == col ? 1.f : 0.f);
+                        sx[s] = (__bf16)(8 * hh + s + 16 == col ? 1.f : 0.f);
+                    }
+                    f32x16 t = mma(MH, sm, zero);
+                    t = mma(ML, sm, t);
+                    t = mma(XH, sx, t);
+                    t = mma(XL, sx, t);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        __bf16 hi, lo;
+                        split2(t[i], hi, lo);
+                        XMh[i >> 3][i & 7] = hi;
+                        XMl[i >> 3][i & 7] = lo;
+                    }
                 }
                 // the A operand of the Mu / x_in term: W' for dB, Gp for dC -- one
-                // product per column half, selected by zeroing the other half of XM
-                bf16x8 XMb[2], XMc[2];
+                // product per column half, the other half of XM zeroed
                 const uint4 z4 = {0u, 0u, 0u, 0u};
+                const bf16x8 zb = __builtin_bit_cast(bf16x8, z4);
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    XMb[kb] = col < N ? XM[kb] : __builtin_bit_cast(bf16x8, z4);
-                    XMc[kb] = col < N ? __builtin_bit_cast(bf16x8, z4) : XM[kb];
+                    const bf16x8 bh = col < N ? XMh[kb] : zb, bl = col < N ? XMl[kb] : zb;
+                    const bf16x8 ch = col < N ? zb : XMh[kb], cl = col < N ? zb : XMl[kb];
+                    dBC = mma(WTh[kb], bh, dBC);  // columns 0..15
+                    dBC = mma(WTh[kb], bl, dBC);
+                    dBC = mma(WTl[kb], bh, dBC);
+                    dBC = mma(GTh[kb], ch, dBC);  // columns 16..31
+                    dBC = mma(GTh[kb], cl, dBC);
+                    dBC = mma(GTl[kb], ch, dBC);
                 }
+                // tril(H) (token m >= k), hi + lo: rows k by lane for tril(H)^T C, then
+                // its transpose (rows m by lane) for tril(H) B
+                {
+                    f32x16 HT = zero;  // HT[i] = H[tok(i)][col]
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    dBC = mma(HTAb[kb], trans(sCr, kb, col < N), dBC);   // columns 0..15
-                    dBC = mma(WpT[kb], XMb[kb], dBC);                   // columns 0..15
-                    dBC = mma(HAb[kb], trans(sBr, kb, col >= N), dBC);  // columns 16..31
-                    dBC = mma(GpT[kb], XMc[kb], dBC);   // columns 16..31
+                    for (int kb = 0; kb < 2; ++kb) {
+                        HT = mma(GTh[kb], WTh[kb], HT);
+                        HT = mma(GTh[kb], WTl[kb], HT);
+                        HT = mma(GTl[kb], WTh[kb], HT);
+                    }
+                    bf16x8 Hh[2], Hl[2];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        __bf16 hi, lo;
+                        split2(tok(i) >= col ? HT[i] : 0.f, hi, lo);
+                        Hh[i >> 3][i & 7] = hi;
+                        Hl[i >> 3][i & 7] = lo;
+                    }
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        const bf16x8 Ct = trans(sCr, kb, col < N);
+                        dBC = mma(Hh[kb], Ct, dBC);  // columns 0..15
+                        dBC = mma(Hl[kb], Ct, dBC);
+                    }
+                    bf16x8 Th[2], Tl[2];
+                    chan_major(Hh, Th);
+                    chan_major(Hl, Tl);
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        const bf16x8 Bt = trans(sBr, kb, col >= N);
+                        dBC = mma(Th[kb], Bt, dBC);  // columns 16..31
+                        dBC = mma(Tl[kb], Bt, dBC);
+                    }
                 }
             }
+
         }
-        __syncthreads();  // sQ, sR, sMu are rewritten by the next tile
+        __syncthreads();  // sQ and sR are rewritten by the next tile
     };
     for (int st = 0; st < n_sub && tile_of(st) < n_tiles; ++st) {
         if (Lw == T)

@@ -531,7 +531,7 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
                             wp[4 * qq + r] = t * (rq * invP);  // h sigma(b) / P
                             Pv[j][i] = fmaf(rq, eb, rq);       // P
                             Y[j][i] = Dn[j] * t;               // D h / P
-                            ok = ok && (__builtin_fabsf(wp[4 * qq + r]) < 1e30f) &&
+                            ok = ok && (__builtin_fabsf(wp[4 * qq + r]) < 0x1p110f) &&
                                  (qv < 1.329228e36f);  // 2^120
                         }
                     }
