@@ -19,10 +19,15 @@
 // carry its state in registers (token block t: states 16 t .. 16 t + 15) and
 // compose it with their chunk aggregates through LDS.  A 64-channel row is a
 // whole 128-byte line, so the tile copies fetch no half lines; one workgroup
-// fills a CU (136 KB of LDS).  A wave whose chunk cannot take the
-// rescaled form (prod 1/f beyond 2^64, a non-finite gate or h) runs the plain
-// register recurrence for it instead.  The host uses this kernel when the
-// rows alone keep a good part of the device busy (Bt * d_inner / 64 >= 32).
+// fills a CU (136 KB of LDS).
+//
+// The decay is pivoted at the wave's token 16: with P_p = prod_{j<=15} f_j the
+// products take W'' = w P_p / P_k, the outputs P_n / P_p, the entering state
+// P_p x_in and the aggregate the factor P_T / P_p, so every scale factor spans at
+// most one 16-token half.  A wave with a half whose product of 1/f passes 2^96,
+// or a non-finite gate or h, runs the plain register recurrence for its chunk
+// instead.  The host uses this kernel when the rows alone keep a good part of
+// the device busy (Bt * d_inner / 64 >= 32).
 #include <type_traits>
 
 #include "naju_device.h"
@@ -319,7 +324,7 @@ __global__ __launch_bounds__(64 * kWv, 1) void fwd_mfma64_kernel(
         // ------------------------------------------------------ gates, W', P
         // Tokens past the end of the sequence (only in the last chunk of a row)
         // get f = 1 and w = 0, so they leave the state and the aggregate alone.
-        float Pv[16], FT[16], Ptot;
+        float Pv[16], FT[16], Ptot, rQ;  // Ptot = P_T / P_p, rQ = P_p
         bf16x8 Whi[2], Wlo[2];
         bool ok = true;
         auto gates = [&](auto tail_c) {
@@ -361,15 +366,22 @@ __global__ __launch_bounds__(64 * kWv, 1) void fwd_mfma64_kernel(
                 }
                 tot[q] = run;
             }
-            float E[4], acc = 1.f;
+            float E[4], acc = 1.f, Q = 1.f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                if (q == 2) {  // restart the running product at the pivot
+                    Q = acc;
+                    acc = 1.f;
+                }
                 const float pt = xhalf(tot[q], upper);  // partner group (q, 1-h)
                 // token order of the groups: (0,0) (0,1) (1,0) (1,1) ...
                 E[q] = upper ? acc * pt : acc;
                 acc *= tot[q] * pt;
             }
-            ok = ok && (acc <= 18446744073709551616.f);  // 2^64; false for NaN
+            ok = ok && (Q <= 0x1p96f) && (acc <= 0x1p96f);  // both halves; false for NaN
+            rQ = rcp(Q);
+            E[0] *= rQ;
+            E[1] *= rQ;
             Ptot = rcp(acc);
             float wp[16];
 #pragma unroll
@@ -381,7 +393,7 @@ __global__ __launch_bounds__(64 * kWv, 1) void fwd_mfma64_kernel(
                 wp[i] = t * (r * invP);        // h sigma(b) / P
                 Pv[i] = fmaf(r, eb[i], r);     // P
                 FT[i] = Dc * t;                // y = P (G W' + C x_in + D h / P)
-                ok = ok && (__builtin_fabsf(wp[i]) < 1e30f) && (qv < 1.329228e36f);  // 2^120
+                ok = ok && (__builtin_fabsf(wp[i]) < 0x1p110f) && (qv < 0x1p120f);
             }
             split16(wp, Whi, Wlo);
         };
@@ -430,7 +442,7 @@ __global__ __launch_bounds__(64 * kWv, 1) void fwd_mfma64_kernel(
                     *(float4 *)&sS[wv][col][32 * rt + 8 * q + 4 * hh] = v;
                 }
             }
-            if (!upper) sP[wv][col] = Ptot;
+            if (!upper) sP[wv][col] = Ptot * rQ;  // P_T
             bf16x8 Ghi[2], Glo[2];
             float gv[16];
 #pragma unroll
@@ -542,7 +554,7 @@ __global__ __launch_bounds__(64 * kWv, 1) void fwd_mfma64_kernel(
             for (int kb = 0; kb < 4; ++kb) {
                 float v[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = xs[kb][e] * scale;
+                for (int e = 0; e < 8; ++e) v[e] = xs[kb][e] * (scale * rQ);  // P_p x_in
                 bf16x8 xh, xl;
                 split8(v, xh, xl);
                 Y = mfma(Cop[kb], xh, Y);

@@ -260,8 +260,9 @@ def test_mfma64_rows_beyond_grid(block):
 def test_bf16_fallback_chunks(block, N):
     """bf16 runs on the matrix-core paths; chunks whose prod(1/f) leaves the safe
     range (a = -inf, or a drawn wide so f is often tiny) or that hold a NaN gate
-    are recomputed by the register recurrence.  Both kinds mix in one call."""
-    Bt, L, Di = (2, 700, 160) if N == 16 else (2, 400, 512)
+    are recomputed by the register recurrence.  Both kinds mix in one call.  (At
+    d_state 64, 2 x 1024 channels make the 32 rows that select the matrix-core form.)"""
+    Bt, L, Di = (2, 700, 160) if N == 16 else (2, 400, 1024)
     d = inputs.draw(Bt, L, Di, N, io="bf16", seed=19, x0=True, block=block, conv_state=block)
     d["a"][0, 100, :10] = -np.inf                      # f = 0: full reset
     d["a"][1, 300:364, 64:] = inputs.bf16_round(       # wide gates: prod(1/f) overflows
@@ -288,16 +289,18 @@ def test_bf16_fallback_chunks(block, N):
     assert_close("x_final", xgh[mx], xf[mx], TOL["bf16"])
 
 
+@pytest.mark.parametrize("N", [16, 64])
 @pytest.mark.parametrize("block", [False, True], ids=["scan", "block"])
-def test_bf16_strongly_forgetting_gates(block):
+def test_bf16_strongly_forgetting_gates(block, N):
     """Forget pre-activations around -3.5 (f ~ 0.03): a 32-token chunk's decay spans
     about 2^160, which only the pivoted factorisation (each half-chunk's product of
     1/f bounded) keeps on the matrix cores; the few half-chunks past the bound take
-    the register recurrence.  Forward and backward against the oracle."""
-    Bt, L, Di, N = 2, 500, 128, 16
+    the register recurrence.  Forward and backward against the oracle (at d_state 64
+    the forward takes its matrix-core form, 32 rows of 64 channels)."""
+    Bt, L, Di = (2, 500, 128) if N == 16 else (2, 300, 1024)
     d = inputs.draw(Bt, L, Di, N, io="bf16", seed=29, a_mu=-3.5, x0=True, backward=True,
                     dx_final=True, block=block, conv_state=block)
-    print("strongly forgetting", block, flush=True)
+    print("strongly forgetting", block, N, flush=True)
     D, x0, dxf = f32_dev(d["D"]), f32_dev(d["x0"]), f32_dev(d["dx_final"])
     if block:
         t = {k: to_dev(d[k], "bf16") for k in ("u", "z", "a", "b", "B", "C", "dy", "conv_state")}
