@@ -88,8 +88,8 @@ __device__ __forceinline__ void stb(rsrc_t r, uint32_t off, float v)
     __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(v), r, off, 0, 0);
 }
 
-// sigma(-v) in (0, 1) is parked as fp16 scaled by 2^15: normal (2^-11 relative)
-// for sigma(-v) >= 2^-29, i.e. v up to about 20; beyond that it underflows
+// sigma(-v) in (0, 1) (v = a or b) is parked as fp16 scaled by 2^15: normal (2^-11
+// relative) for sigma(-v) >= 2^-29, i.e. v up to about 20; beyond that it underflows
 // gradually towards 0 (a gradient factor below 2e-9 there)
 constexpr float kSigScale = 32768.f, kSigUnscale = 1.f / 32768.f;
 
@@ -143,9 +143,10 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
     // reverse carries of the four waves
     __shared__ float sQ[kTW][32];
     __shared__ float sR[kTW][16][32];
-    // per-token factors consumed once, after the matrix products: sigma(-a) and
-    // dy SiLU'(z)  [wave][slot][lane]
+    // per-token factors consumed once, after the matrix products: sigma(-a),
+    // sigma(b), sigma(-b) and dy SiLU'(z)  [wave][slot][lane]
     __shared__ _Float16 sSA[kTW][16][64];  // sigma(-a) * kSigScale
+    __shared__ float sEB[kTW][16][64];     // e^{-b}
     __shared__ float sGZ[BLOCK ? kTW : 1][16][64];
     __shared__ bf16 sUw[BLOCK ? kTW : 1][35][32];  // u: three tokens before the wave, then its 32
     __shared__ __attribute__((aligned(16))) bf16 sBr[kTW * 32][16];  // B rows of the 128 tokens
@@ -388,9 +389,15 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
         float h[16], hdk[BLOCK ? 16 : 1];  // h and (block) SiLU'(pre)
         bf16x8 WB[2], WBl[2];     // W' as bf16 hi + lo parts
         {
+            // sigma(b), and sigma(-b) = e^{-b} sigma(b) (not 1 - sigma(b), which cancels
+            // for large b), parked for the epilogue
             float ib[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) ib[i] = rcp(1.f + ex2(-bf(rb[i]) * kLog2e));
+            for (int i = 0; i < 16; ++i) {
+                const float eb = ex2(-bf(rb[i]) * kLog2e);
+                ib[i] = rcp(1.f + eb);
+                sEB[tw][i][lane] = eb;
+            }
             if (BLOCK) fill_window();
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -605,9 +612,6 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
             // per 4-token group q: outputs, the exclusive prefix for da, the conv
             // transpose (the upper half finishes its previous group once the
             // partner's first three dpre of this group arrive) and dconv_w partials
-            float bq[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) bq[i] = LD(bg, i);
             float dDp = 0.f, dwa0 = 0.f, dwa1 = 0.f, dwa2 = 0.f, dwa3 = 0.f;
             float base = 0.f;              // prefix of ph over the groups before
             float dprev[4] = {0.f, 0.f, 0.f, 0.f};  // upper half: previous group's dpre
@@ -620,10 +624,7 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                     const int i = 4 * q + r;
                     const float dw = invP[i] * PU[i];
                     const float ysd = rcp(invP[i]) * Z[i];
-                    // sigma(b) and sigma(-b) = e^{-b} sigma(b) from b, read again (an L2
-                    // hit; sigma(b) comes out as in the first phase, and sigma(-b) is not
-                    // taken as 1 - sigma(b), which cancels for large b)
-                    const float eb = ex2(-bq[i] * kLog2e);
+                    const float eb = sEB[tw][i][lane];
                     const float ibv = rcp(1.f + eb);
                     const float sbm = eb < __builtin_huge_valf() ? eb * ibv : 1.f;
                     const float hv = h[i];
@@ -726,11 +727,19 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
             {
                 // selection over tokens: element s of block kb in lane (col, h) stands
                 // for token 16 kb + 8 (s >> 2) + 4 h + (s & 3), i.e. tok(8 kb + s)
+                // a 0/1 operand with a single 1 (bf16 0x3f80) at element s, if on
+                auto one_hot = [](bool on, int s) -> bf16x8 {
+                    const uint32_t v = on ? (0x3f80u << (16 * (s & 1))) : 0u;
+                    const int d = s >> 1;
+                    const uint4 q = {d == 0 ? v : 0u, d == 1 ? v : 0u, d == 2 ? v : 0u,
+                                     d == 3 ? v : 0u};
+                    return __builtin_bit_cast(bf16x8, q);
+                };
+                // tok(8 kb + s) == col  <=>  kb = col / 16, h = (col / 4) % 2 and
+                // s = 4 ((col / 8) % 2) + col % 4
                 auto sel_tok = [&](int kb) -> bf16x8 {
-                    bf16x8 v;
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) v[s] = (__bf16)(tok(8 * kb + s) == col ? 1.f : 0.f);
-                    return v;
+                    return one_hot((col >> 4) == kb && ((col >> 2) & 1) == hh,
+                                   4 * ((col >> 3) & 1) + (col & 3));
                 };
                 const bf16x8 S0 = sel_tok(0), S1 = sel_tok(1);
                 // transpose of a 32 x 32 operand pair held with rows by lane and
@@ -751,12 +760,9 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                 // of the first half or of the second
                 bf16x8 XMh[2], XMl[2];
                 {
-                    bf16x8 sm, sx;
-#pragma unroll
-                    for (int s = 0; s < 8; ++s) {
-                        sm[s] = (__bf16)(8 * hh + s == col ? 1.f : 0.f);
-                        sx[s] = (__bf16)(8 * hh + s + 16 == col ? 1.f : 0.f);
-                    }
+                    // 8 h + s == col (columns 0..15), 8 h + s + 16 == col (16..31)
+                    const bf16x8 sm = one_hot(col < 16 && ((col >> 3) & 1) == hh, col & 7);
+                    const bf16x8 sx = one_hot(col >= 16 && ((col >> 3) & 1) == hh, col & 7);
                     f32x16 t = mma(MH, sm, zero);
                     t = mma(ML, sm, t);
                     t = mma(XH, sx, t);
