@@ -42,42 +42,19 @@
 // follow-up kernel recomputes its gradients with the plain reverse recurrence.
 #include "naju_device.h"
 #include "naju_launch.h"
+#include "naju_mfma.h"
 
 namespace naju {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
 namespace {
 
-constexpr int kTW = 4;                  // token-waves per workgroup (128 tokens)
-constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every range used here
+constexpr int kTW = 4;  // token-waves per workgroup (128 tokens)
 
 __device__ __forceinline__ f32x16 mma(const bf16x8 &a, const bf16x8 &b, const f32x16 &c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void split2(float v, __bf16 &hi, __bf16 &lo)
-{
-    hi = (__bf16)v;
-    lo = (__bf16)(v - (float)hi);
-}
-
-__device__ __forceinline__ __bf16 asbf(bf16 v) { return __builtin_bit_cast(__bf16, v); }
-
-// Raw buffer over [p, p + bytes): loads past the end return 0, stores past the
-// end are dropped (the hardware range check of a stride-0 buffer, applied to the
-// lane offset).  Every offset that must be range-checked, row offsets included,
-// is passed as the lane offset; a nonzero scalar soffset carries only offsets
-// that stay in range for every lane that is not already out of range by its
-// lane offset alone, so nothing depends on whether the check covers it.
-__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
-{
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
-                                             0x00020000);
-}
 // bf16 element at byte offset off
 __device__ __forceinline__ float ldb(rsrc_t r, uint32_t off)
 {
@@ -92,16 +69,6 @@ __device__ __forceinline__ void stb(rsrc_t r, uint32_t off, float v)
 // relative) for sigma(-v) >= 2^-29, i.e. v up to about 20; beyond that it underflows
 // gradually towards 0 (a gradient factor below 2e-9 there)
 constexpr float kSigScale = 32768.f, kSigUnscale = 1.f / 32768.f;
-
-// Value held by lane l ^ 32.  v_permlane32_swap exchanges the upper half of
-// its first operand with the lower half of its second; with both operands
-// equal, each half then finds its partner's value in the other result.
-__device__ __forceinline__ float xhalf(float v, bool upper)
-{
-    const uint32_t u = __float_as_uint(v);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __uint_as_float(upper ? r[0] : r[1]);
-}
 
 // Workgroups b and b + 8 run on the same XCD (round-robin dispatch) and start
 // together; they are paired on the two halves of 128-byte rows (two adjacent
@@ -216,7 +183,7 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const bf16 e = r[32 * tw + tok(8 * kb + s)][col & 15];
-                v[s] = asbf(on ? e : (bf16)0);
+                v[s] = as_bf(on ? e : (bf16)0);
             }
             return v;
         };
@@ -354,17 +321,14 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
             rQ = rcp(Q);
             E[0] *= rQ;
             E[1] *= rQ;
+            float gp[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 invP[i] = E[i >> 2] * cum[i];
-                const float P = rcp(invP[i]);
-                const float gp = g[i] * P;
-                ok = ok && (__builtin_fabsf(gp) < 0x1p110f);
-                __bf16 hi, lo;
-                split2(gp, hi, lo);
-                GpH[i >> 3][i & 7] = hi;
-                GpL[i >> 3][i & 7] = lo;
+                gp[i] = g[i] * rcp(invP[i]);
+                ok = ok && (__builtin_fabsf(gp[i]) < 0x1p110f);
             }
+            split16(gp, GpH, GpL);
         }
         // the u window: the wave's 32 tokens and the three before, staged in LDS
         // (row 3 + t is token n0 + t); window u_{n-3..n} of slot 4q+r is rows
@@ -389,6 +353,7 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
         float h[16], hdk[BLOCK ? 16 : 1];  // h and (block) SiLU'(pre)
         bf16x8 WB[2], WBl[2];     // W' as bf16 hi + lo parts
         {
+            float wp[16];
             // sigma(b), and sigma(-b) = e^{-b} sigma(b) (not 1 - sigma(b), which cancels
             // for large b), parked for the epilogue
             float ib[16];
@@ -410,14 +375,11 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                     else
                         hv = bf(ru[i]);
                     h[i] = hv;
-                    const float wp = ib[i] * hv * invP[i];
-                    ok = ok && (__builtin_fabsf(wp) < 0x1p110f);
-                    __bf16 whi, wlo;
-                    split2(wp, whi, wlo);
-                    WB[i >> 3][i & 7] = whi;
-                    WBl[i >> 3][i & 7] = wlo;
+                    wp[i] = ib[i] * hv * invP[i];
+                    ok = ok && (__builtin_fabsf(wp[i]) < 0x1p110f);
                 }
             }
+            split16(wp, WB, WBl);
         }
         const bool wave_ok = __all(ok);
         // x_in (forward checkpoint): states 8h..8h+7 of channel col; and the
@@ -465,7 +427,7 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                 }
                 tot[q] = run;
             }
-            float acc = 1.f;
+            float acc = 1.f, gpt[16];
             bf16x8 PH[2], PL[2];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -476,12 +438,10 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                 for (int r = 0; r < 4; ++r) {
                     const int i = 4 * q + r;
                     cum[i] *= Eq;  // 1 / P at token tok(i)
-                    __bf16 hi, lo;
-                    split2(g[i] * rcp(cum[i]), hi, lo);
-                    PH[i >> 3][i & 7] = hi;
-                    PL[i >> 3][i & 7] = lo;
+                    gpt[i] = g[i] * rcp(cum[i]);
                 }
             }
+            split16(gpt, PH, PL);
             f32x16 r = {};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -551,16 +511,8 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
         } else if (active) {
             const f32x16 zero = {};
             bf16x8 XH, XL, MH, ML;  // x_in and Mu (states 8h..8h+7) as A operands
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                __bf16 h1, l1, h2, l2;
-                split2(xin[k], h1, l1);
-                split2(Mu[k], h2, l2);
-                XH[k] = h1;
-                XL[k] = l1;
-                MH[k] = h2;
-                ML[k] = l2;
-            }
+            split8(xin, XH, XL);
+            split8(Mu, MH, ML);
 
             f32x16 Z, PU;  // PU = G^T_{m>=n} Gp + B.Mu, so dw = PU / P
             {
@@ -572,13 +524,10 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                 {
                     bf16x8 GA[2], GAl[2];
                     const f32x16 g1 = mma(Bop, Csc, zero);  // g1[i] = G[col][tok(i)]
+                    float gm[16];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        __bf16 hi, lo;
-                        split2((tok(i) <= col) ? g1[i] : 0.f, hi, lo);
-                        GA[i >> 3][i & 7] = hi;
-                        GAl[i >> 3][i & 7] = lo;
-                    }
+                    for (int i = 0; i < 16; ++i) gm[i] = (tok(i) <= col) ? g1[i] : 0.f;
+                    split16(gm, GA, GAl);
                     Z = mma(Csc, XH, zero);
                     Z = mma(Csc, XL, Z);
 #pragma unroll
@@ -591,13 +540,10 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                 {
                     bf16x8 GTA[2], GTAl[2];
                     const f32x16 g2 = mma(Csc, Bop, zero);  // g2[i] = G[tok(i)][col]
+                    float gm[16];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        __bf16 hi, lo;
-                        split2((tok(i) >= col) ? g2[i] : 0.f, hi, lo);
-                        GTA[i >> 3][i & 7] = hi;
-                        GTAl[i >> 3][i & 7] = lo;
-                    }
+                    for (int i = 0; i < 16; ++i) gm[i] = (tok(i) >= col) ? g2[i] : 0.f;
+                    split16(gm, GTA, GTAl);
                     PU = mma(Bop, MH, zero);
                     PU = mma(Bop, ML, PU);
 #pragma unroll
@@ -767,13 +713,10 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                     t = mma(ML, sm, t);
                     t = mma(XH, sx, t);
                     t = mma(XL, sx, t);
+                    float tv[16];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        __bf16 hi, lo;
-                        split2(t[i], hi, lo);
-                        XMh[i >> 3][i & 7] = hi;
-                        XMl[i >> 3][i & 7] = lo;
-                    }
+                    for (int i = 0; i < 16; ++i) tv[i] = t[i];
+                    split16(tv, XMh, XMl);
                 }
                 // the A operand of the Mu / x_in term: W' for dB, Gp for dC -- one
                 // product per column half, the other half of XM zeroed
@@ -801,13 +744,10 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                         HT = mma(GTl[kb], WTh[kb], HT);
                     }
                     bf16x8 Hh[2], Hl[2];
+                    float hm[16];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        __bf16 hi, lo;
-                        split2(tok(i) >= col ? HT[i] : 0.f, hi, lo);
-                        Hh[i >> 3][i & 7] = hi;
-                        Hl[i >> 3][i & 7] = lo;
-                    }
+                    for (int i = 0; i < 16; ++i) hm[i] = tok(i) >= col ? HT[i] : 0.f;
+                    split16(hm, Hh, Hl);
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb) {
                         const bf16x8 Ct = trans(sCr, kb, col < N);
@@ -945,13 +885,10 @@ __global__ __launch_bounds__(64 * kTW) void bwd_carry_kernel(
             acc *= tot[q] * pt;
         }
         bf16x8 GpH[2], GpL[2];
+        float gp[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            __bf16 hi, lo;
-            split2(g[j][i] * rcp(E[i >> 2] * cum[i]), hi, lo);
-            GpH[i >> 3][i & 7] = hi;
-            GpL[i >> 3][i & 7] = lo;
-        }
+        for (int i = 0; i < 16; ++i) gp[i] = g[j][i] * rcp(E[i >> 2] * cum[i]);
+        split16(gp, GpH, GpL);
         f32x16 r = {};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {

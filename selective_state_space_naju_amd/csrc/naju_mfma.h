@@ -1,6 +1,6 @@
-// naju_mfma.h -- matrix-core and buffer-copy helpers shared by the forward
-// kernels of libnaju (gfx950): the 32x32x16 bf16 MFMA, bf16 hi + lo operand
-// splits, raw buffer descriptors and the HBM -> LDS copy.
+// naju_mfma.h -- matrix-core and buffer helpers shared by the chunk kernels of
+// libnaju (gfx950): the 32x32x16 bf16 MFMA, bf16 hi + lo operand splits, raw
+// buffer descriptors, the lane-half exchange and the forward's HBM -> LDS copy.
 #pragma once
 
 #include "naju_device.h"
@@ -29,8 +29,9 @@ constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every range used
 // are dropped.  The range check of a stride-0 buffer compares the lane offset
 // (voffset plus the instruction's immediate offset) with the range; whether the
 // scalar soffset operand takes part is not relied on anywhere: every offset that
-// must be range-checked (row offsets included) goes into voffset, and soffset
-// is 0.
+// must be range-checked (row offsets included) goes into voffset, and a nonzero
+// soffset carries only offsets under which every lane is in range or already out
+// of range by its voffset alone.
 __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
