@@ -618,8 +618,15 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                                          cw3 * d[3] + cw2 * e[0] + cw1 * e[1] + cw0 * e[2]};
                     const int qo = upper ? q - 1 : q;  // the group finished here
                     if (qo >= 0) {
+                        // qo differs between the halves, so its row offset joins the lane
+                        // offset: as a scalar offset or a per-group buffer it would be
+                        // lane-dependent, and each store a loop over its distinct values
+                        const rsrc_t rdu = trs(dhu);
+                        const uint32_t go = (uint32_t)(8 * qo) * row2;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) ST(dhu, 4 * qo + r, du[r]);
+                        for (int r = 0; r < 4; ++r)
+                            __builtin_amdgcn_raw_buffer_store_b16(from_f<bf16>(du[r]), rdu,
+                                                                  vr[r] + go, 0, 0);
                     }
                     if (q == 0 && !upper && valid) {
                         // the wave's first three dpre, for the previous wave's last tokens
