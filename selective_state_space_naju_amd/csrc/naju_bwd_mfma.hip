@@ -170,7 +170,7 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
         const int lane = ln, col = ln & 31, hh = ln >> 5;
         const bool upper = hh != 0;
         auto tok = [&](int i) -> int { return 8 * (i >> 2) + 4 * hh + (i & 3); };
-        auto tval = [&](int i) -> bool { return tok(i) < Lw; };
+        auto tval = [&](int i) -> bool { return FULL || tok(i) < Lw; };
         // token-shared operands: Bop / Csc are A/B-operand rows (token col, states
         // 8h..8h+7); Bsv / Csv the transposed operands over tokens tok(i), Csv
         // holding state col in columns 0..15 and Bsv state col-16 in columns
@@ -342,10 +342,14 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                 for (int k = 0; k < 3; ++k) sUw[tw][k][col] = (bf16)rpv[k];
             }
         };
-        // h = SiLU(pre) of the block and its derivative, from the u window in LDS
-        auto silu_at = [&](int q, int r, float &hd) -> float {
-            const float pre = cw0 * win(q, r) + cw1 * win(q, r + 1) + cw2 * win(q, r + 2) +
-                              cw3 * win(q, r + 3);
+        // the seven u values behind group q's windows
+        auto window = [&](int q, float (&uw)[7]) {
+#pragma unroll
+            for (int k = 0; k < 7; ++k) uw[k] = win(q, k);
+        };
+        // h = SiLU(pre) of the block and its derivative, from the group's u values
+        auto silu_at = [&](const float (&uw)[7], int r, float &hd) -> float {
+            const float pre = cw0 * uw[r] + cw1 * uw[r + 1] + cw2 * uw[r + 2] + cw3 * uw[r + 3];
             const float sp = rcp(1.f + ex2(-pre * kLog2e));
             hd = sp * fmaf(pre, 1.f - sp, 1.f);  // SiLU'(pre); 1 - sp enters only as pre (1 - sp)
             return pre * sp;
@@ -366,12 +370,14 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
             if (BLOCK) fill_window();
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
+                float uw[7];
+                if (BLOCK) window(q, uw);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 4 * q + r;
                     float hv;
                     if constexpr (BLOCK)
-                        hv = silu_at(q, r, hdk[i]);
+                        hv = silu_at(uw, r, hdk[i]);
                     else
                         hv = bf(ru[i]);
                     h[i] = hv;
@@ -598,12 +604,14 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                     base += sq + ps;
                 }
                 if (BLOCK) {
+                    float uw[7];
+                    window(q, uw);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        dwa0 = fmaf(dp[r], win(q, r), dwa0);
-                        dwa1 = fmaf(dp[r], win(q, r + 1), dwa1);
-                        dwa2 = fmaf(dp[r], win(q, r + 2), dwa2);
-                        dwa3 = fmaf(dp[r], win(q, r + 3), dwa3);
+                        dwa0 = fmaf(dp[r], uw[r], dwa0);
+                        dwa1 = fmaf(dp[r], uw[r + 1], dwa1);
+                        dwa2 = fmaf(dp[r], uw[r + 2], dwa2);
+                        dwa3 = fmaf(dp[r], uw[r + 3], dwa3);
                     }
                     // du_m = sum_k w_k dpre_{m+3-k}.  Lower half: group q followed by the
                     // partner's group q.  Upper half: group q-1 followed by the partner's
