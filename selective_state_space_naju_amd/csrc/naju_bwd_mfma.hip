@@ -226,17 +226,16 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
         };
 
         // ------------------------------------------------------- phase A
-        // Every global load of the phase is issued first, so that the phase waits for
-        // one round trip: a, dy, z, b, h|u (the block's u rows, and the three rows
-        // before the wave, go to LDS below), D and the conv taps.
+        // The loads the gates need (a, dy, z, the three rows of u before the wave, D
+        // and the conv taps) are issued first, b and h|u once the gates are under way:
+        // a wave keeps at most 63 memory operations in flight, so issuing all 86 at
+        // once would wait out a round trip before the last of them.
         uint16_t ra[16], rdy[16], rz[BLOCK ? 16 : 1], rb[16], ru[16], rpv[3];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             ra[i] = LD16(a, i);
             rdy[i] = LD16(dy, i);
             if (BLOCK) rz[i] = LD16(z, i);
-            rb[i] = LD16(bg, i);
-            ru[i] = LD16(hu, i);
         }
         if (BLOCK) {
             // u at the three tokens before the wave: the previous rows of u, or the
@@ -293,6 +292,13 @@ __global__ __launch_bounds__(64 * kTW, NAJU_BWD_MINB) void bwd_mfma_kernel(
                     dv *= zv * sz;                                     // dy SiLU(z)
                 }
                 g[i] = dv;
+            }
+            // b and h|u, issued once the first loads are in use (a wave keeps at most
+            // 63 loads in flight)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                rb[i] = LD16(bg, i);
+                ru[i] = LD16(hu, i);
             }
             float tot[4], cum[16];
 #pragma unroll
