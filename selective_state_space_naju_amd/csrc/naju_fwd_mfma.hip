@@ -622,6 +622,9 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
         // inclusive state ends the walk; otherwise its aggregate is folded in
         // and the walk moves one chunk further.
         if (wv < 2) {
+            // the walk is the ticket's critical path (the other two waves wait at the
+            // barrier below): its waves go first among the SIMD's waves while it runs
+            __builtin_amdgcn_s_setprio(2);
             constexpr int SG = 8;
             const int s0 = SG * wv;
             const int64_t c_l = cbase + lane;
@@ -733,6 +736,7 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
                     conv_state_out[((int64_t)bi * 3 + k) * Di + c_l] = v;
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         }
         // static tickets: the next ticket's successor, for the next release
         // (every wave has read s_tk[1] by now: it did so before the two barriers
