@@ -344,6 +344,13 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
             have_req = true;
         }
         __syncthreads();  // the tile of `cur` is in LDS
+        // Wave priorities (among the waves of the SIMD, i.e. against the other
+        // workgroup): 1 from the tile's arrival to its release, so that the next
+        // copy starts early; 2 for the look-back walk, which the whole workgroup
+        // waits for; 1 for the outputs, which end the ticket; 0 in between (the
+        // second column tile's gates and the aggregate, which the other workgroup's
+        // critical phases may overtake).
+        __builtin_amdgcn_s_setprio(1);
 
         // lane-dependent values are re-derived every ticket (kept out of
         // loop-invariant code motion, which would pin per-lane addresses in
@@ -443,6 +450,7 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
         };
         uint32_t nxt = 0;
         auto release = [&]() {  // every wave holds what it needs of the tile
+            __builtin_amdgcn_s_setprio(0);
             __syncthreads();
             nxt = s_tk[1];  // (published before this ticket's first barrier, or statically)
             if (nxt < total && wv >= 2) prefetch(nxt, lane);
@@ -622,9 +630,7 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
         // inclusive state ends the walk; otherwise its aggregate is folded in
         // and the walk moves one chunk further.
         if (wv < 2) {
-            // the walk is the ticket's critical path (the other two waves wait at the
-            // barrier below): its waves go first among the SIMD's waves while it runs
-            __builtin_amdgcn_s_setprio(2);
+            __builtin_amdgcn_s_setprio(2);  // the walk: the other two waves wait for it
             constexpr int SG = 8;
             const int s0 = SG * wv;
             const int64_t c_l = cbase + lane;
@@ -743,6 +749,7 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
         // since)
         if (!dyn && threadIdx.x == 0) s_tk[1] = nxt + gridDim.x;
         __syncthreads();  // the workgroup's entering state is in LDS
+        __builtin_amdgcn_s_setprio(1);
 
         after = (!wave_ok || !y) ? 0 : (ckpt && active) ? 24 : 16;
         if (!wave_ok) {
@@ -815,6 +822,7 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
         cur = nxt;
     }
     // the last workgroup out resets the ticket counter and advances the epoch
