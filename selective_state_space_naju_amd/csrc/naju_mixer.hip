@@ -22,6 +22,7 @@
 // scan is the block forward of this library.
 #include <hipblaslt/hipblaslt.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -129,11 +130,13 @@ struct GemmShape {
     bool tx, ty;
     hipDataType td;  // type of D (and C): HIP_R_16BF or HIP_R_32F
     bool bias, beta;
+    int batch = 1;                 // strided batch of independent products
+    int64_t sx = 0, sy = 0, sd = 0;  // element strides between the batch's operands
 };
 
 static std::mutex g_lt_mu;
 static std::map<int, hipblasLtHandle_t> g_lt;
-static std::map<std::tuple<int, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int>,
+static std::map<std::tuple<int, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int, int>,
                 GemmPlan>
     g_plans;
 
@@ -154,7 +157,7 @@ static const char *gemm_cm(hipStream_t st, const GemmShape &g, const void *X, co
     }
     const int flags = (g.bias ? 1 : 0) | (g.beta ? 2 : 0) | (g.tx ? 4 : 0) | (g.ty ? 8 : 0) |
                       (g.td == HIP_R_32F ? 16 : 0);
-    GemmPlan &p = g_plans[std::make_tuple(dev, g.m, g.n, g.k, g.ldx, g.ldy, g.ldd, flags)];
+    GemmPlan &p = g_plans[std::make_tuple(dev, g.m, g.n, g.k, g.ldx, g.ldy, g.ldd, flags, g.batch)];
     if (!p.ok) {
         const uint64_t xr = g.tx ? g.k : g.m, xc = g.tx ? g.m : g.k;
         const uint64_t yr = g.ty ? g.n : g.k, yc = g.ty ? g.k : g.n;
@@ -167,6 +170,18 @@ static const char *gemm_cm(hipStream_t st, const GemmShape &g, const void *X, co
             hipblasLtMatrixLayoutCreate(&p.ld, g.td, (uint64_t)g.m, (uint64_t)g.n, g.ldd) !=
                 HIPBLAS_STATUS_SUCCESS)
             return "hipBLASLt descriptor creation failed";
+        if (g.batch > 1) {
+            const int32_t bc = g.batch;
+            const int64_t st3[3] = {g.sx, g.sy, g.sd};
+            hipblasLtMatrixLayout_t ls[3] = {p.lx, p.ly, p.ld};
+            for (int q = 0; q < 3; ++q)
+                if (hipblasLtMatrixLayoutSetAttribute(ls[q], HIPBLASLT_MATRIX_LAYOUT_BATCH_COUNT,
+                                                      &bc, sizeof(bc)) != HIPBLAS_STATUS_SUCCESS ||
+                    hipblasLtMatrixLayoutSetAttribute(
+                        ls[q], HIPBLASLT_MATRIX_LAYOUT_STRIDED_BATCH_OFFSET, &st3[q],
+                        sizeof(st3[q])) != HIPBLAS_STATUS_SUCCESS)
+                    return "hipBLASLt batch attributes failed";
+        }
         const hipblasOperation_t opx = g.tx ? HIPBLAS_OP_T : HIPBLAS_OP_N;
         const hipblasOperation_t opy = g.ty ? HIPBLAS_OP_T : HIPBLAS_OP_N;
         hipblasLtMatmulDescSetAttribute(p.md, HIPBLASLT_MATMUL_DESC_TRANSA, &opx, sizeof(opx));
@@ -230,12 +245,44 @@ static const char *gemm_nt(hipStream_t st, int64_t T, int64_t n, int64_t k, cons
     return gemm_cm(st, g, W, A, nullptr, D, D, gws);
 }
 
-// G[k][n] (fp32) = A[T][k]^T E[T][n]: the weight gradient of D = A W
-static const char *gemm_wgrad(hipStream_t st, int64_t T, int64_t n, int64_t k, const void *A,
-                              const void *E, float *G, void *gws)
+// out[i] = sum_s part[s][i], s = 0 .. S-1 in order (fp32)
+__global__ __launch_bounds__(256) void sum_parts_kernel(const int64_t n, const int S,
+                                                        const float *__restrict__ part,
+                                                        float *__restrict__ out)
 {
-    const GemmShape g{n, k, T, n, k, n, false, true, HIP_R_32F, false, false};
-    return gemm_cm(st, g, E, A, nullptr, nullptr, G, gws);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        float v = part[i];
+        for (int s = 1; s < S; ++s) v += part[(int64_t)s * n + i];
+        out[i] = v;
+    }
+}
+
+// G[k][n] (fp32) = A[T][k]^T E[T][n]: the weight gradient of D = A W.  The output
+// is small (k x n) and the contraction long (T tokens), so one product fills few
+// of the CUs: with `scratch` (fp32, `scratch_bytes`) the tokens are cut into S
+// slices, multiplied as one strided batch into S partial gradients, and summed in
+// slice order.
+static const char *gemm_wgrad(hipStream_t st, int64_t T, int64_t n, int64_t k, const void *A,
+                              const void *E, float *G, void *gws, float *scratch = nullptr,
+                              size_t scratch_bytes = 0)
+{
+    const int64_t tiles = ((n + 127) / 128) * ((k + 127) / 128);
+    int S = (int)std::min<int64_t>(8, std::max<int64_t>(1, (512 + tiles - 1) / tiles));
+    while (S > 1 && (T % S != 0 || T / S < 512 || (size_t)S * n * k * 4 > scratch_bytes)) --S;
+    if (!scratch || S == 1) {
+        const GemmShape g{n, k, T, n, k, n, false, true, HIP_R_32F, false, false};
+        return gemm_cm(st, g, E, A, nullptr, nullptr, G, gws);
+    }
+    const int64_t Ts = T / S;
+    const GemmShape g{n, k, Ts, n, k, n, false, true, HIP_R_32F, false, false, S, Ts * n, Ts * k,
+                      n * k};
+    const char *e = gemm_cm(st, g, E, A, nullptr, nullptr, scratch, gws);
+    if (e) return e;
+    const int64_t cnt = n * k;
+    const unsigned blocks = (unsigned)std::min<int64_t>((cnt + 255) / 256, 4096);
+    hipLaunchKernelGGL(sum_parts_kernel, dim3(blocks), dim3(256), 0, st, cnt, S,
+                       (const float *)scratch, G);
+    return hipGetLastError() == hipSuccess ? nullptr : "partial-sum launch failed";
 }
 
 // ------------------------------------------------------------ layout of ws
@@ -625,7 +672,9 @@ const char *mixer_bwd(const MixerArgs &g, const MixerGrads &d, hipStream_t st)
     if (!d.saved && (e = mixer_forward_pass(g, f, ck, st))) return e;
     // out = y W_out + res
     if ((e = gemm_nt(st, T, g.Di, g.dm, d.d_out, g.W_out, false, dy, HIP_R_16BF, gws))) return e;
-    if ((e = gemm_wgrad(st, T, g.dm, g.Di, y, d.d_out, d.dW_out, gws))) return e;
+    // (dh is free until the dh products below: the weight gradients' partials go there)
+    const size_t dh_bytes = (size_t)T * g.Di * 4;
+    if ((e = gemm_wgrad(st, T, g.dm, g.Di, y, d.d_out, d.dW_out, gws, dh, dh_bytes))) return e;
     // the block scan
     BwdArgs k{};
     k.io = NAJU_BF16;
@@ -670,12 +719,6 @@ const char *mixer_bwd(const MixerArgs &g, const MixerGrads &d, hipStream_t st)
                        (const bf16 *)g.W_B, (const bf16 *)g.W_C, WBC);
     if (hipGetLastError() != hipSuccess) return "pack launch failed";
     if ((e = gemm_nt(st, T, g.Di, 2 * g.N, dBC, WBC, true, dh, HIP_R_32F, gws))) return e;
-    if ((e = gemm_wgrad(st, T, g.Di, g.Di, h, da, d.dW_a, gws))) return e;
-    if ((e = gemm_wgrad(st, T, g.Di, g.Di, h, db, d.dW_b, gws))) return e;
-    if ((e = gemm_wgrad(st, T, 2 * g.N, g.Di, h, dBC, gBC, gws))) return e;
-    hipLaunchKernelGGL(unpack2_kernel, dim3(256), dim3(256), 0, st, g.Di, (int)g.N,
-                       (const float *)gBC, d.dW_B, d.dW_C);
-    if (hipGetLastError() != hipSuccess) return "unpack launch failed";
     // bias gradients: column sums of da and db (two fixed-order passes)
     if (colsum((const bf16 *)da, T, g.Di, nullptr, csum, kSlices, d.da_bias, st) != hipSuccess ||
         colsum((const bf16 *)db, T, g.Di, nullptr, csum, kSlices, d.db_bias, st) != hipSuccess)
@@ -694,11 +737,19 @@ const char *mixer_bwd(const MixerArgs &g, const MixerGrads &d, hipStream_t st)
                    d.dconv_w, st) != hipSuccess)
             return "dconv_w reduction launch failed";
     }
+    // the gate and B, C projections' weight gradients (dh is free again: its
+    // partials scratch)
+    if ((e = gemm_wgrad(st, T, g.Di, g.Di, h, da, d.dW_a, gws, dh, dh_bytes))) return e;
+    if ((e = gemm_wgrad(st, T, g.Di, g.Di, h, db, d.dW_b, gws, dh, dh_bytes))) return e;
+    if ((e = gemm_wgrad(st, T, 2 * g.N, g.Di, h, dBC, gBC, gws, dh, dh_bytes))) return e;
+    hipLaunchKernelGGL(unpack2_kernel, dim3(256), dim3(256), 0, st, g.Di, (int)g.N,
+                       (const float *)gBC, d.dW_B, d.dW_C);
+    if (hipGetLastError() != hipSuccess) return "unpack launch failed";
     // u = xn W_u, z = xn W_z
     if ((e = gemm_nt(st, T, g.dm, g.Di, du, g.W_u, false, d.dxn, HIP_R_32F, gws))) return e;
     if ((e = gemm_nt(st, T, g.dm, g.Di, dz, g.W_z, true, d.dxn, HIP_R_32F, gws))) return e;
-    if ((e = gemm_wgrad(st, T, g.Di, g.dm, g.xn, du, d.dW_u, gws))) return e;
-    if ((e = gemm_wgrad(st, T, g.Di, g.dm, g.xn, dz, d.dW_z, gws))) return e;
+    if ((e = gemm_wgrad(st, T, g.Di, g.dm, g.xn, du, d.dW_u, gws, dh, dh_bytes))) return e;
+    if ((e = gemm_wgrad(st, T, g.Di, g.dm, g.xn, dz, d.dW_z, gws, dh, dh_bytes))) return e;
     return nullptr;
 }
 
