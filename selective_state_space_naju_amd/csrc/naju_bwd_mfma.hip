@@ -846,6 +846,9 @@ __global__ __launch_bounds__(64 * kTW) void bwd_carry_kernel(
     const bool valid = c0 < Di;                      // Di is even: both or neither
     auto tok = [&](int i) -> int { return 8 * (i >> 2) + 4 * hh + (i & 3); };
 
+    // the loads go out first among the CU's workgroups (wave priority 2 until the
+    // last is issued): a carry is one round trip and then arithmetic
+    __builtin_amdgcn_s_setprio(2);
     bf16x8 Csv[2];
     {
         const rsrc_t rC = make_rsrc(Cm + (tokbase + (active ? n0 : 0)) * N, (uint32_t)Lw * N * 2);
@@ -885,6 +888,7 @@ __global__ __launch_bounds__(64 * kTW) void bwd_carry_kernel(
             g[j][i] = dj;
         }
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         float tot[4], cum[16];
