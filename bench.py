@@ -355,7 +355,9 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the Naju scan path has no multi-GPU "
-              "implementation here (see DESIGN.md for how it would shard).", file=sys.stderr)
+              "implementation here (it would shard over batch rows, over channels with B and C "
+              "replicated, or over sequence segments chained through the x0 input).",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
