@@ -92,6 +92,8 @@ BWD_CASES = [
     (1, 333, 96, 64, 64, True),
     (2, 130, 32, 256, 16, True),
     (8, 2048, 64, 128, 16, False),  # the training batch shape (16384 tokens), narrow layer
+    # 3000 tokens: the weight gradients split over 4 token slices of 750
+    (2, 1500, 64, 128, 16, False),
     # the benchmarked layer width, fewer tokens: the layer's dh = dB W_B^T + dC W_C^T
     # spreads any error of dB / dC over every channel of a token, so this case holds
     # the channel contractions of the block backward to near-fp32 accuracy
