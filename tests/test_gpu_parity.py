@@ -362,5 +362,8 @@ def test_bf16_bwd_fallback_chunks(block):
                        t["dy"], x0, dxf, t["conv_state"]) if block else
           nb.scan_bwd(t["h"], t["a"], t["b"], t["B"], t["C"], D, t["dy"], x0, dxf))
     torch.cuda.synchronize()
+    # (the checkpoints are recomputed by the forward, whose look-back may fold a
+    # predecessor's aggregate in one call and read its inclusive state in the other:
+    # rounding only)
     for k in names:
-        assert_close(k + "(2nd)", host(g2[k]), host(g[k]), 1e-2)
+        assert_agree(k + "(2nd)", host(g2[k]), host(g[k]), ulps=2.0)
