@@ -16,7 +16,7 @@ stream; median, mean, p10 and p90 over at least 50 launches):
 * every other workload of the hot path: the fp32 1 x 256 x 192 scan, the
   4 x 8192 x 4096 d_state-64 scan (one call, and the same sequence as 4 chained
   calls of 2048 tokens carrying the state), the 1 x 65536 x 2048 long scan, the
-  step's scan shape with forgetful gates (every chunk on the register fallback),
+  step's scan shape with forgetful gates (forget pre-activations ~ N(-2, 1)),
   and the mixer layer around the scan (8 x 2048, d_model 768, d_inner 1536);
 * the CPU oracle (the cpu_baseline leg) on a bounded sample of each workload,
   on the host's cores and, for the fp32 1 x 256 x 192 scan, on one thread.
