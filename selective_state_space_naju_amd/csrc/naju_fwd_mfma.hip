@@ -292,10 +292,10 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
 
     // Tickets: dyn = 1 takes them from this XCD's queue (workgroups are
     // dispatched round-robin over the 8 XCDs, so blockIdx % 8 names it; the
-    // mapping only decides locality, never correctness), two ahead: the one
-    // after next is requested at the start of a ticket, so the counter's round
-    // trip never delays the next tile's copy.  dyn = 0 assigns them statically
-    // (w, w + G, ...).
+    // mapping only decides locality, never correctness), one ahead: the next
+    // is requested at the start of a ticket and known at its release, when the
+    // next tile's copy is issued.  dyn = 2 takes them from one queue in their
+    // own order.  dyn = 0 assigns them statically (w, w + G, ...).
     const uint32_t qx = blockIdx.x & 7;
     // the k-th ticket of queue qx (total when the queue is exhausted)
     auto ticket_of = [&](uint32_t k) -> uint32_t {
@@ -304,10 +304,16 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
         const uint32_t row = qx + 8 * (k - chk * tq.rows[qx].d);
         return chk * fd_chunk.d + row;
     };
+    // dyn = 2: one queue for the whole grid, handing out tickets in their own
+    // (chunk-major) order
+    uint32_t *const qc = dyn == 2 ? &hdr->queue[0] : &hdr->queue[qx];
+    auto tk_of = [&](uint32_t k) -> uint32_t {
+        return dyn == 2 ? (k < total ? k : total) : ticket_of(k);
+    };
     if (threadIdx.x == 0) {
         s_epoch = (ld_agent(&hdr->epoch) + 1u) & 0x3FFFFFFFu;
         if (dyn) {
-            s_tk[0] = ticket_of(add_agent(&hdr->queue[qx], 1u));
+            s_tk[0] = tk_of(add_agent(qc, 1u));
         } else {
             s_tk[0] = blockIdx.x;
             s_tk[1] = blockIdx.x + gridDim.x;
@@ -322,11 +328,9 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
     // ticket): waiting until that many are outstanding waits for the copy only
     int after = 0;
 
-    // (dyn) the queue position requested during the previous ticket by the first
-    // lane of wave 2, a copy wave: its round trip is waited for only together
-    // with that wave's tile copy, never by the look-back waves
+    // (dyn) the queue position requested at this ticket's start by the first lane
+    // of wave 2, a copy wave
     uint32_t k_req = 0;
-    bool have_req = false;
     while (cur < total) {
         if (wv >= 2) {
             if (after == 24)
@@ -336,13 +340,12 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
             else
                 wait_mem();
         }
-        if (dyn && threadIdx.x == 128) {
-            // the next ticket: requested a ticket ago (the first one now, so that
-            // every workgroup's first two tickets follow the start order)
-            s_tk[1] = ticket_of(have_req ? k_req : add_agent(&hdr->queue[qx], 1u));
-            k_req = add_agent(&hdr->queue[qx], 1u);
-            have_req = true;
-        }
+        // (dyn) the next ticket is requested now and read just before the release
+        // barrier, half a ticket later: reading the counter's reply waits for every
+        // memory operation the wave issued before it, and by then the previous
+        // ticket's output stores have drained (read here, the wait would put their
+        // round trip into every ticket)
+        if (dyn && threadIdx.x == 128) k_req = add_agent(qc, 1u);
         __syncthreads();  // the tile of `cur` is in LDS
         // Wave priorities (among the waves of the SIMD, i.e. against the other
         // workgroup): 1 from the tile's arrival to its release, so that the next
@@ -451,8 +454,9 @@ __global__ __launch_bounds__(64 * kW, 2) void fwd_chunk_kernel(
         uint32_t nxt = 0;
         auto release = [&]() {  // every wave holds what it needs of the tile
             __builtin_amdgcn_s_setprio(0);
+            if (dyn && threadIdx.x == 128) s_tk[1] = tk_of(k_req);
             __syncthreads();
-            nxt = s_tk[1];  // (published before this ticket's first barrier, or statically)
+            nxt = s_tk[1];  // (dyn: requested at this ticket's start; else static)
             if (nxt < total && wv >= 2) prefetch(nxt, lane);
         };
         float Pv[2][16];  // P (block: P SiLU(z)), the factor of the token's output
@@ -879,10 +883,16 @@ hipError_t launch_fwd_mfma(const FwdArgs &g, hipStream_t stream)
     const FastDiv fdc = make_fastdiv(per_chunk), fdt = make_fastdiv((uint32_t)pl.n_tiles);
     const uint32_t total = per_chunk * (uint32_t)pl.n_chunks;
     const TicketQueues tq = make_ticket_queues(per_chunk, (uint32_t)pl.n_chunks);
-    // NAJU_FWD_TICKETS=dynamic (read at every call) takes tickets from the
-    // per-XCD queues instead of the static assignment
+    // Ticket schedule: one queue handing out tickets in their own order.  Every
+    // predecessor is then held by a workgroup that is running or done, so each
+    // wait ends whatever share of the device this launch gets; deep chains also
+    // advance as workgroups free up instead of in lockstep rounds (1 x 65536 x
+    // 2048: 435 -> 394 us against the static assignment, 8 x 2048 x 1536: 2 %
+    // slower).  NAJU_FWD_TICKETS=static (w, w + G, ..., which needs every
+    // workgroup resident) or dynamic (per-XCD queues), read at every call,
+    // overrides it.
     const char *tkenv = getenv("NAJU_FWD_TICKETS");
-    const int dyn = (tkenv && tkenv[0] == 'd') ? 1 : 0;
+    const int dyn = (tkenv && tkenv[0] == 'd') ? 1 : (tkenv && tkenv[0] == 's') ? 0 : 2;
     int64_t L = g.L, Di = g.Di;
     int n_chunks = pl.n_chunks;
     float scale = g.scale;

@@ -222,10 +222,12 @@ def test_outputs_stay_in_bounds(io):
         assert_close(k, host(o[k]).reshape(ref[k].shape), ref[k], TOL[io])
 
 
+@pytest.mark.parametrize("sched", ["static", "dynamic", "global"])
 @pytest.mark.parametrize("block", [False, True], ids=["scan", "block"])
-def test_ticket_schedules_agree(block):
-    """The static schedule (default) and the per-XCD ticket queues
-    (NAJU_FWD_TICKETS=dynamic, read at each call) compute the same results."""
+def test_ticket_schedules_agree(block, sched):
+    """Every ticket schedule of the matrix-core forward -- static, per-XCD queues,
+    one queue in ticket order (the default; NAJU_FWD_TICKETS, read at each call) --
+    computes the same results."""
     Bt, L, Di, N = 4, 2100, 264, 16
     d = inputs.draw(Bt, L, Di, N, io="bf16", seed=36, x0=True, block=block, conv_state=block)
     hk = "u" if block else "h"
@@ -239,7 +241,7 @@ def test_ticket_schedules_agree(block):
         return nb.scan_fwd(t["h"], t["a"], t["b"], t["B"], t["C"], D, x0, check_errors=True)
     y0, xf0 = run()
     old = os.environ.get("NAJU_FWD_TICKETS")
-    os.environ["NAJU_FWD_TICKETS"] = "dynamic"
+    os.environ["NAJU_FWD_TICKETS"] = sched
     try:
         ys = [run() for _ in range(3)]
     finally:
@@ -249,6 +251,6 @@ def test_ticket_schedules_agree(block):
             os.environ["NAJU_FWD_TICKETS"] = old
     torch.cuda.synchronize()
     for y1, xf1 in ys:
-        assert_agree("y(dynamic)", host(y1), host(y0))
+        assert_agree("y(%s)" % sched, host(y1), host(y0))
         e = np.abs(host(xf1) - host(xf0)).max() / np.abs(host(xf0)).max()
         assert e <= 1e-6, e
