@@ -111,7 +111,12 @@ naju_status_t naju_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Synchronises `stream`, then reads the workspace's device-side error word:
  * *flags = 0 if every cross-workgroup wait of the previous calls completed,
- * nonzero if one gave up after its bounded spin (results are then invalid). */
+ * nonzero if one gave up after its bounded spin (results are then invalid).
+ * Every kernel that waits on another workgroup takes its work items from an
+ * in-order counter (the matrix-core forward by default), so a
+ * wait is always on an item already held by a running workgroup and ends
+ * however many workgroups the device runs at once; the bound (about 0.4 s of
+ * polling) only catches a device stalled for longer than that. */
 naju_status_t naju_workspace_check(const void *ws, size_t ws_bytes, void *stream,
                                    uint32_t *flags);
 
