@@ -525,8 +525,8 @@ __global__ __launch_bounds__(64 * kWv, 1) void fwd_mfma64_kernel(
         if (ckpt && active) {
             float *cp = ckpt + (((int64_t)bi * n_waves + (int64_t)chunk * 4 + tbw) * N) * Di + cbase + kCW * chh;
             const rsrc_t rc = make_rsrc(cp, (uint32_t)(N * Di * 4));
-            // every offset in the lane's voffset: a buffer's range check does not
-            // cover the scalar soffset operand, so nothing may rely on it
+            // every offset in the lane's voffset (the rule for range-checked
+            // offsets that every kernel here keeps)
             const uint32_t vo = c_col < Di ? (uint32_t)((8 * hh) * Di + col) * 4 : kOOB;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)

@@ -26,12 +26,12 @@ __device__ __forceinline__ __bf16 as_bf(bf16 v) { return __builtin_bit_cast(__bf
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every range used here
 
 // Raw buffer over [p, p + bytes): loads past the end read 0, stores past the end
-// are dropped.  The range check of a stride-0 buffer compares the lane offset
-// (voffset plus the instruction's immediate offset) with the range; whether the
-// scalar soffset operand takes part is not relied on anywhere: every offset that
-// must be range-checked (row offsets included) goes into voffset, and a nonzero
-// soffset carries only offsets under which every lane is in range or already out
-// of range by its voffset alone.
+// are dropped.  On gfx950 the range check of a stride-0 buffer covers the whole
+// offset (voffset + soffset + the immediate offset), dword by dword for wider
+// accesses.  The kernels still put every offset that must be range-checked (row
+// offsets included) into voffset, and a nonzero soffset carries only offsets
+// under which every lane is in range or already out of range by its voffset
+// alone.
 __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
